@@ -1,0 +1,332 @@
+"""CPU oracle for the forward pass of one sparsely-gated MoE FFN layer.
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, plain, fp64 statement of
+what the layer computes.  Only the test-suite, the package smoke check and the
+``cpu_baseline`` leg of the benchmark may import or call it.  The HIP library
+never imports it, links it or calls it, and it shares no code with that
+library (no kernels, headers, helpers, tables or constants).
+
+Sources (web pages, cited by title and section):
+
+* [SG]   "Sparsely-Gated MoE 구현 관점에서 살펴보기: Router, Top-k, 부하 분산"
+         (molayo1419.me) -- the method page.  Sections used: "Router를 텐서
+         형태에서 추적하기" (router tensor shapes), "Top-2 라우팅의 수치 예시"
+         (top-2 worked example), "순전파 과정(forward pass)은 디스패치와
+         결합(combine)을 포함" (the five-step forward pipeline), "로드 밸런싱
+         손실과 용량은 별개" (capacity and overflow), "pure Python으로 Top-k
+         Router 확인하기" (stable softmax over the selected logits).
+* [EP]   "5.3 Expert Parallelism" (sungeuns.github.io), section
+         "3. 고도화된 최적화" / "최적화 2: GroupGEMM" (the per-expert loop).
+* [HF]   "Expert를 똑같이 나눴는데도 GPU가 대기하는 이유: MoE의 토큰 쏠림"
+         (portfolio.ywsung.com), table "실행 백엔드별 메커니즘과 최적
+         시나리오" (the ``eager`` backend: a sequential per-expert loop, meant
+         for correctness checking).
+* [MOON] "가장 바쁜 랭크가 속도를 정합니다: MoonEP의 계획 코드를 직접
+         돌려봤습니다" (thakicloud.com), section "설치 및 통합" (packed
+         per-projection weights, ``cu_seqlens`` selecting each expert's rows,
+         ``tokens_per_expert``).
+
+Readings where the pages are silent or garbled (each also listed in the
+repository's design notes):
+
+* The expert FFN is SwiGLU: ``y = (silu(x Wg^T) * (x Wu^T)) Wd^T`` with
+  ``silu(z) = z / (1 + exp(-z))``; no biases.  The pages do not define the
+  expert FFN; this form is the one the workloads name.
+* Weights are stored ``[E, out, in]`` so that every product is ``A @ W.T``, as
+  in the router's ``X @ W_r.T`` ([SG] forward pipeline).
+* Ties among equal logits go to the lower expert id; selected slots are
+  ordered by descending logit.
+* Capacity is ``C = min(T, ceil(cf * T * k / E))`` (the printed formula is
+  lost in [SG] "capacity").  Overflow is resolved first-come in token order:
+  each expert keeps its C lowest token ids.  A dropped copy contributes zero;
+  the surviving weights are not renormalised; nothing is re-routed.
+* Logits are fp32: the dot product is accumulated in fp64, rounded to fp32,
+  then the fp32 bias is added in fp32.  Gate weights are computed in fp64.
+
+Parity pins: every function here is pinned by ``tests/test_oracle.py``
+against the worked example, closed forms, invariants, textbook special cases
+and brute force; see the docstrings for which pin covers which step.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+TOPK_THEN_SOFTMAX = 0
+SOFTMAX_THEN_TOPK = 1
+
+# A token whose k-th and (k+1)-th fp32 logits differ by less than this is a
+# near tie: its expert set is not decided robustly by fp32 rounding.
+NEAR_TIE_GAP = 1e-5
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# O1  router logits            [SG] "Router를 텐서 형태에서 추적하기";
+#                              [SG] forward pipeline, step 1 (X @ W_r.T)
+# ---------------------------------------------------------------------------
+def router_logits(X, W_r, bias=None):
+    """Router logits ``l[t, e] = fp32(sum_i X[t,i] W_r[e,i]) + b[e]``.
+
+    X: [T, d] (values exactly representable in fp32), W_r: [E, d] fp32,
+    bias: [E] fp32 or None.  The dot products are accumulated in fp64 and
+    rounded once to fp32; the bias is then added in fp32 arithmetic.
+    Returns [T, E] float32.
+    """
+    l64 = _f64(X) @ _f64(W_r).T
+    l32 = l64.astype(np.float32)
+    if bias is not None:
+        l32 = (l32 + np.asarray(bias, dtype=np.float32)).astype(np.float32)
+    return l32
+
+
+# ---------------------------------------------------------------------------
+# O2/O3  top-k selection and gate weights
+#        [SG] "Top-2 라우팅의 수치 예시" (select k largest, renormalise with
+#        softmax over the selected logits; ids are 0-based);
+#        [SG] "pure Python으로 Top-k Router 확인하기" (stable softmax: the max
+#        selected logit is subtracted before exponentiating);
+#        [SG] same example section, last paragraph (the other order:
+#        softmax over all experts first, then top-k, then renormalise).
+# ---------------------------------------------------------------------------
+def select_topk(logits, k):
+    """Per row, the k largest logits ordered by (logit desc, expert id asc).
+
+    Returns (idx [T,k] int32, near_tie [T] bool).  ``near_tie[t]`` is set when
+    k < E and the gap between the k-th and (k+1)-th largest logit is below
+    ``NEAR_TIE_GAP``.
+    """
+    logits = np.asarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    # A stable sort of the negated logits orders equal logits by ascending id.
+    order = np.argsort(-logits.astype(np.float64), axis=1, kind="stable")
+    idx = order[:, :k].astype(np.int32)
+    if k < E:
+        srt = np.take_along_axis(logits, order, axis=1).astype(np.float64)
+        near_tie = (srt[:, k - 1] - srt[:, k]) < NEAR_TIE_GAP
+    else:
+        near_tie = np.zeros(T, dtype=bool)
+    return idx, near_tie
+
+
+def gate_weights(logits, idx, gating):
+    """Gate weights for the selected experts, in fp64.
+
+    TOPK_THEN_SOFTMAX: ``w_j = exp(l_j - m) / sum_{j' in S} exp(l_j' - m)``
+    with ``m`` the largest selected logit.
+    SOFTMAX_THEN_TOPK: ``p = softmax(l)`` over all E experts (max-shifted),
+    then ``w_j = p_j / sum_{j' in S} p_j'``.
+    Returns [T, k] float64.
+    """
+    l = _f64(logits)
+    sel = np.take_along_axis(l, np.asarray(idx, dtype=np.int64), axis=1)
+    if gating == TOPK_THEN_SOFTMAX:
+        m = sel.max(axis=1, keepdims=True)
+        ex = np.exp(sel - m)
+        return ex / ex.sum(axis=1, keepdims=True)
+    if gating == SOFTMAX_THEN_TOPK:
+        M = l.max(axis=1, keepdims=True)
+        ex = np.exp(l - M)
+        p = ex / ex.sum(axis=1, keepdims=True)
+        psel = np.take_along_axis(p, np.asarray(idx, dtype=np.int64), axis=1)
+        return psel / psel.sum(axis=1, keepdims=True)
+    raise ValueError(f"unknown gating {gating}")
+
+
+def route(X, W_r, bias, k, gating):
+    """Router step: logits -> (topk_idx int32 [T,k], topk_w fp64 [T,k],
+    near_tie bool [T], logits fp32 [T,E])."""
+    logits = router_logits(X, W_r, bias)
+    idx, near_tie = select_topk(logits, k)
+    w = gate_weights(logits, idx, gating)
+    return idx, w, near_tie, logits
+
+
+# ---------------------------------------------------------------------------
+# O4-O6  counts, capacity, slots      [SG] forward pipeline step 2 (assign
+#        per-expert capacity slots); [SG] "로드 밸런싱 손실과 용량은 별개"
+#        (capacity bounds the tokens one expert takes; overflow is dropped);
+#        [MOON] "설치 및 통합" (tokens_per_expert, cu_seqlens);
+#        [EP] "2. 디스패처 엔지니어링" (bincount of the routed ids).
+# ---------------------------------------------------------------------------
+def capacity(T, k, E, capacity_factor):
+    """Per-expert capacity ``min(T, ceil(cf*T*k/E))``; None means unlimited
+    (capacity_factor <= 0 or None)."""
+    if capacity_factor is None or capacity_factor <= 0:
+        return None
+    return min(T, int(math.ceil(capacity_factor * T * k / E)))
+
+
+def assign(idx, E, C):
+    """Assign capacity slots, first-come in token-major order.
+
+    Walks the copies (t, j) with t = 0..T-1 outer and j = 0..k-1 inner; copy
+    (t, j) takes slot ``pos = fill[e]`` of expert ``e = idx[t, j]`` and is kept
+    iff ``pos < C`` (always kept when C is None).
+
+    Returns a dict with
+      counts  [E]   int64  raw copies per expert (before capacity)
+      kept    [E]   int64  min(counts, C)
+      offsets [E+1] int64  exclusive prefix sum of kept (cu_seqlens)
+      dest    [T,k] int64  row of the copy in expert-contiguous order, -1 if dropped
+      row_token [N] int64  token id of each kept row
+      dropped int          number of dropped copies
+    """
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    counts = np.zeros(E, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            counts[idx[t, j]] += 1
+    cap = np.iinfo(np.int64).max if C is None else int(C)
+    kept = np.minimum(counts, cap)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + kept[e]
+    fill = np.zeros(E, dtype=np.int64)
+    dest = np.full((T, k), -1, dtype=np.int64)
+    row_token = np.full(int(offsets[E]), -1, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            pos = fill[e]
+            fill[e] += 1
+            if pos < cap:
+                r = offsets[e] + pos
+                dest[t, j] = r
+                row_token[r] = t
+    dropped = int((counts - kept).sum())
+    return dict(counts=counts, kept=kept, offsets=offsets, dest=dest,
+                row_token=row_token, dropped=dropped)
+
+
+# ---------------------------------------------------------------------------
+# O7  permute / dispatch           [SG] forward pipeline step 3 (reorder the
+#                                  tokens in expert order and dispatch them)
+# ---------------------------------------------------------------------------
+def gather_rows(X, row_token):
+    """``X_perm[r] = X[row_token[r]]`` (values copied unchanged)."""
+    X = np.asarray(X)
+    return X[np.asarray(row_token, dtype=np.int64)]
+
+
+# ---------------------------------------------------------------------------
+# O8  per-expert FFN, one expert at a time
+#     [SG] forward pipeline step 4 (run each expert's FFN on its batch);
+#     [EP] "최적화 2: GroupGEMM" (the plain loop over local experts);
+#     [HF] backend table (``eager``: sequential loop per expert, for
+#     correctness checking).
+# ---------------------------------------------------------------------------
+def silu(z):
+    z = _f64(z)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(A, Wg, Wu, Wd):
+    """One expert's SwiGLU FFN on the rows A [n, d], all in fp64:
+    ``(silu(A Wg^T) * (A Wu^T)) Wd^T`` with Wg, Wu [d_ff, d] and Wd [d, d_ff].
+    """
+    A = _f64(A)
+    G = A @ _f64(Wg).T
+    U = A @ _f64(Wu).T
+    H = silu(G) * U
+    return H @ _f64(Wd).T
+
+
+def grouped_ffn(X_perm, offsets, W_gate, W_up, W_down):
+    """Loop over experts e = 0..E-1, each on its rows [offsets[e], offsets[e+1]).
+    Returns Y_perm [N, d] fp64."""
+    X_perm = _f64(X_perm)
+    E = len(offsets) - 1
+    d = W_down.shape[1]
+    Y = np.zeros((int(offsets[E]), d), dtype=np.float64)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            Y[lo:hi] = expert_ffn(X_perm[lo:hi], W_gate[e], W_up[e], W_down[e])
+    return Y
+
+
+# ---------------------------------------------------------------------------
+# O9  unpermute + gate-weighted combine
+#     [SG] "Router를 텐서 형태에서 추적하기" (the layer output is the weighted
+#     average of the selected experts' outputs; unselected experts contribute
+#     nothing); [SG] forward pipeline step 5 (un-permute, combine with the
+#     router weights, original token order).
+# ---------------------------------------------------------------------------
+def combine(Y_perm, dest, w, T):
+    """``out[t] = sum_{j : dest[t,j] >= 0} w[t,j] * Y_perm[dest[t,j]]`` (fp64).
+    A token whose copies were all dropped gets a zero row."""
+    Y_perm = _f64(Y_perm)
+    dest = np.asarray(dest)
+    w = _f64(w)
+    d = Y_perm.shape[1] if Y_perm.ndim == 2 else 0
+    out = np.zeros((T, d), dtype=np.float64)
+    for t in range(T):
+        for j in range(dest.shape[1]):
+            r = dest[t, j]
+            if r >= 0:
+                out[t] += w[t, j] * Y_perm[r]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# The whole layer.
+# ---------------------------------------------------------------------------
+def moe_forward(X, W_r, bias, W_gate, W_up, W_down, k, capacity_factor=None,
+                gating=TOPK_THEN_SOFTMAX):
+    """Forward pass of the layer, [SG] forward pipeline steps 1-5 in order.
+
+    Returns a dict with ``out`` [T, d] fp64 plus every intermediate
+    (idx, w, near_tie, logits, counts, kept, offsets, dest, row_token,
+    dropped, C, X_perm, Y_perm).
+    """
+    X = np.asarray(X)
+    T = X.shape[0]
+    E = W_r.shape[0]
+    idx, w, near_tie, logits = route(X, W_r, bias, k, gating)
+    C = capacity(T, k, E, capacity_factor)
+    a = assign(idx, E, C)
+    X_perm = gather_rows(X, a["row_token"])
+    Y_perm = grouped_ffn(X_perm, a["offsets"], W_gate, W_up, W_down)
+    out = combine(Y_perm, a["dest"], w, T)
+    res = dict(out=out, idx=idx, w=w, near_tie=near_tie, logits=logits, C=C,
+               X_perm=X_perm, Y_perm=Y_perm)
+    res.update(a)
+    return res
+
+
+def moe_forward_tokens(tokens, X, idx, w, dest, expert_weights, d_out):
+    """Layer output for a subset of tokens, given the full routing.
+
+    ``out[t]`` depends on the other tokens only through which of t's copies
+    capacity kept (``dest``), so once routing and assignment have been done
+    for every token, the output of a token is its own weighted sum of expert
+    FFNs.  The experts are visited one at a time (ascending id) so that only
+    one expert's weights are held at once; ``expert_weights(e)`` returns
+    (Wg, Wu, Wd) for expert e.  Returns [len(tokens), d_out] fp64.
+    """
+    tokens = [int(t) for t in tokens]
+    k = idx.shape[1]
+    y = {}
+    need = {}
+    for t in tokens:
+        for j in range(k):
+            if dest[t, j] >= 0:
+                need.setdefault(int(idx[t, j]), []).append((t, j))
+    for e in sorted(need):
+        Wg, Wu, Wd = expert_weights(e)
+        for (t, j) in need[e]:
+            y[(t, j)] = expert_ffn(_f64(X[t])[None, :], Wg, Wu, Wd)[0]
+    out = np.zeros((len(tokens), d_out), dtype=np.float64)
+    for i, t in enumerate(tokens):
+        for j in range(k):
+            if (t, j) in y:
+                out[i] += w[t, j] * y[(t, j)]
+    return out
