@@ -1,0 +1,191 @@
+"""Benchmark of the MoE FFN layer forward pass on one MI355X.
+
+One step = one moe_forward call (router, permute, grouped SwiGLU FFN,
+combine) over one batch of the Mixtral-8x7B-shaped workload (T=4096,
+d_model=4096, E=8, top-2, d_ff=14336, bf16 with fp32 accumulation, router in
+fp32), inputs resident in HBM.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--cpu-sample-tokens N]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=64)
+    return ap.parse_args()
+
+
+def _time_loop(fn, steps, stream):
+    import torch
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(steps):
+        fn()
+    e.record(stream)
+    e.synchronize()
+    return s.elapsed_time(e) / steps  # ms per call
+
+
+def _cpu_baseline(wl, dev, ntok):
+    """The CPU oracle (as it stands) on the first `ntok` tokens of the same
+    batch with the same weights; returns the dict for the JSON line."""
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+
+    host = {k: (None if v is None else v.float().cpu().numpy())
+            for k, v in dev.items()}
+    X = host["X"][:ntok]
+    cf = float(np.float32(wl.capacity_factor))
+    t0 = time.perf_counter()
+    O.moe_forward(X, host["W_r"], host["bias"], host["W_gate"], host["W_up"],
+                  host["W_down"], wl.top_k, cf if cf > 0 else None, wl.gating)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {ntok} of the {wl.T} tokens, all {wl.E} experts "
+                      f"(full weights), fp64 NumPy per-expert loop, "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the whole MoE layer runs on a single "
+              "MI355X; multi-GPU runs are not supported (use --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_layer_wavefront_amd as M
+    from mixture_experts_layer_wavefront_amd import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    dev = W.make_device(wl, "cuda")
+    p = M.problem(wl.T, wl.d_model, wl.E, wl.top_k, wl.d_ff,
+                  wl.capacity_factor, wl.dtype, wl.gating, "f32")
+    ws = torch.empty(M.workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    out = torch.empty((wl.T, wl.d_model), dtype=torch.float32, device="cuda")
+    stats = torch.empty(2 * wl.E + 2, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    a = (dev["X"], dev["W_r"], dev["bias"], dev["W_gate"], dev["W_up"],
+         dev["W_down"])
+
+    def step():
+        M.moe_forward(p, *a, out=out, stats=stats, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = _time_loop(step, args.steps, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = stats.cpu().numpy()
+    N = int(st[2 * wl.E])                       # kept token copies
+    counts = st[:wl.E]
+    active = int(np.count_nonzero(st[wl.E + 1:2 * wl.E + 1] - st[wl.E:2 * wl.E]))
+
+    # ---- per stage (same kernels, called through the stage entry points) ----
+    idx, w = M.moe_route(p, dev["X"], dev["W_r"], dev["bias"])
+    perm = M.moe_permute(p, dev["X"], idx)
+    Y = M.moe_grouped_ffn(p, perm["X_perm"], perm["offsets"], dev["W_gate"],
+                          dev["W_up"], dev["W_down"])
+    o2 = M.moe_combine(p, Y, perm["dest_row"], w)
+    ffn_ws = torch.empty(M.grouped_ffn_workspace_bytes(p), dtype=torch.uint8,
+                         device="cuda")
+    perm_ws = torch.empty(M.permute_workspace_bytes(p), dtype=torch.uint8,
+                          device="cuda")
+    n = max(args.steps, 5)
+    t_route = _time_loop(lambda: M.moe_route(p, dev["X"], dev["W_r"], dev["bias"],
+                                             idx, w), n, stream)
+    t_perm = _time_loop(lambda: M.moe_permute(p, dev["X"], idx, perm_ws, out=perm),
+                        n, stream)
+    t_ffn = _time_loop(lambda: M.moe_grouped_ffn(p, perm["X_perm"], perm["offsets"],
+                                                 dev["W_gate"], dev["W_up"],
+                                                 dev["W_down"], Y, ffn_ws), n, stream)
+    t_comb = _time_loop(lambda: M.moe_combine(p, Y, perm["dest_row"], w, o2),
+                        n, stream)
+    torch.cuda.synchronize()
+
+    a_b = 2 if wl.dtype == W.BF16 else 4
+    T, d, E, k, dff = wl.T, wl.d_model, wl.E, wl.top_k, wl.d_ff
+    ffn_flops = 6.0 * N * d * dff
+    ffn_tflops = ffn_flops / (t_ffn * 1e-3) / 1e12
+    bytes_route = T * d * a_b + E * d * 4 + T * k * 8
+    bytes_perm = T * d * a_b + N * d * a_b + T * k * 24 + N * 4
+    bytes_comb = N * d * 4 + T * d * 4 + T * k * 8
+    bytes_ffn = 3 * active * d * dff * a_b + N * d * a_b + N * d * 4
+
+    line = {
+        "metric": "MoE-layer tokens/s + grouped-GEMM TFLOP/s (% bf16 MFMA peak), "
+                  "Mixtral shape",
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == W.BF16 else "f32",
+        "data": "synthetic (seeded; random weights of the layer's shape)",
+        "config": {"workload": f"{wl.name}: one MoE FFN layer forward, T={T}, "
+                               f"d_model={d}, E={E}, top-{k}, SwiGLU d_ff={dff}, "
+                               f"{wl.dtype} weights/activations, fp32 router and "
+                               f"accumulation, fp32 output",
+                   "T": T, "d_model": d, "E": E, "top_k": k, "d_ff": dff,
+                   "capacity_factor": wl.capacity_factor,
+                   "gating": ["topk_then_softmax", "softmax_then_topk"][wl.gating]},
+        "roofline": {"bound": "mfma", "kernel": "grouped SwiGLU FFN "
+                     "(gate/up GEMM + SwiGLU epilogue, down GEMM)",
+                     "achieved": ffn_tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": ffn_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": None,
+                     "flops_per_launch": ffn_flops, "ms_per_launch": t_ffn},
+        "stages_ms": {"route": t_route, "permute": t_perm, "grouped_ffn": t_ffn,
+                      "combine": t_comb},
+        "stages_gbs": {"route": bytes_route / (t_route * 1e6),
+                       "permute": bytes_perm / (t_perm * 1e6),
+                       "combine": bytes_comb / (t_comb * 1e6),
+                       "grouped_ffn_weights_and_rows": bytes_ffn / (t_ffn * 1e6)},
+        "routing": {"kept_copies": N, "dropped": int(st[-1]),
+                    "active_experts": active,
+                    "max_over_mean_load": float(counts.max() / max(counts.mean(), 1e-9))},
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = _cpu_baseline(wl, dev, args.cpu_sample_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

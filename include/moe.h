@@ -1,0 +1,198 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) forward pass of one sparsely-gated
+ * mixture-of-experts FFN layer.
+ *
+ * The layer, as the method page states it ("Sparsely-Gated MoE 구현 관점에서
+ * 살펴보기: Router, Top-k, 부하 분산", section "순전파 과정(forward pass)은
+ * 디스패치와 결합(combine)을 포함" -- the five-step forward pipeline):
+ *   1. router logits  l = X @ W_r^T (+ bias)                    -> moe_route
+ *   2. top-k experts per token and their renormalised weights   -> moe_route
+ *   3. per-expert capacity slots (overflowing copies dropped)   -> moe_permute
+ *   4. permute token copies into expert-contiguous order        -> moe_permute
+ *   5. each expert's FFN on its rows, as one grouped GEMM       -> moe_grouped_ffn
+ *   6. un-permute and combine with the gate weights             -> moe_combine
+ * moe_forward runs all of them.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers (HIP device memory), row-major
+ *   and contiguous, 16-byte aligned.  Host pointers: only `const
+ *   moe_problem_t*`.
+ * - Weights are stored [E, out, in], so every product is A @ W^T:
+ *     W_r    [E, d_model]          fp32
+ *     W_gate [E, d_ff, d_model]    act dtype
+ *     W_up   [E, d_ff, d_model]    act dtype
+ *     W_down [E, d_model, d_ff]    act dtype
+ *   This is the packed one-tensor-per-projection layout of "MoonEP의 계획
+ *   코드를 직접 돌려봤습니다" (thakicloud.com), section "설치 및 통합".
+ * - Ownership: the caller owns every buffer, including the workspace.  The
+ *   library never allocates, frees or synchronises, and keeps no mutable
+ *   global state.  Calls on distinct streams with distinct buffers and
+ *   workspaces may run concurrently.
+ * - Every call only enqueues kernels on `stream` and returns; no host
+ *   synchronisation happens inside any call (no per-expert size is read
+ *   back: the grouped GEMM schedules its tiles from device-side offsets).
+ * - Errors: arguments are validated on the host before anything is
+ *   enqueued.  An invalid argument returns a negative status and writes
+ *   nothing.  A failed launch returns MOE_ERR_HIP.  Faults inside kernels
+ *   surface at the caller's next synchronisation.
+ * - Supported envelope: 0 <= T < 2^24, 1 <= top_k <= E <= 256, top_k <= 32,
+ *   d_model and d_ff multiples of 8 (16-byte rows), act/weight dtype pairs
+ *   (F32,F32) and (BF16,BF16), out_dtype F32 or BF16.  T == 0 is a valid
+ *   no-op.  Anything else is
+ *   MOE_ERR_UNSUPPORTED (or MOE_ERR_INVALID_ARG for nonsense such as a
+ *   negative size or a NULL required pointer).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* NULL required pointer, negative size, k > E */
+  MOE_ERR_UNSUPPORTED = -2, /* outside the supported envelope above */
+  MOE_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than required */
+  MOE_ERR_HIP = -4          /* a kernel launch failed */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+/* Order of softmax and top-k ("Sparsely-Gated MoE 구현 관점에서 살펴보기",
+ * section "Top-2 라우팅의 수치 예시": implementations either take the top-k
+ * and renormalise the selected logits with a softmax, or take a softmax over
+ * all experts first, then the top-k, then renormalise).  Selection is always
+ * on the logits (ties to the lower expert id). */
+typedef enum {
+  MOE_TOPK_THEN_SOFTMAX = 0, /* w_j = exp(l_j - m) / sum_sel exp(l - m) */
+  MOE_SOFTMAX_THEN_TOPK = 1  /* p = softmax(l over E); w_j = p_j / sum_sel p */
+} moe_gating_t;
+
+/* Shape of the problem (host struct, read synchronously during the call). */
+typedef struct {
+  int32_t T;               /* tokens (batch x sequence flattened)           */
+  int32_t d_model;         /* hidden size                                   */
+  int32_t E;               /* number of experts                             */
+  int32_t top_k;           /* experts per token                             */
+  int32_t d_ff;            /* expert FFN inner size                         */
+  float capacity_factor;   /* <= 0: unlimited; else C = min(T, ceil(cf*T*k/E)) */
+  moe_dtype_t act_dtype;   /* X, X_perm, H                                  */
+  moe_dtype_t w_dtype;     /* W_gate, W_up, W_down (W_r, bias: always fp32) */
+  moe_gating_t gating;
+  moe_dtype_t out_dtype;   /* out: F32 (no rounding beyond fp32) or BF16    */
+} moe_problem_t;
+
+/* Per-expert capacity C of the problem, or -1 when unlimited.  The capacity
+ * bounds how many token copies one expert takes ("Sparsely-Gated MoE 구현
+ * 관점에서 살펴보기", section "로드 밸런싱 손실과 용량은 별개"); the printed
+ * formula is lost, the reading is C = min(T, ceil(cf * T * k / E)). */
+int64_t moe_capacity(const moe_problem_t* p);
+
+/* R: static upper bound on the number of kept token copies, the row count
+ * of X_perm and Y_perm: T*k without capacity, else min(T*k, E*C). */
+int64_t moe_rows_bound(const moe_problem_t* p);
+
+/* Workspace bytes needed by moe_permute, moe_grouped_ffn and moe_forward
+ * (0 for an invalid problem).  Workspaces are plain device memory, 256-byte
+ * aligned, with no state kept between calls. */
+size_t moe_permute_workspace_bytes(const moe_problem_t* p);
+size_t moe_grouped_ffn_workspace_bytes(const moe_problem_t* p);
+size_t moe_workspace_bytes(const moe_problem_t* p);
+
+/* Step 1-2: router logits, top-k and gate weights.
+ * "Sparsely-Gated MoE 구현 관점에서 살펴보기", sections "Router를 텐서
+ * 형태에서 추적하기" (logits X @ W_r^T per token, T x E) and "Top-2 라우팅의
+ * 수치 예시" (top-k, renormalised weights).
+ *   X        [T, d_model]  act dtype
+ *   W_r      [E, d_model]  fp32
+ *   bias     [E] fp32, or NULL for none (added to the fp32 logits)
+ *   topk_idx [T, top_k] int32 out: expert ids, by descending logit, ties to
+ *                                  the lower id
+ *   topk_w   [T, top_k] fp32  out: gate weights (sum to 1 per token)
+ * Logits are accumulated in fp32 and never leave the chip. */
+moe_status_t moe_route(const moe_problem_t* p, const void* X, const float* W_r,
+                       const float* bias, int32_t* topk_idx, float* topk_w,
+                       hipStream_t stream);
+
+/* Step 3-4: histogram, capacity, offsets and the stable counting-sort
+ * permute.  Copy (t, j) of expert e = topk_idx[t, j] gets rank
+ * #{t' < t : e in topk_idx[t', :]}; it is kept iff rank < C and then goes to
+ * row expert_offsets[e] + rank.  ("Sparsely-Gated MoE 구현 관점에서
+ * 살펴보기", forward pipeline steps 2-3; counts and offsets are the
+ * tokens_per_expert and cu_seqlens of "MoonEP의 계획 코드를 직접
+ * 돌려봤습니다", section "설치 및 통합".)
+ *   X              [T, d_model] act dtype
+ *   topk_idx       [T, top_k] int32, every id in [0, E) (not checked on the
+ *                  device; ids out of range are undefined behaviour)
+ *   expert_counts  [E]   int32 out: copies routed to each expert (pre-capacity)
+ *   expert_offsets [E+1] int32 out: exclusive prefix sum of min(count, C)
+ *   num_dropped    [1]   int32 out: copies dropped by capacity
+ *   dest_row       [T, top_k] int32 out: row in X_perm, -1 if dropped
+ *   row_token      [R] int32 out: token of each row (rows >= offsets[E]
+ *                  are not written)
+ *   X_perm         [R, d_model] act dtype out: X_perm[r] = X[row_token[r]]
+ *   workspace      >= moe_permute_workspace_bytes(p) bytes */
+moe_status_t moe_permute(const moe_problem_t* p, const void* X,
+                         const int32_t* topk_idx, int32_t* expert_counts,
+                         int32_t* expert_offsets, int32_t* num_dropped,
+                         int32_t* dest_row, int32_t* row_token, void* X_perm,
+                         void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Step 5: every expert's SwiGLU FFN over its rows [offsets[e], offsets[e+1])
+ * of X_perm, as one grouped GEMM pair ("5.3 Expert Parallelism", section
+ * "최적화 2: GroupGEMM"; "Sparsely-Gated MoE 구현 관점에서 살펴보기",
+ * forward pipeline step 4):
+ *   Y[r] = (silu(X_perm[r] Wg_e^T) * (X_perm[r] Wu_e^T)) Wd_e^T
+ * with silu(z) = z / (1 + exp(-z)).  bf16 inputs use bf16 MFMA with fp32
+ * accumulation; the SwiGLU product is formed in fp32 and rounded once to
+ * the act dtype.
+ *   X_perm         [R, d_model] act dtype
+ *   expert_offsets [E+1] int32 (device; never read back to the host)
+ *   Y_perm         [R, d_model] fp32 out (rows >= offsets[E] not written)
+ *   workspace      >= moe_grouped_ffn_workspace_bytes(p) bytes */
+moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* X_perm,
+                             const int32_t* expert_offsets, const void* W_gate,
+                             const void* W_up, const void* W_down,
+                             float* Y_perm, void* workspace, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* Step 6: out[t] = sum over j ascending with dest_row[t, j] >= 0 of
+ * topk_w[t, j] * Y_perm[dest_row[t, j]], accumulated in fp32 and stored in
+ * out_dtype (one rounding when that is BF16).  A token with every copy dropped gets a zero row.
+ * ("Sparsely-Gated MoE 구현 관점에서 살펴보기", section "Router를 텐서
+ * 형태에서 추적하기": the output is the weighted sum of the selected
+ * experts' outputs; forward pipeline step 5: un-permute and combine.)
+ *   Y_perm   [R, d_model] fp32
+ *   dest_row [T, top_k] int32, topk_w [T, top_k] fp32
+ *   out      [T, d_model] out_dtype out */
+moe_status_t moe_combine(const moe_problem_t* p, const float* Y_perm,
+                         const int32_t* dest_row, const float* topk_w,
+                         void* out, hipStream_t stream);
+
+/* The whole layer: moe_route, moe_permute, moe_grouped_ffn, moe_combine in
+ * order on `stream`, intermediates carved from the workspace.
+ *   out   [T, d_model] out_dtype out
+ *   stats [E + (E+1) + 1] int32 out, or NULL: expert_counts | expert_offsets
+ *         | num_dropped (routing statistics for monitoring)
+ *   workspace >= moe_workspace_bytes(p) bytes */
+moe_status_t moe_forward(const moe_problem_t* p, const void* X,
+                         const float* W_r, const float* bias,
+                         const void* W_gate, const void* W_up,
+                         const void* W_down, void* out, int32_t* stats,
+                         void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Static string naming a status code. */
+const char* moe_status_string(moe_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,12 @@
+"""MI355X (gfx950) forward pass of one sparsely-gated MoE FFN layer.
+
+The layer runs in the HIP library libmoe_mi355x.so behind the C ABI of
+include/moe.h; this package is its ctypes binding (``binding``), the build
+script (``build``) and the seeded synthetic inputs (``workloads``).
+"""
+from .binding import (MOE_BF16, MOE_F32, MOE_SOFTMAX_THEN_TOPK,  # noqa: F401
+                      MOE_TOPK_THEN_SOFTMAX, MoeError, Problem, capacity,
+                      grouped_ffn_workspace_bytes, load, moe_combine,
+                      moe_forward, moe_grouped_ffn, moe_permute, moe_route,
+                      permute_workspace_bytes, problem, rows_bound,
+                      workspace_bytes)

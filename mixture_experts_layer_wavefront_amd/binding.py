@@ -1,0 +1,266 @@
+"""Thin ctypes binding of libmoe_mi355x.so (the C ABI in include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  torch supplies device memory and the current stream.  There is no
+fallback: if the library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_mi355x.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_WORKSPACE = -3
+MOE_ERR_HIP = -4
+
+MOE_F32 = 0
+MOE_BF16 = 1
+MOE_TOPK_THEN_SOFTMAX = 0
+MOE_SOFTMAX_THEN_TOPK = 1
+
+# every entry point declared in include/moe.h
+SYMBOLS = ("moe_capacity", "moe_rows_bound", "moe_permute_workspace_bytes",
+           "moe_grouped_ffn_workspace_bytes", "moe_workspace_bytes",
+           "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
+           "moe_forward", "moe_status_string")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+class Problem(ctypes.Structure):
+    """moe_problem_t."""
+    _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("d_ff", ctypes.c_int32), ("capacity_factor", ctypes.c_float),
+                ("act_dtype", ctypes.c_int), ("w_dtype", ctypes.c_int),
+                ("gating", ctypes.c_int), ("out_dtype", ctypes.c_int)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with "
+            "`python -m mixture_experts_layer_wavefront_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(Problem)
+    vp, sz, st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p
+    i64 = ctypes.c_int64
+    sig = {
+        "moe_capacity": (i64, [P]),
+        "moe_rows_bound": (i64, [P]),
+        "moe_permute_workspace_bytes": (sz, [P]),
+        "moe_grouped_ffn_workspace_bytes": (sz, [P]),
+        "moe_workspace_bytes": (sz, [P]),
+        "moe_route": (ctypes.c_int, [P, vp, vp, vp, vp, vp, st]),
+        "moe_permute": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       sz, st]),
+        "moe_grouped_ffn": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, sz,
+                                           st]),
+        "moe_combine": (ctypes.c_int, [P, vp, vp, vp, vp, st]),
+        "moe_forward": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       sz, st]),
+        "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().moe_status_string(int(status)).decode()
+
+
+def _dt(x):
+    return {"bf16": MOE_BF16, "f32": MOE_F32}[x] if isinstance(x, str) \
+        else int(x)
+
+
+def problem(T, d_model, E, top_k, d_ff, capacity_factor=0.0, dtype="bf16",
+            gating=MOE_TOPK_THEN_SOFTMAX, out_dtype="f32") -> Problem:
+    """moe_problem_t; `dtype` is the activation and expert-weight dtype,
+    `out_dtype` the dtype of the layer output (fp32 by default)."""
+    dt = _dt(dtype)
+    return Problem(int(T), int(d_model), int(E), int(top_k), int(d_ff),
+                   float(capacity_factor or 0.0), dt, dt, int(gating),
+                   _dt(out_dtype))
+
+
+def capacity(p: Problem) -> int:
+    return load().moe_capacity(ctypes.byref(p))
+
+
+def rows_bound(p: Problem) -> int:
+    return load().moe_rows_bound(ctypes.byref(p))
+
+
+def permute_workspace_bytes(p: Problem) -> int:
+    return load().moe_permute_workspace_bytes(ctypes.byref(p))
+
+
+def grouped_ffn_workspace_bytes(p: Problem) -> int:
+    return load().moe_grouped_ffn_workspace_bytes(ctypes.byref(p))
+
+
+def workspace_bytes(p: Problem) -> int:
+    return load().moe_workspace_bytes(ctypes.byref(p))
+
+
+# ---------------------------------------------------------------- torch side
+def _torch():
+    import torch
+    return torch
+
+
+def _act_dtype(p: Problem):
+    torch = _torch()
+    return torch.bfloat16 if p.act_dtype == MOE_BF16 else torch.float32
+
+
+def _out_dtype(p: Problem):
+    torch = _torch()
+    return torch.bfloat16 if p.out_dtype == MOE_BF16 else torch.float32
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status, where):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def _workspace(nbytes, device, workspace):
+    torch = _torch()
+    if workspace is not None:
+        return workspace
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def moe_route(p, X, W_r, bias=None, topk_idx=None, topk_w=None, stream=None):
+    """Router logits, top-k ids and gate weights.  Returns (topk_idx, topk_w)."""
+    torch = _torch()
+    dev = X.device
+    if topk_idx is None:
+        topk_idx = torch.empty((p.T, p.top_k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((p.T, p.top_k), dtype=torch.float32, device=dev)
+    _check(load().moe_route(
+        ctypes.byref(p), _ptr(X, _act_dtype(p), "X"),
+        _ptr(W_r, torch.float32, "W_r"), _ptr(bias, torch.float32, "bias"),
+        _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(topk_w, torch.float32, "topk_w"), _stream(stream)), "moe_route")
+    return topk_idx, topk_w
+
+
+def moe_permute(p, X, topk_idx, workspace=None, stream=None, out=None):
+    """Counts, offsets, drops, dest rows, inverse map and X_perm (dict)."""
+    torch = _torch()
+    dev = X.device
+    R = rows_bound(p)
+    o = out if out is not None else dict(
+        counts=torch.empty(p.E, dtype=torch.int32, device=dev),
+        offsets=torch.empty(p.E + 1, dtype=torch.int32, device=dev),
+        dropped=torch.empty(1, dtype=torch.int32, device=dev),
+        dest_row=torch.empty((p.T, p.top_k), dtype=torch.int32, device=dev),
+        row_token=torch.empty(max(R, 1), dtype=torch.int32, device=dev),
+        X_perm=torch.empty((max(R, 1), p.d_model), dtype=_act_dtype(p),
+                           device=dev))
+    ws = _workspace(permute_workspace_bytes(p), dev, workspace)
+    _check(load().moe_permute(
+        ctypes.byref(p), _ptr(X, _act_dtype(p), "X"),
+        _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(o["counts"], torch.int32), _ptr(o["offsets"], torch.int32),
+        _ptr(o["dropped"], torch.int32), _ptr(o["dest_row"], torch.int32),
+        _ptr(o["row_token"], torch.int32), _ptr(o["X_perm"], _act_dtype(p)),
+        _ptr(ws), ws.numel(), _stream(stream)), "moe_permute")
+    return o
+
+
+def moe_grouped_ffn(p, X_perm, offsets, W_gate, W_up, W_down, Y_perm=None,
+                    workspace=None, stream=None):
+    """Every expert's SwiGLU FFN over its rows.  Returns Y_perm (fp32)."""
+    torch = _torch()
+    dev = X_perm.device
+    R = rows_bound(p)
+    if Y_perm is None:
+        Y_perm = torch.empty((max(R, 1), p.d_model), dtype=torch.float32,
+                             device=dev)
+    ws = _workspace(grouped_ffn_workspace_bytes(p), dev, workspace)
+    wt = _act_dtype(p)
+    _check(load().moe_grouped_ffn(
+        ctypes.byref(p), _ptr(X_perm, wt, "X_perm"),
+        _ptr(offsets, torch.int32, "offsets"), _ptr(W_gate, wt, "W_gate"),
+        _ptr(W_up, wt, "W_up"), _ptr(W_down, wt, "W_down"),
+        _ptr(Y_perm, torch.float32, "Y_perm"), _ptr(ws), ws.numel(),
+        _stream(stream)), "moe_grouped_ffn")
+    return Y_perm
+
+
+def moe_combine(p, Y_perm, dest_row, topk_w, out=None, stream=None):
+    """Gate-weighted gather back to token order.  Returns out."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((p.T, p.d_model), dtype=_out_dtype(p),
+                          device=Y_perm.device)
+    _check(load().moe_combine(
+        ctypes.byref(p), _ptr(Y_perm, torch.float32, "Y_perm"),
+        _ptr(dest_row, torch.int32, "dest_row"),
+        _ptr(topk_w, torch.float32, "topk_w"),
+        _ptr(out, _out_dtype(p), "out"), _stream(stream)), "moe_combine")
+    return out
+
+
+def moe_forward(p, X, W_r, bias, W_gate, W_up, W_down, out=None, stats=None,
+                workspace=None, stream=None):
+    """The whole layer.  Returns out; `stats` (int32 [2E+2]) if given is
+    filled with counts | offsets | dropped."""
+    torch = _torch()
+    dev = X.device
+    if out is None:
+        out = torch.empty((p.T, p.d_model), dtype=_out_dtype(p), device=dev)
+    ws = _workspace(workspace_bytes(p), dev, workspace)
+    wt = _act_dtype(p)
+    _check(load().moe_forward(
+        ctypes.byref(p), _ptr(X, wt, "X"), _ptr(W_r, torch.float32, "W_r"),
+        _ptr(bias, torch.float32, "bias"), _ptr(W_gate, wt, "W_gate"),
+        _ptr(W_up, wt, "W_up"), _ptr(W_down, wt, "W_down"),
+        _ptr(out, _out_dtype(p), "out"), _ptr(stats, torch.int32, "stats"),
+        _ptr(ws),
+        ws.numel(), _stream(stream)), "moe_forward")
+    return out

@@ -1,0 +1,40 @@
+// Internal launchers of the gfx950 kernels (not part of the C ABI).
+// Each enqueues its kernels on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Router: fused fp32 logits tile, wavefront top-k, softmax.
+hipError_t launch_route(const void* X, bool x_bf16, const float* W_r,
+                        const float* bias, int T, int d, int E, int k,
+                        int gating, int32_t* topk_idx, float* topk_w,
+                        hipStream_t stream);
+
+// Permute, three kernels: per-block counts and in-block ranks; one-block
+// scan with capacity; destination rows and the row copy.
+size_t permute_scratch_bytes(int T, int k, int E);
+hipError_t launch_permute(const void* X, bool x_bf16, const int32_t* topk_idx,
+                          int T, int d, int E, int k, int C,
+                          int32_t* counts, int32_t* offsets, int32_t* dropped,
+                          int32_t* dest_row, int32_t* row_token, void* X_perm,
+                          void* scratch, hipStream_t stream);
+
+// Grouped SwiGLU FFN.  `small_m` picks the 32-row tile shape meant for few
+// rows per expert.
+size_t ffn_scratch_bytes(int64_t R, int E, int d_ff, bool bf16);
+hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
+                              const int32_t* offsets, const void* W_gate,
+                              const void* W_up, const void* W_down,
+                              int64_t R, int d, int E, int d_ff, bool small_m,
+                              float* Y_perm, void* scratch, hipStream_t stream);
+
+// Gate-weighted gather-combine back to token order.
+hipError_t launch_combine(const float* Y_perm, const int32_t* dest_row,
+                          const float* topk_w, int T, int d, int k,
+                          bool out_bf16, void* out, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,223 @@
+// C ABI of the MoE FFN layer forward pass: argument validation, workspace
+// carving and the kernel sequence.  Declarations and the contract of every
+// entry point are in include/moe.h.
+#include "moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxE = 256;
+constexpr int kMaxK = 32;
+constexpr int kMaxT = 1 << 24;
+constexpr int kMaxDim = 1 << 20;
+
+size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool is_bf16(const moe_problem_t* p) { return p->act_dtype == MOE_BF16; }
+bool out_bf16(const moe_problem_t* p) { return p->out_dtype == MOE_BF16; }
+size_t act_bytes(const moe_problem_t* p) { return is_bf16(p) ? 2 : 4; }
+
+moe_status_t validate(const moe_problem_t* p) {
+  if (p == nullptr) return MOE_ERR_INVALID_ARG;
+  if (p->T < 0 || p->d_model <= 0 || p->E <= 0 || p->top_k <= 0 || p->d_ff <= 0)
+    return MOE_ERR_INVALID_ARG;
+  if (p->top_k > p->E) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(p->capacity_factor)) return MOE_ERR_INVALID_ARG;
+  if (p->act_dtype != MOE_F32 && p->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (p->w_dtype != MOE_F32 && p->w_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (p->gating != MOE_TOPK_THEN_SOFTMAX && p->gating != MOE_SOFTMAX_THEN_TOPK)
+    return MOE_ERR_INVALID_ARG;
+  if (p->out_dtype != MOE_F32 && p->out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (p->E > kMaxE || p->top_k > kMaxK || p->T >= kMaxT) return MOE_ERR_UNSUPPORTED;
+  if (p->d_model % 8 != 0 || p->d_ff % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (p->d_model > kMaxDim || p->d_ff > kMaxDim) return MOE_ERR_UNSUPPORTED;
+  if (p->act_dtype != p->w_dtype) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// C as an int for the kernels: INT_MAX when unlimited.
+int capacity_int(const moe_problem_t* p) {
+  const int64_t C = moe_capacity(p);
+  return C < 0 ? INT_MAX : (int)C;
+}
+
+bool use_small_m(const moe_problem_t* p) {
+  // mean rows per expert, known on the host without reading device data
+  double mean = (double)p->T * p->top_k / p->E;
+  const int64_t C = moe_capacity(p);
+  if (C >= 0 && (double)C < mean) mean = (double)C;
+  return mean <= 64.0;
+}
+
+struct ForwardLayout {
+  size_t topk_idx, topk_w, perm_scratch, stats, dest_row, row_token, x_perm,
+      ffn_scratch, y_perm, total;
+};
+
+ForwardLayout forward_layout(const moe_problem_t* p) {
+  const size_t Tk = (size_t)p->T * p->top_k;
+  const size_t R = (size_t)moe_rows_bound(p);
+  ForwardLayout L{};
+  size_t o = 0;
+  L.topk_idx = o; o += a256(Tk * 4);
+  L.topk_w = o; o += a256(Tk * 4);
+  L.perm_scratch = o; o += a256(moe::permute_scratch_bytes(p->T, p->top_k, p->E));
+  L.stats = o; o += a256((size_t)(2 * p->E + 2) * 4);
+  L.dest_row = o; o += a256(Tk * 4);
+  L.row_token = o; o += a256(R * 4);
+  L.x_perm = o; o += a256(R * p->d_model * act_bytes(p));
+  L.ffn_scratch = o; o += a256(moe::ffn_scratch_bytes((int64_t)R, p->E, p->d_ff, is_bf16(p)));
+  L.y_perm = o; o += a256(R * p->d_model * 4);
+  L.total = o;
+  return L;
+}
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_capacity(const moe_problem_t* p) {
+  if (validate(p) != MOE_OK) return -1;
+  if (!(p->capacity_factor > 0.f)) return -1;
+  const double c = std::ceil((double)p->capacity_factor * p->T * p->top_k / p->E);
+  return c < (double)p->T ? (int64_t)c : (int64_t)p->T;
+}
+
+int64_t moe_rows_bound(const moe_problem_t* p) {
+  if (validate(p) != MOE_OK) return 0;
+  const int64_t Tk = (int64_t)p->T * p->top_k;
+  const int64_t C = moe_capacity(p);
+  if (C < 0) return Tk;
+  const int64_t EC = (int64_t)p->E * C;
+  return EC < Tk ? EC : Tk;
+}
+
+size_t moe_permute_workspace_bytes(const moe_problem_t* p) {
+  if (validate(p) != MOE_OK) return 0;
+  return a256(moe::permute_scratch_bytes(p->T, p->top_k, p->E));
+}
+
+size_t moe_grouped_ffn_workspace_bytes(const moe_problem_t* p) {
+  if (validate(p) != MOE_OK) return 0;
+  return a256(moe::ffn_scratch_bytes(moe_rows_bound(p), p->E, p->d_ff, is_bf16(p)));
+}
+
+size_t moe_workspace_bytes(const moe_problem_t* p) {
+  if (validate(p) != MOE_OK) return 0;
+  return forward_layout(p).total;
+}
+
+moe_status_t moe_route(const moe_problem_t* p, const void* X, const float* W_r,
+                       const float* bias, int32_t* topk_idx, float* topk_w,
+                       hipStream_t stream) {
+  moe_status_t st = validate(p);
+  if (st != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;
+  if (!X || !W_r || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_route(X, is_bf16(p), W_r, bias, p->T, p->d_model, p->E,
+                                      p->top_k, (int)p->gating, topk_idx, topk_w, stream));
+}
+
+moe_status_t moe_permute(const moe_problem_t* p, const void* X,
+                         const int32_t* topk_idx, int32_t* expert_counts,
+                         int32_t* expert_offsets, int32_t* num_dropped,
+                         int32_t* dest_row, int32_t* row_token, void* X_perm,
+                         void* workspace, size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = validate(p);
+  if (st != MOE_OK) return st;
+  if (!expert_counts || !expert_offsets || !num_dropped) return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && (!X || !topk_idx || !dest_row || !row_token || !X_perm))
+    return MOE_ERR_INVALID_ARG;
+  if (!workspace || ws_bytes < moe_permute_workspace_bytes(p)) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_permute(X, is_bf16(p), topk_idx, p->T, p->d_model, p->E,
+                                        p->top_k, capacity_int(p), expert_counts,
+                                        expert_offsets, num_dropped, dest_row, row_token,
+                                        X_perm, workspace, stream));
+}
+
+moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* X_perm,
+                             const int32_t* expert_offsets, const void* W_gate,
+                             const void* W_up, const void* W_down, float* Y_perm,
+                             void* workspace, size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = validate(p);
+  if (st != MOE_OK) return st;
+  const int64_t R = moe_rows_bound(p);
+  if (R == 0) return MOE_OK;
+  if (!X_perm || !expert_offsets || !W_gate || !W_up || !W_down || !Y_perm)
+    return MOE_ERR_INVALID_ARG;
+  if (!workspace || ws_bytes < moe_grouped_ffn_workspace_bytes(p)) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_grouped_ffn(X_perm, is_bf16(p), expert_offsets, W_gate, W_up,
+                                            W_down, R, p->d_model, p->E, p->d_ff,
+                                            use_small_m(p), Y_perm, workspace, stream));
+}
+
+moe_status_t moe_combine(const moe_problem_t* p, const float* Y_perm,
+                         const int32_t* dest_row, const float* topk_w, void* out,
+                         hipStream_t stream) {
+  moe_status_t st = validate(p);
+  if (st != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;
+  if (!Y_perm || !dest_row || !topk_w || !out) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_combine(Y_perm, dest_row, topk_w, p->T, p->d_model,
+                                        p->top_k, out_bf16(p), out, stream));
+}
+
+moe_status_t moe_forward(const moe_problem_t* p, const void* X, const float* W_r,
+                         const float* bias, const void* W_gate, const void* W_up,
+                         const void* W_down, void* out, int32_t* stats,
+                         void* workspace, size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = validate(p);
+  if (st != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;
+  if (!X || !W_r || !W_gate || !W_up || !W_down || !out) return MOE_ERR_INVALID_ARG;
+  const ForwardLayout L = forward_layout(p);
+  if (!workspace || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* topk_idx = reinterpret_cast<int32_t*>(ws + L.topk_idx);
+  float* topk_w = reinterpret_cast<float*>(ws + L.topk_w);
+  int32_t* st_buf = stats ? stats : reinterpret_cast<int32_t*>(ws + L.stats);
+  int32_t* counts = st_buf;
+  int32_t* offsets = st_buf + p->E;
+  int32_t* dropped = st_buf + 2 * p->E + 1;
+  int32_t* dest_row = reinterpret_cast<int32_t*>(ws + L.dest_row);
+  int32_t* row_token = reinterpret_cast<int32_t*>(ws + L.row_token);
+  void* x_perm = ws + L.x_perm;
+  float* y_perm = reinterpret_cast<float*>(ws + L.y_perm);
+  const bool bf = is_bf16(p);
+
+  hipError_t e = moe::launch_route(X, bf, W_r, bias, p->T, p->d_model, p->E, p->top_k,
+                                   (int)p->gating, topk_idx, topk_w, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_permute(X, bf, topk_idx, p->T, p->d_model, p->E, p->top_k,
+                          capacity_int(p), counts, offsets, dropped, dest_row, row_token,
+                          x_perm, ws + L.perm_scratch, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_grouped_ffn(x_perm, bf, offsets, W_gate, W_up, W_down, moe_rows_bound(p),
+                              p->d_model, p->E, p->d_ff, use_small_m(p), y_perm,
+                              ws + L.ffn_scratch, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_combine(y_perm, dest_row, topk_w, p->T, p->d_model, p->top_k,
+                          out_bf16(p), out, stream);
+  return hip_status(e);
+}
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: outside the supported envelope";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a kernel launch failed";
+  }
+  return "unknown moe_status_t";
+}
+
+}  // extern "C"

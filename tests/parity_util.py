@@ -1,0 +1,136 @@
+"""Helpers shared by the parity tests: run the HIP path through the C ABI and
+compare each stage with the CPU oracle at the stated tolerances.
+
+Tolerances (fixed by the layer's accuracy contract):
+  * routing ids, counts, offsets, dest rows, inverse map, drops: bit-exact,
+    except tokens whose k-th and (k+1)-th fp32 logits are within 1e-5 (near
+    ties), which are reported and excluded;
+  * fp32 outputs: max_i |g_i - o_i| / max(|o_i|, rms(o)) <= 1e-4;
+  * bf16 layers (bf16 inputs and weights, fp32 accumulation):
+    max |g - o| / rms(o) <= 2e-2, with rms over the output rows of tokens
+    that kept at least one copy (rows of fully dropped tokens must be exact
+    zeros and are checked separately).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+from mixture_experts_layer_wavefront_amd import binding as B
+from mixture_experts_layer_wavefront_amd import workloads as W
+
+FP32_TOL = 1e-4
+BF16_TOL = 2e-2
+GATE_W_TOL = 1e-4
+
+
+def rms(o):
+    return float(np.sqrt(np.mean(np.square(o)))) if o.size else 0.0
+
+
+def fp32_err(g, o):
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    if o.size == 0:
+        return 0.0
+    den = np.maximum(np.abs(o), max(rms(o), 1e-300))
+    return float(np.max(np.abs(g - o) / den))
+
+
+def bf16_err(g, o):
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    if o.size == 0:
+        return 0.0
+    r = rms(o)
+    return float(np.max(np.abs(g - o)) / (r if r > 0 else 1.0))
+
+
+def out_err(wl: W.Workload, g, o):
+    return fp32_err(g, o) if wl.dtype == W.F32 else bf16_err(g, o)
+
+
+def out_tol(wl: W.Workload):
+    return FP32_TOL if wl.dtype == W.F32 else BF16_TOL
+
+
+def problem_of(wl: W.Workload, out_dtype="f32"):
+    return B.problem(wl.T, wl.d_model, wl.E, wl.top_k, wl.d_ff,
+                     wl.capacity_factor, wl.dtype, wl.gating, out_dtype)
+
+
+def oracle_capacity(wl: W.Workload):
+    # the ABI carries the capacity factor as fp32
+    cf = float(np.float32(wl.capacity_factor))
+    return O.capacity(wl.T, wl.top_k, wl.E, cf if cf > 0 else None)
+
+
+def to_device(host: dict, wl: W.Workload, device="cuda"):
+    tdt = torch.bfloat16 if wl.dtype == W.BF16 else torch.float32
+    d = {}
+    for key in ("X", "W_gate", "W_up", "W_down"):
+        d[key] = torch.from_numpy(host[key]).to(device).to(tdt).contiguous()
+    d["W_r"] = torch.from_numpy(host["W_r"]).to(device)
+    d["bias"] = None if host["bias"] is None else \
+        torch.from_numpy(host["bias"]).to(device)
+    return d
+
+
+def host_f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check_routing(g_idx, g_w, o_idx, o_w, near_tie, logits):
+    """Per non-near-tie token: same expert set (bit-exact ids), gate weights
+    within GATE_W_TOL relative, slot order descending in the oracle's
+    logits.  Returns (n_excluded, tokens whose expert set differs)."""
+    g_idx = np.asarray(g_idx)
+    g_w = np.asarray(g_w, np.float64)
+    T, k = g_idx.shape
+    bad, differ = [], []
+    for t in range(T):
+        gs, os_ = set(g_idx[t].tolist()), set(o_idx[t].tolist())
+        if gs != os_:
+            differ.append(t)
+            if not near_tie[t]:
+                bad.append(t)
+            continue
+        if near_tie[t]:
+            continue
+        ow = dict(zip(o_idx[t].tolist(), o_w[t].tolist()))
+        for j in range(k):
+            e = int(g_idx[t, j])
+            if abs(g_w[t, j] - ow[e]) > GATE_W_TOL * max(abs(ow[e]), 1e-30):
+                bad.append(t)
+                break
+        sel = logits[t, g_idx[t]].astype(np.float64)
+        if np.any(np.diff(sel) > O.NEAR_TIE_GAP):
+            bad.append(t)
+    assert not bad, f"routing mismatch at tokens {bad[:10]} (of {len(bad)})"
+    return int(np.sum(near_tie)), differ
+
+
+def check_permute(res, g_idx, E, C, T, k):
+    """Oracle assignment of the GPU's own ids must match bit-exactly."""
+    a = O.assign(np.asarray(g_idx), E, C)
+    np.testing.assert_array_equal(res["counts"].cpu().numpy(), a["counts"])
+    np.testing.assert_array_equal(res["offsets"].cpu().numpy(), a["offsets"])
+    assert int(res["dropped"].cpu().item()) == a["dropped"]
+    np.testing.assert_array_equal(res["dest_row"].cpu().numpy(), a["dest"])
+    N = int(a["offsets"][-1])
+    np.testing.assert_array_equal(res["row_token"][:N].cpu().numpy(),
+                                  a["row_token"])
+    return a
+
+
+def run_stages(p, dev):
+    """Run the four stage entry points on device inputs; returns dict."""
+    idx, w = B.moe_route(p, dev["X"], dev["W_r"], dev["bias"])
+    perm = B.moe_permute(p, dev["X"], idx)
+    Y = B.moe_grouped_ffn(p, perm["X_perm"], perm["offsets"], dev["W_gate"],
+                          dev["W_up"], dev["W_down"])
+    out = B.moe_combine(p, Y, perm["dest_row"], w)
+    torch.cuda.synchronize()
+    return dict(idx=idx, w=w, Y=Y, out=out, **perm)

@@ -1,0 +1,137 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point
+include/moe.h declares, and rejects bad arguments on the host before any
+device work (these paths make no HIP call, so they run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_wavefront_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load()
+    names = _declared()
+    assert set(names) == set(B.SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in (B.MOE_OK, B.MOE_ERR_INVALID_ARG, B.MOE_ERR_UNSUPPORTED,
+              B.MOE_ERR_WORKSPACE, B.MOE_ERR_HIP):
+        assert B.status_string(s).startswith("MOE_")
+
+
+def test_capacity_and_rows_bound():
+    p = B.problem(16384, 2048, 128, 8, 768, 1.25)
+    assert B.capacity(p) == 1280
+    assert B.rows_bound(p) == min(16384 * 8, 128 * 1280)
+    p = B.problem(100, 64, 8, 2, 64, 0.5)           # C = ceil(12.5) = 13
+    assert B.capacity(p) == 13 and B.rows_bound(p) == 8 * 13
+    p = B.problem(10, 64, 4, 2, 64, 100.0)          # capped at T
+    assert B.capacity(p) == 10 and B.rows_bound(p) == 20
+    p = B.problem(4096, 4096, 8, 2, 14336)
+    assert B.capacity(p) == -1 and B.rows_bound(p) == 8192
+
+
+def test_workspace_sizes_cover_the_intermediates():
+    p = B.problem(4096, 7168, 256, 8, 2048, 0.0, "bf16", 1)
+    R = B.rows_bound(p)
+    ws = B.workspace_bytes(p)
+    # X_perm (bf16) + H (bf16) + Y_perm (fp32) at least
+    assert ws >= R * 7168 * 2 + R * 2048 * 2 + R * 7168 * 4
+    assert B.grouped_ffn_workspace_bytes(p) >= R * 2048 * 2
+    assert B.permute_workspace_bytes(p) >= 4096 * 8 * 4
+    assert ws % 256 == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=8, d_model=64, E=4, top_k=5, d_ff=64), B.MOE_ERR_INVALID_ARG),
+    (dict(T=-1, d_model=64, E=4, top_k=2, d_ff=64), B.MOE_ERR_INVALID_ARG),
+    (dict(T=8, d_model=0, E=4, top_k=2, d_ff=64), B.MOE_ERR_INVALID_ARG),
+    (dict(T=8, d_model=60, E=4, top_k=2, d_ff=64), B.MOE_ERR_UNSUPPORTED),
+    (dict(T=8, d_model=64, E=4, top_k=2, d_ff=20), B.MOE_ERR_UNSUPPORTED),
+    (dict(T=8, d_model=64, E=300, top_k=2, d_ff=64), B.MOE_ERR_UNSUPPORTED),
+    (dict(T=8, d_model=64, E=64, top_k=40, d_ff=64), B.MOE_ERR_UNSUPPORTED),
+])
+def test_invalid_problems_rejected(kw, status):
+    lib = B.load()
+    p = B.problem(**kw)
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    r = lib.moe_route(ctypes.byref(p), fake, fake, None, fake, fake, None)
+    assert r == status
+    r = lib.moe_forward(ctypes.byref(p), fake, fake, None, fake, fake, fake,
+                        fake, None, fake, 1 << 40, None)
+    assert r == status
+    assert lib.moe_workspace_bytes(ctypes.byref(p)) == 0
+
+
+def test_mixed_dtypes_and_bad_enums_rejected():
+    lib = B.load()
+    p = B.problem(8, 64, 4, 2, 64)
+    p.w_dtype = B.MOE_F32
+    assert lib.moe_route(ctypes.byref(p), None, None, None, None, None,
+                         None) == B.MOE_ERR_UNSUPPORTED
+    p = B.problem(8, 64, 4, 2, 64)
+    p.gating = 7
+    assert lib.moe_route(ctypes.byref(p), None, None, None, None, None,
+                         None) == B.MOE_ERR_INVALID_ARG
+    p = B.problem(8, 64, 4, 2, 64, float("nan"))
+    assert lib.moe_route(ctypes.byref(p), None, None, None, None, None,
+                         None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(None, None, None, None, None, None,
+                         None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_null_pointers_and_small_workspace_rejected():
+    lib = B.load()
+    p = B.problem(8, 64, 4, 2, 64)
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.moe_route(ctypes.byref(p), None, fake, None, fake, fake,
+                         None) == B.MOE_ERR_INVALID_ARG
+    need = lib.moe_permute_workspace_bytes(ctypes.byref(p))
+    r = lib.moe_permute(ctypes.byref(p), fake, fake, fake, fake, fake, fake,
+                        fake, fake, fake, need - 1, None)
+    assert r == B.MOE_ERR_WORKSPACE
+    r = lib.moe_permute(ctypes.byref(p), fake, fake, fake, fake, fake, fake,
+                        fake, fake, None, need, None)
+    assert r == B.MOE_ERR_WORKSPACE
+    need = lib.moe_workspace_bytes(ctypes.byref(p))
+    r = lib.moe_forward(ctypes.byref(p), fake, fake, None, fake, fake, fake,
+                        fake, None, fake, need - 1, None)
+    assert r == B.MOE_ERR_WORKSPACE
+    need = lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(p))
+    r = lib.moe_grouped_ffn(ctypes.byref(p), fake, fake, fake, fake, fake,
+                            fake, fake, need - 1, None)
+    assert r == B.MOE_ERR_WORKSPACE
+
+
+def test_empty_batch_is_a_noop_without_device_work():
+    lib = B.load()
+    p = B.problem(0, 64, 4, 2, 64)
+    assert lib.moe_forward(ctypes.byref(p), None, None, None, None, None,
+                           None, None, None, None, 0, None) == B.MOE_OK
+    assert lib.moe_route(ctypes.byref(p), None, None, None, None, None,
+                         None) == B.MOE_OK
+    assert lib.moe_combine(ctypes.byref(p), None, None, None, None,
+                           None) == B.MOE_OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    p = B.problem(8, 64, 4, 2, 64)
+    X = torch.zeros((8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        B.moe_route(p, X, torch.zeros((4, 64)), topk_idx=X, topk_w=X)
