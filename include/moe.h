@@ -99,9 +99,11 @@ int64_t moe_capacity(const moe_problem_t* p);
  * of X_perm and Y_perm: T*k without capacity, else min(T*k, E*C). */
 int64_t moe_rows_bound(const moe_problem_t* p);
 
-/* Workspace bytes needed by moe_permute, moe_grouped_ffn and moe_forward
- * (0 for an invalid problem).  Workspaces are plain device memory, 256-byte
- * aligned, with no state kept between calls. */
+/* Workspace bytes needed by moe_route, moe_permute, moe_grouped_ffn and
+ * moe_forward (0 for an invalid problem; moe_route needs none for fp32
+ * layers).  Workspaces are plain device memory, 256-byte aligned, with no
+ * state kept between calls. */
+size_t moe_route_workspace_bytes(const moe_problem_t* p);
 size_t moe_permute_workspace_bytes(const moe_problem_t* p);
 size_t moe_grouped_ffn_workspace_bytes(const moe_problem_t* p);
 size_t moe_workspace_bytes(const moe_problem_t* p);
@@ -116,10 +118,15 @@ size_t moe_workspace_bytes(const moe_problem_t* p);
  *   topk_idx [T, top_k] int32 out: expert ids, by descending logit, ties to
  *                                  the lower id
  *   topk_w   [T, top_k] fp32  out: gate weights (sum to 1 per token)
- * Logits are accumulated in fp32 and never leave the chip. */
+ *   workspace >= moe_route_workspace_bytes(p) bytes (may be NULL when that
+ *            is 0)
+ * Logits are fp32.  bf16 layers: X is exactly bf16 and W_r is split exactly
+ * into three bf16 terms, so the matrix cores form every product exactly and
+ * accumulate in fp32; partial sums over K-slices are added in a fixed order.
+ * fp32 layers: fp32 FMA accumulation. */
 moe_status_t moe_route(const moe_problem_t* p, const void* X, const float* W_r,
                        const float* bias, int32_t* topk_idx, float* topk_w,
-                       hipStream_t stream);
+                       void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Step 3-4: histogram, capacity, offsets and the stable counting-sort
  * permute.  Copy (t, j) of expert e = topk_idx[t, j] gets rank

@@ -8,5 +8,6 @@ from .binding import (MOE_BF16, MOE_F32, MOE_SOFTMAX_THEN_TOPK,  # noqa: F401
                       MOE_TOPK_THEN_SOFTMAX, MoeError, Problem, capacity,
                       grouped_ffn_workspace_bytes, load, moe_combine,
                       moe_forward, moe_grouped_ffn, moe_permute, moe_route,
-                      permute_workspace_bytes, problem, rows_bound,
+                      permute_workspace_bytes, problem, route_workspace_bytes,
+                      rows_bound,
                       workspace_bytes)

@@ -25,7 +25,8 @@ MOE_TOPK_THEN_SOFTMAX = 0
 MOE_SOFTMAX_THEN_TOPK = 1
 
 # every entry point declared in include/moe.h
-SYMBOLS = ("moe_capacity", "moe_rows_bound", "moe_permute_workspace_bytes",
+SYMBOLS = ("moe_capacity", "moe_rows_bound", "moe_route_workspace_bytes",
+           "moe_permute_workspace_bytes",
            "moe_grouped_ffn_workspace_bytes", "moe_workspace_bytes",
            "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
            "moe_forward", "moe_status_string")
@@ -65,10 +66,11 @@ def load(path: str = LIB_PATH):
     sig = {
         "moe_capacity": (i64, [P]),
         "moe_rows_bound": (i64, [P]),
+        "moe_route_workspace_bytes": (sz, [P]),
         "moe_permute_workspace_bytes": (sz, [P]),
         "moe_grouped_ffn_workspace_bytes": (sz, [P]),
         "moe_workspace_bytes": (sz, [P]),
-        "moe_route": (ctypes.c_int, [P, vp, vp, vp, vp, vp, st]),
+        "moe_route": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, sz, st]),
         "moe_permute": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        sz, st]),
         "moe_grouped_ffn": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, sz,
@@ -111,6 +113,10 @@ def capacity(p: Problem) -> int:
 
 def rows_bound(p: Problem) -> int:
     return load().moe_rows_bound(ctypes.byref(p))
+
+
+def route_workspace_bytes(p: Problem) -> int:
+    return load().moe_route_workspace_bytes(ctypes.byref(p))
 
 
 def permute_workspace_bytes(p: Problem) -> int:
@@ -172,7 +178,8 @@ def _workspace(nbytes, device, workspace):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
-def moe_route(p, X, W_r, bias=None, topk_idx=None, topk_w=None, stream=None):
+def moe_route(p, X, W_r, bias=None, topk_idx=None, topk_w=None,
+              workspace=None, stream=None):
     """Router logits, top-k ids and gate weights.  Returns (topk_idx, topk_w)."""
     torch = _torch()
     dev = X.device
@@ -180,11 +187,13 @@ def moe_route(p, X, W_r, bias=None, topk_idx=None, topk_w=None, stream=None):
         topk_idx = torch.empty((p.T, p.top_k), dtype=torch.int32, device=dev)
     if topk_w is None:
         topk_w = torch.empty((p.T, p.top_k), dtype=torch.float32, device=dev)
+    ws = _workspace(route_workspace_bytes(p), dev, workspace)
     _check(load().moe_route(
         ctypes.byref(p), _ptr(X, _act_dtype(p), "X"),
         _ptr(W_r, torch.float32, "W_r"), _ptr(bias, torch.float32, "bias"),
         _ptr(topk_idx, torch.int32, "topk_idx"),
-        _ptr(topk_w, torch.float32, "topk_w"), _stream(stream)), "moe_route")
+        _ptr(topk_w, torch.float32, "topk_w"), _ptr(ws), ws.numel(),
+        _stream(stream)), "moe_route")
     return topk_idx, topk_w
 
 

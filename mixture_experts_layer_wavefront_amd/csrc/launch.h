@@ -8,11 +8,13 @@
 
 namespace moe {
 
-// Router: fused fp32 logits tile, wavefront top-k, softmax.
+// Router: logits (bf16 X: split-bf16 MFMA with partial sums in `scratch`;
+// fp32 X: fused FMA kernel, no scratch), wavefront top-k, softmax.
+size_t route_scratch_bytes(int T, int E, int d, bool x_bf16);
 hipError_t launch_route(const void* X, bool x_bf16, const float* W_r,
                         const float* bias, int T, int d, int E, int k,
                         int gating, int32_t* topk_idx, float* topk_w,
-                        hipStream_t stream);
+                        void* scratch, hipStream_t stream);
 
 // Permute, three kernels: per-block counts and in-block ranks; one-block
 // scan with capacity; destination rows and the row copy.

@@ -56,8 +56,8 @@ bool use_small_m(const moe_problem_t* p) {
 }
 
 struct ForwardLayout {
-  size_t topk_idx, topk_w, perm_scratch, stats, dest_row, row_token, x_perm,
-      ffn_scratch, y_perm, total;
+  size_t topk_idx, topk_w, route_scratch, perm_scratch, stats, dest_row, row_token,
+      x_perm, ffn_scratch, y_perm, total;
 };
 
 ForwardLayout forward_layout(const moe_problem_t* p) {
@@ -67,6 +67,7 @@ ForwardLayout forward_layout(const moe_problem_t* p) {
   size_t o = 0;
   L.topk_idx = o; o += a256(Tk * 4);
   L.topk_w = o; o += a256(Tk * 4);
+  L.route_scratch = o; o += a256(moe::route_scratch_bytes(p->T, p->E, p->d_model, is_bf16(p)));
   L.perm_scratch = o; o += a256(moe::permute_scratch_bytes(p->T, p->top_k, p->E));
   L.stats = o; o += a256((size_t)(2 * p->E + 2) * 4);
   L.dest_row = o; o += a256(Tk * 4);
@@ -100,6 +101,11 @@ int64_t moe_rows_bound(const moe_problem_t* p) {
   return EC < Tk ? EC : Tk;
 }
 
+size_t moe_route_workspace_bytes(const moe_problem_t* p) {
+  if (validate(p) != MOE_OK) return 0;
+  return a256(moe::route_scratch_bytes(p->T, p->E, p->d_model, is_bf16(p)));
+}
+
 size_t moe_permute_workspace_bytes(const moe_problem_t* p) {
   if (validate(p) != MOE_OK) return 0;
   return a256(moe::permute_scratch_bytes(p->T, p->top_k, p->E));
@@ -117,13 +123,16 @@ size_t moe_workspace_bytes(const moe_problem_t* p) {
 
 moe_status_t moe_route(const moe_problem_t* p, const void* X, const float* W_r,
                        const float* bias, int32_t* topk_idx, float* topk_w,
-                       hipStream_t stream) {
+                       void* workspace, size_t ws_bytes, hipStream_t stream) {
   moe_status_t st = validate(p);
   if (st != MOE_OK) return st;
   if (p->T == 0) return MOE_OK;
   if (!X || !W_r || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe_route_workspace_bytes(p);
+  if (need > 0 && (!workspace || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_route(X, is_bf16(p), W_r, bias, p->T, p->d_model, p->E,
-                                      p->top_k, (int)p->gating, topk_idx, topk_w, stream));
+                                      p->top_k, (int)p->gating, topk_idx, topk_w, workspace,
+                                      stream));
 }
 
 moe_status_t moe_permute(const moe_problem_t* p, const void* X,
@@ -194,7 +203,8 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* X, const float* W_r
   const bool bf = is_bf16(p);
 
   hipError_t e = moe::launch_route(X, bf, W_r, bias, p->T, p->d_model, p->E, p->top_k,
-                                   (int)p->gating, topk_idx, topk_w, stream);
+                                   (int)p->gating, topk_idx, topk_w, ws + L.route_scratch,
+                                   stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_permute(X, bf, topk_idx, p->T, p->d_model, p->E, p->top_k,
                           capacity_int(p), counts, offsets, dropped, dest_row, row_token,

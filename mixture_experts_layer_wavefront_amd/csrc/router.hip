@@ -8,14 +8,18 @@
 // by top-k and renormalisation) and "pure Python으로 Top-k Router
 // 확인하기" (the largest selected logit is subtracted before exponentiating).
 //
-// One workgroup (4 wavefronts) owns TT tokens and all E <= 256 experts.  The
-// [TT x E] logit tile is accumulated in registers from LDS-staged fp32
-// slices of X and W_r, then parked in LDS; it never goes to HBM.  Each
-// wavefront then takes one token at a time: every lane holds up to four of
-// the E logits, and k rounds of a 64-lane butterfly argmax (ties to the
-// lower expert id) pick the experts in descending-logit order.
+// bf16 layers: the logits run on the matrix cores (exact three-way bf16 split
+// of W_r, K split over workgroups), then one wavefront per token adds the
+// partial logits and the bias and takes the top-k.  fp32 layers: one fused
+// kernel accumulates a [TT x E] logit tile with fp32 FMAs from LDS-staged
+// slices of X and W_r and keeps it in LDS for the top-k.  The top-k itself:
+// every lane holds up to four of the E logits, and k rounds of a 64-lane
+// butterfly argmax (ties to the lower expert id) pick the experts in
+// descending-logit order.
 #include "common.h"
 #include "launch.h"
+
+#include <algorithm>
 
 namespace moe {
 namespace {
@@ -47,7 +51,64 @@ struct XLoad<uint16_t> {
   }
 };
 
-// TX threads across experts (expert e = tx + TX*j, j < RE), TY = 256/TX
+// Top-k of one token's logits held across a wavefront (lane l holds experts
+// l, l+64, ...; -inf beyond E), then its gate weights; lanes j < k store slot
+// j.  k rounds of a 64-lane butterfly argmax pick the experts in descending
+// logit order, ties to the lower id.
+template <int VPL>
+__device__ __forceinline__ void topk_softmax_store(float (&v)[VPL], int E, int k, int gating,
+                                                   int lane, int32_t* __restrict__ idx_out,
+                                                   float* __restrict__ w_out) {
+  // softmax over all experts needs the untouched logits: its denominator first
+  float M = v[0];
+#pragma unroll
+  for (int i = 1; i < VPL; ++i) M = fmaxf(M, v[i]);
+  M = wave_max(M);
+  float Z = 0.f;
+  if (gating != 0) {
+    float z = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (lane + kWave * i < E) z += expf(v[i] - M);
+    Z = wave_sum(z);
+  }
+  float my_s = -INFINITY;
+  int my_id = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = v[0];
+    int be = lane;
+#pragma unroll
+    for (int i = 1; i < VPL; ++i)
+      if (v[i] > bv) { bv = v[i]; be = lane + kWave * i; }
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oe = __shfl_xor(be, o, kWave);
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+    }
+    if (lane == j) { my_s = bv; my_id = be; }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (be == lane + kWave * i) v[i] = -INFINITY;
+  }
+  float w;
+  if (gating == 0) {
+    // softmax over the selected logits, shifted by the largest of them
+    const float ex = (lane < k) ? expf(my_s - M) : 0.f;
+    w = ex / wave_sum(ex);
+  } else {
+    // softmax over all experts, then renormalised over the selected ones
+    const float pj = (lane < k) ? expf(my_s - M) / Z : 0.f;
+    w = pj / wave_sum(pj);
+  }
+  if (lane < k) {
+    idx_out[lane] = my_id;
+    w_out[lane] = w;
+  }
+}
+
+// fp32 layers: one fused kernel.  TX threads across experts (expert
+// e = tx + TX*j, j < RE), TY = 256/TX
 // threads across tokens (token row = ty + TY*i, i < RT).
 template <int TX, int RE, int RT, typename XT>
 __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(
@@ -138,46 +199,197 @@ __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(
       const int e = lane + kWave * i;
       v[i] = (e < E) ? Ls[row][e] : -INFINITY;
     }
-    float my_s = -INFINITY;
-    int my_id = 0;
-    for (int j = 0; j < k; ++j) {
-      float bv = v[0];
-      int be = lane;
+    topk_softmax_store<VPL>(v, E, k, gating, lane, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
+  }
+}
+
+// ---- bf16 layers: logits on the matrix cores --------------------------------
+// X is exactly bf16.  W_r (fp32) is split exactly into three bf16 planes,
+// W_r = hi + mid + lo (hi and mid truncate, lo holds the last 8 bits), so
+// X W_r^T = X hi^T + X mid^T + X lo^T with every product exact in fp32; the
+// v_mfma_f32_16x16x32_bf16 sums are fp32.  The K dimension is split over
+// S workgroups per token tile for parallelism; a select kernel adds the S
+// partial logits in a fixed order (then the bias) and takes the top-k.
+
+constexpr int kRtTok = 128;  // tokens per logits workgroup (4 waves x 32)
+constexpr int kRtK = 32;     // K per stage: one 16x16x32 MFMA k-step
+
+__device__ __forceinline__ uint32_t rt_swz(uint32_t r) { return ((r >> 1) ^ (r >> 3)) & 3u; }
+
+// W_r [E, d] fp32 -> Wsplit [3][EP][d32] bf16 (zero rows e >= E, zero k >= d)
+__global__ __launch_bounds__(256) void router_split_kernel(
+    const float* __restrict__ W_r, int E, int d, int EP, int d32,
+    uint16_t* __restrict__ Wsplit) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // 8 k per thread
+  const int per_row = d32 / 8;
+  if (i >= (int64_t)EP * per_row) return;
+  const int e = (int)(i / per_row), k0 = (int)(i % per_row) * 8;
+  uint32_t hw[4] = {0, 0, 0, 0}, mw[4] = {0, 0, 0, 0}, lw[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int i = 1; i < VPL; ++i)
-        if (v[i] > bv) { bv = v[i]; be = lane + kWave * i; }
-#pragma unroll
-      for (int o = kWave / 2; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, kWave);
-        const int oe = __shfl_xor(be, o, kWave);
-        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-      }
-      if (lane == j) { my_s = bv; my_id = be; }
-#pragma unroll
-      for (int i = 0; i < VPL; ++i)
-        if (be == lane + kWave * i) v[i] = -INFINITY;
+  for (int j = 0; j < 8; ++j) {
+    const int kk = k0 + j;
+    const float w = (e < E && kk < d) ? W_r[(int64_t)e * d + kk] : 0.f;
+    const float hi = __uint_as_float(__float_as_uint(w) & 0xFFFF0000u);
+    const float r1 = w - hi;  // exact
+    const float mid = __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
+    const float r2 = r1 - mid;  // exact, <= 8 significant bits: bf16 holds it
+    const uint32_t sh = (j & 1) * 16;
+    hw[j >> 1] |= (__float_as_uint(hi) >> 16) << sh;
+    mw[j >> 1] |= (__float_as_uint(mid) >> 16) << sh;
+    lw[j >> 1] |= (uint32_t)f32_to_bf16_bits(r2) << sh;
+  }
+  const int64_t plane = (int64_t)EP * d32;
+  const int64_t o = (int64_t)e * d32 + k0;
+  *reinterpret_cast<i32x4*>(Wsplit + o) = i32x4{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3]};
+  *reinterpret_cast<i32x4*>(Wsplit + plane + o) = i32x4{(int)mw[0], (int)mw[1], (int)mw[2], (int)mw[3]};
+  *reinterpret_cast<i32x4*>(Wsplit + 2 * plane + o) = i32x4{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3]};
+}
+
+// Partial logits of 128 tokens x EP experts over K-steps [k-slice of s].
+// Wave w owns tokens 32w + [0, 32) (two 16-row tiles) and all NTE expert
+// tiles; the three weight planes of each K-step are staged in LDS (64-byte
+// rows, chunk-swizzled), X fragments come straight from global memory.
+template <int NTE>
+__global__ __launch_bounds__(256) void router_logits_kernel(
+    const uint16_t* __restrict__ X, int T, int d, const uint16_t* __restrict__ Wsplit,
+    int d32, int S, float* __restrict__ partial) {
+  constexpr int EP = 16 * NTE;
+  constexpr int ROWS = 3 * EP;           // staged rows per K-step
+  constexpr int STAGE = ROWS * 64;       // bytes
+  constexpr int NINSTR = ROWS / 16;      // 1 KB wave-level loads per stage
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int t0 = blockIdx.x * kRtTok;
+  const int s = blockIdx.y;
+  const int nk = d32 / kRtK;
+  const int ks0 = (int)((int64_t)s * nk / S), ks1 = (int)((int64_t)(s + 1) * nk / S);
+  const int nks = ks1 - ks0;
+
+  // weight-plane loads: instruction q covers rows 16q..16q+15
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wsplit, (uint32_t)((int64_t)ROWS * d32 * 2));
+  auto issue = [&](int stage, int kstep) {
+    for (int q = wave; q < NINSTR; q += 4) {
+      const uint32_t R = q * 16 + (lane >> 2);
+      const uint32_t c = (lane & 3) ^ rt_swz(R);
+      const uint32_t vo = R * (uint32_t)d32 * 2u + (uint32_t)kstep * (kRtK * 2) + c * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, MOE_LDS_PTR(smem + stage * STAGE + q * 1024),
+                                               16, vo, 0, 0, 0);
     }
-    const float m = __shfl(my_s, 0, kWave);  // the largest logit of the token
-    float w;
-    if (gating == 0) {
-      const float ex = (lane < k) ? expf(my_s - m) : 0.f;
-      w = ex / wave_sum(ex);
-    } else {
-      float z = 0.f;
+  };
+  // X fragments: lane holds token (l % 16) of a 16-row tile, k chunk (l / 16)
+  const int xt0 = t0 + wave * 32;
+  const int xrows = max(0, min(32, T - xt0));
+  const __amdgpu_buffer_rsrc_t rX =
+      make_rsrc(X + (int64_t)min(xt0, max(T - 1, 0)) * d, (uint32_t)xrows * (uint32_t)d * 2u);
+  auto load_x = [&](int kstep, bf16x8 (&x)[2]) {
+    const int kk = kstep * kRtK + 8 * (lane >> 4);
 #pragma unroll
-      for (int i = 0; i < VPL; ++i) {
-        const int e = lane + kWave * i;
-        if (e < E) z += expf(Ls[row][e] - m);
-      }
-      const float Z = wave_sum(z);
-      const float p = (lane < k) ? expf(my_s - m) / Z : 0.f;
-      w = p / wave_sum(p);
+    for (int mt = 0; mt < 2; ++mt) {
+      const uint32_t vo = (kk < d) ? ((uint32_t)(mt * 16 + (lane & 15)) * (uint32_t)d + kk) * 2u : kOob;
+      const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rX, vo, 0, 0);
+      x[mt] = __builtin_bit_cast(bf16x8, v);
     }
-    if (lane < k) {
-      topk_idx[(int64_t)t * k + lane] = my_id;
-      topk_w[(int64_t)t * k + lane] = w;
+  };
+  f32x4 acc[2][NTE];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTE; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  bf16x8 xc[2], xn[2];
+  issue(0, ks0);
+  load_x(ks0, xc);
+  for (int j = 0; j < nks; ++j) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (j + 1 < nks) {
+      issue((j + 1) & 1, ks0 + j + 1);
+      load_x(ks0 + j + 1, xn);
+    }
+    const char* st = smem + (j & 1) * STAGE;
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int nt = 0; nt < NTE; ++nt) {
+        // B fragment of expert tile nt, plane p: row p*EP + nt*16 + (l % 16),
+        // chunk l / 16
+        const uint32_t R = p * EP + nt * 16 + (lane & 15);
+        const uint32_t off = R * 64 + (((lane >> 4) ^ rt_swz(R)) * 16);
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(st + off);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xc[mt], b, acc[mt][nt], 0, 0, 0);
+      }
+    if (j + 1 < nks) {
+      xc[0] = xn[0];
+      xc[1] = xn[1];
     }
   }
+
+  // D[token][expert]: lane holds rows 4*(l/16) + r, column l % 16
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = xt0 + mt * 16 + 4 * (lane >> 4) + r;
+      if (t < T) {
+        float* dst = partial + ((int64_t)s * T + t) * EP + (lane & 15);
+#pragma unroll
+        for (int nt = 0; nt < NTE; ++nt) dst[nt * 16] = acc[mt][nt][r];
+      }
+    }
+}
+
+// One wavefront per token: sum the S partials in order, add the bias, top-k.
+template <int VPL>
+__global__ __launch_bounds__(256) void router_select_kernel(
+    const float* __restrict__ partial, const float* __restrict__ bias, int T, int E,
+    int EP, int S, int k, int gating, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w) {
+  const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= T) return;
+  float v[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = lane + kWave * i;
+    if (e < E) {
+      float acc = 0.f;
+      for (int s = 0; s < S; ++s) acc += partial[((int64_t)s * T + t) * EP + e];
+      v[i] = acc + (bias != nullptr ? bias[e] : 0.f);
+    } else {
+      v[i] = -INFINITY;
+    }
+  }
+  topk_softmax_store<VPL>(v, E, k, gating, lane, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
+}
+
+struct RoutePlan {
+  int NTE, EP, d32, S, tiles;
+  size_t split_bytes, partial_bytes;
+};
+
+size_t a256r(size_t x) { return (x + 255) & ~size_t(255); }
+
+RoutePlan route_plan(int T, int E, int d) {
+  RoutePlan P{};
+  int nte = (E + 15) / 16, p2 = 1;
+  while (p2 < nte) p2 <<= 1;
+  P.NTE = p2;
+  P.EP = 16 * p2;
+  P.d32 = (d + kRtK - 1) / kRtK * kRtK;
+  P.tiles = (T + kRtTok - 1) / kRtTok;
+  const int nk = P.d32 / kRtK;
+  const int64_t cap = std::max<int64_t>(1, (int64_t(32) << 20) / std::max<int64_t>(1, (int64_t)T * P.EP * 4));
+  int S = std::max(1, (256 + std::max(P.tiles, 1) - 1) / std::max(P.tiles, 1));
+  S = (int)std::min<int64_t>(std::min<int64_t>(S, nk), cap);
+  P.S = std::max(1, S);
+  P.split_bytes = a256r((size_t)3 * P.EP * P.d32 * 2);
+  P.partial_bytes = a256r((size_t)P.S * T * P.EP * 4);
+  return P;
 }
 
 template <int TX, int RE, int RT>
@@ -197,11 +409,43 @@ hipError_t launch_cfg(const void* X, bool x_bf16, const float* W_r,
 
 }  // namespace
 
+size_t route_scratch_bytes(int T, int E, int d, bool x_bf16) {
+  if (!x_bf16 || T == 0) return 0;
+  const RoutePlan P = route_plan(T, E, d);
+  return P.split_bytes + P.partial_bytes;
+}
+
 hipError_t launch_route(const void* X, bool x_bf16, const float* W_r,
                         const float* bias, int T, int d, int E, int k,
                         int gating, int32_t* topk_idx, float* topk_w,
-                        hipStream_t stream) {
+                        void* scratch, hipStream_t stream) {
   if (T == 0) return hipSuccess;
+  if (x_bf16) {
+    const RoutePlan P = route_plan(T, E, d);
+    uint16_t* Wsplit = static_cast<uint16_t*>(scratch);
+    float* partial = reinterpret_cast<float*>(static_cast<char*>(scratch) + P.split_bytes);
+    const int64_t nthr = (int64_t)P.EP * (P.d32 / 8);
+    router_split_kernel<<<(unsigned)((nthr + 255) / 256), 256, 0, stream>>>(W_r, E, d, P.EP, P.d32, Wsplit);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const dim3 g(P.tiles, P.S);
+    switch (P.NTE) {
+      case 1: router_logits_kernel<1><<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(X), T, d, Wsplit, P.d32, P.S, partial); break;
+      case 2: router_logits_kernel<2><<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(X), T, d, Wsplit, P.d32, P.S, partial); break;
+      case 4: router_logits_kernel<4><<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(X), T, d, Wsplit, P.d32, P.S, partial); break;
+      case 8: router_logits_kernel<8><<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(X), T, d, Wsplit, P.d32, P.S, partial); break;
+      default: router_logits_kernel<16><<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(X), T, d, Wsplit, P.d32, P.S, partial); break;
+    }
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const unsigned gs = (unsigned)((T + 3) / 4);
+    if (E <= 64)
+      router_select_kernel<1><<<gs, 256, 0, stream>>>(partial, bias, T, E, P.EP, P.S, k, gating, topk_idx, topk_w);
+    else if (E <= 128)
+      router_select_kernel<2><<<gs, 256, 0, stream>>>(partial, bias, T, E, P.EP, P.S, k, gating, topk_idx, topk_w);
+    else
+      router_select_kernel<4><<<gs, 256, 0, stream>>>(partial, bias, T, E, P.EP, P.S, k, gating, topk_idx, topk_w);
+    return hipGetLastError();
+  }
   if (E <= 8) return launch_cfg<8, 1, 1>(X, x_bf16, W_r, bias, T, d, E, k, gating, topk_idx, topk_w, stream);
   if (E <= 16) return launch_cfg<16, 1, 1>(X, x_bf16, W_r, bias, T, d, E, k, gating, topk_idx, topk_w, stream);
   if (E <= 32) return launch_cfg<32, 1, 2>(X, x_bf16, W_r, bias, T, d, E, k, gating, topk_idx, topk_w, stream);

@@ -70,7 +70,7 @@ def test_invalid_problems_rejected(kw, status):
     lib = B.load()
     p = B.problem(**kw)
     fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
-    r = lib.moe_route(ctypes.byref(p), fake, fake, None, fake, fake, None)
+    r = lib.moe_route(ctypes.byref(p), fake, fake, None, fake, fake, fake, 1 << 40, None)
     assert r == status
     r = lib.moe_forward(ctypes.byref(p), fake, fake, None, fake, fake, fake,
                         fake, None, fake, 1 << 40, None)
@@ -82,16 +82,16 @@ def test_mixed_dtypes_and_bad_enums_rejected():
     lib = B.load()
     p = B.problem(8, 64, 4, 2, 64)
     p.w_dtype = B.MOE_F32
-    assert lib.moe_route(ctypes.byref(p), None, None, None, None, None,
-                         None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route(ctypes.byref(p), None, None, None, None, None, None,
+                         0, None) == B.MOE_ERR_UNSUPPORTED
     p = B.problem(8, 64, 4, 2, 64)
     p.gating = 7
-    assert lib.moe_route(ctypes.byref(p), None, None, None, None, None,
-                         None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(p), None, None, None, None, None, None,
+                         0, None) == B.MOE_ERR_INVALID_ARG
     p = B.problem(8, 64, 4, 2, 64, float("nan"))
-    assert lib.moe_route(ctypes.byref(p), None, None, None, None, None,
-                         None) == B.MOE_ERR_INVALID_ARG
-    assert lib.moe_route(None, None, None, None, None, None,
+    assert lib.moe_route(ctypes.byref(p), None, None, None, None, None, None,
+                         0, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(None, None, None, None, None, None, None, 0,
                          None) == B.MOE_ERR_INVALID_ARG
 
 
@@ -99,8 +99,12 @@ def test_null_pointers_and_small_workspace_rejected():
     lib = B.load()
     p = B.problem(8, 64, 4, 2, 64)
     fake = ctypes.c_void_p(0x1000)
-    assert lib.moe_route(ctypes.byref(p), None, fake, None, fake, fake,
-                         None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(p), None, fake, None, fake, fake, fake,
+                         1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    need = lib.moe_route_workspace_bytes(ctypes.byref(p))
+    assert need > 0
+    assert lib.moe_route(ctypes.byref(p), fake, fake, None, fake, fake, fake,
+                         need - 1, None) == B.MOE_ERR_WORKSPACE
     need = lib.moe_permute_workspace_bytes(ctypes.byref(p))
     r = lib.moe_permute(ctypes.byref(p), fake, fake, fake, fake, fake, fake,
                         fake, fake, fake, need - 1, None)
@@ -123,8 +127,8 @@ def test_empty_batch_is_a_noop_without_device_work():
     p = B.problem(0, 64, 4, 2, 64)
     assert lib.moe_forward(ctypes.byref(p), None, None, None, None, None,
                            None, None, None, None, 0, None) == B.MOE_OK
-    assert lib.moe_route(ctypes.byref(p), None, None, None, None, None,
-                         None) == B.MOE_OK
+    assert lib.moe_route(ctypes.byref(p), None, None, None, None, None, None,
+                         0, None) == B.MOE_OK
     assert lib.moe_combine(ctypes.byref(p), None, None, None, None,
                            None) == B.MOE_OK
 
