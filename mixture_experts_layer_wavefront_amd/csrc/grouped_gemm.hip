@@ -33,6 +33,8 @@
 //    workgroups over the 8 XCDs gives each XCD a contiguous run of tiles:
 //    the tiles sharing one expert's weights and rows share one L2.
 #include "common.h"
+
+#include <type_traits>
 #include "launch.h"
 
 #ifndef MOE_BK
@@ -40,6 +42,15 @@
 #endif
 #ifndef MOE_NS
 #define MOE_NS 2
+#endif
+#ifndef MOE_DTN
+#define MOE_DTN 8   // down GEMM: 32-column sub-tiles per 256-row tile
+#endif
+#ifndef MOE_WL
+#define MOE_WL 1
+#endif
+#ifndef MOE_SKIP
+#define MOE_SKIP 1
 #endif
 #ifndef MOE_LW
 #define MOE_LW 4
@@ -208,7 +219,17 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(
   };
 
   // ---- per-lane fragment read offsets within a stage ------------------------
+  // wm = wave / NW: the hardware puts waves w and w + 4 on one SIMD, so each
+  // SIMD holds waves of different row halves and skipping the empty row
+  // sub-tiles of a ragged tile leaves every SIMD with work.
+#if MOE_WL
+  const int wm = wave / NW, wn = wave % NW;
+#else
   const int wm = wave % MW, wn = wave / MW;
+#endif
+  // row sub-tiles of this wave that hold any of the tile's rows
+  int tm_active = (rows - wm * TM * 32 + 31) / 32;
+  tm_active = tm_active < 0 ? 0 : (tm_active > TM ? TM : tm_active);
   uint32_t offA[TM][KSUB], offB[NB][KSUB];
 #pragma unroll
   for (int ks = 0; ks < KSUB; ++ks) {
@@ -236,31 +257,39 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.f;
 
-  {
-  // NS-stage pipeline: stage kt+NS-1 is requested while stage kt is consumed
+  // NS-stage pipeline: stage kt+NS-1 is requested while stage kt is consumed.
+  // RAGGED: only the row sub-tiles of this wave that hold rows issue MFMAs
+  // (and read their A fragments); full tiles take the branch-free loop.
+  auto kloop = [&](auto ragged) {
+    constexpr bool RAGGED = decltype(ragged)::value;
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue(s, s);
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + NS - 2 < nk) stage_barrier<IPW * (NS - 2)>();
-    else stage_barrier<0>();
-    if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, kt + NS - 1);
-    const char* st = smem + (kt % NS) * STAGE;
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < nk) issue(s, s);
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + NS - 2 < nk) stage_barrier<IPW * (NS - 2)>();
+      else stage_barrier<0>();
+      if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, kt + NS - 1);
+      const char* st = smem + (kt % NS) * STAGE;
 #pragma unroll
-    for (int ks = 0; ks < KSUB; ++ks) {
-      bf16x8 a[TM], b[NB];
+      for (int ks = 0; ks < KSUB; ++ks) {
+        bf16x8 a[TM], b[NB];
 #pragma unroll
-      for (int mi = 0; mi < TM; ++mi) a[mi] = *reinterpret_cast<const bf16x8*>(st + offA[mi][ks]);
+        for (int mi = 0; mi < TM; ++mi)
+          if (!RAGGED || mi < tm_active) a[mi] = *reinterpret_cast<const bf16x8*>(st + offA[mi][ks]);
 #pragma unroll
-      for (int nj = 0; nj < NB; ++nj) b[nj] = *reinterpret_cast<const bf16x8*>(st + offB[nj][ks]);
+        for (int nj = 0; nj < NB; ++nj) b[nj] = *reinterpret_cast<const bf16x8*>(st + offB[nj][ks]);
 #pragma unroll
-      for (int mi = 0; mi < TM; ++mi)
+        for (int mi = 0; mi < TM; ++mi)
+          if (!RAGGED || mi < tm_active) {
 #pragma unroll
-        for (int nj = 0; nj < NB; ++nj)
-          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[nj], acc[mi][nj], 0, 0, 0);
+            for (int nj = 0; nj < NB; ++nj)
+              acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[nj], acc[mi][nj], 0, 0, 0);
+          }
+      }
     }
-  }
-  }
+  };
+  if (!MOE_SKIP || tm_active == TM) kloop(std::false_type{});
+  else kloop(std::true_type{});
 
   // ---- epilogue ---------------------------------------------------------------
   // acc[mi][nj][r] is element (row, col) of the tile with
@@ -639,7 +668,7 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
 #else
   err = launch_gemm<2, MOE_NW, 4, 4 / MOE_NW, true, MOE_BK, MOE_NS>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
   if (err != hipSuccess) return err;
-  return launch_gemm<2, MOE_NW, 4, 8 / MOE_NW, false, MOE_BK, MOE_NS>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
+  return launch_gemm<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
 #endif
 }
 
