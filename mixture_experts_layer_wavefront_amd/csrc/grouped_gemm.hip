@@ -18,13 +18,20 @@
 //    32x32 sub-tiles and issues v_mfma_f32_32x32x16_bf16 (fp32 accumulate).
 //    For gate/up one wavefront holds the gate AND the up accumulator of the
 //    same output columns, so SwiGLU is applied in registers before the
-//    single bf16 store of H.
+//    single bf16 store of H.  256-row tiles use 8 wavefronts (2 x 4) with
+//    128 x 64 wave tiles; 32-row tiles (few rows per expert) use 4.
 //  * Operands are staged global -> LDS with buffer_load_dwordx4 ... lds (no
-//    VGPR round trip), double-buffered.  A buffer resource per operand bounds
-//    the tile, so rows past an expert's end, columns past N and the K tail
-//    read as zero.  LDS rows are 128 B (64 bf16 of K); the 16-byte chunks of
-//    row R are XOR-swizzled by ((R ^ (R >> 3)) & 7) so the ds_read_b128
-//    fragment reads hit distinct banks.
+//    VGPR round trip), double-buffered, issued by half of the wavefronts so
+//    that on every SIMD one wave keeps issuing MFMAs while the other issues
+//    loads.  A buffer resource per operand bounds the tile, so rows past an
+//    expert's end, columns past N and the K tail read as zero.  LDS rows are
+//    128 B (64 bf16 of K); the 16-byte chunks of row R are XOR-swizzled by
+//    ((R ^ (R >> 3)) & 7) so the ds_read_b128 fragment reads hit distinct
+//    banks (rocprof: zero LDS bank conflicts).
+//  * Ragged tiles (an expert's last rows) run a second instance of the K loop
+//    in which each wave only issues the MFMAs of its row sub-tiles that hold
+//    rows; the hardware pairs waves w and w + 4 on one SIMD, and those hold
+//    different row halves, so every SIMD keeps working.
 //  * Schedule: a one-workgroup kernel turns expert_offsets into a prefix of
 //    per-expert M-tile counts.  The grid is a static upper bound; each
 //    workgroup finds its (expert, n-tile, m-tile) from the prefix and exits
@@ -54,9 +61,6 @@
 #endif
 #ifndef MOE_LW
 #define MOE_LW 4
-#endif
-#ifndef MOE_PP
-#define MOE_PP 0
 #endif
 #ifndef MOE_NW
 #define MOE_NW 4   // waves across N in the 256-row tile (2 x MOE_NW waves)
@@ -331,209 +335,6 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(
   }
 }
 
-// ---- 256-row tiles, 4 wavefronts of 128 x 128 -----------------------------
-// LDS bandwidth, not the matrix cores, bounds the 8-wave 128 x 64 layout (a
-// wave re-reads its A and B fragments from LDS for every 8 MFMAs), so here
-// each wave owns a 128 x 128 quarter of the 256 x 256 tile: 8 fragment reads
-// feed 16 MFMAs, the accumulators (256 per lane) live in AGPRs and one wave
-// runs per SIMD.  With no second wave to hide LDS latency, fragments are
-// double-buffered in registers: the reads for k-step ks+1 are in flight
-// while the MFMAs of ks run, and the reads of the next stage's first k-step
-// are issued right after the barrier, in the middle of the last k-step's
-// MFMAs.  BK = 64, two LDS stages of 64 KB.  Wave (wm, wn) = (w % 2, w / 2);
-// for gate/up a wave's 128 columns are 64 gate plus the matching 64 up.
-template <int TN, bool GATEUP>
-__global__ __launch_bounds__(256) void grouped_gemm_w4_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
-    const uint16_t* __restrict__ B1, int N, int K, int E,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ mt_prefix,
-    void* __restrict__ Cout) {
-  constexpr int TM = 4, BM = 256, NWAVES = 4;
-  constexpr int BN = 2 * TN * 32;
-  constexpr int NB = GATEUP ? 2 * TN : TN;
-  static_assert(NB == 4, "128-column wave tiles");
-  constexpr int BROWS = GATEUP ? 2 * BN : BN;
-  static_assert(BM + BROWS == 512, "512 staged rows");
-  constexpr int BK = 64, RB = 128, CPR = 8, RPI = 8, STAGE = 512 * RB;
-  constexpr int IPW = 512 / RPI / NWAVES;  // 16 loads per lane per stage
-  extern __shared__ __attribute__((aligned(1024))) char smem[];
-  int32_t* s_pref = reinterpret_cast<int32_t*>(smem + 2 * STAGE);
-
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-
-  for (int i = tid; i <= E; i += 256) s_pref[i] = mt_prefix[i];
-  __syncthreads();
-
-  const int n_nt = (N + BN - 1) / BN;
-  const int total = s_pref[E] * n_nt;
-  const int q = (total + kXcds - 1) / kXcds;
-  const int slot = blockIdx.x / kXcds;
-  if (slot >= q) return;
-  const int logical = (blockIdx.x % kXcds) * q + slot;
-  if (logical >= total) return;
-  int lo = 0, hi = E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (s_pref[mid] * n_nt <= logical) lo = mid; else hi = mid;
-  }
-  const int e = lo;
-  const int mt_e = s_pref[e + 1] - s_pref[e];
-  const int local = logical - s_pref[e] * n_nt;
-  const int n_t = local / mt_e, m_t = local % mt_e;
-  const int m_start = offsets[e] + m_t * BM;
-  const int rows = min(BM, offsets[e + 1] - m_start);
-  const int n0 = n_t * BN;
-  const int ncols = min(BN, N - n0);
-  const uint32_t kbytes = (uint32_t)K * 2u;
-  const int nk = (K + BK - 1) / BK;
-  const bool ktail = (K % BK) != 0;
-
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(A + (int64_t)m_start * K, (uint32_t)rows * kbytes);
-  const int64_t boff = ((int64_t)e * N + n0) * K;
-  const __amdgpu_buffer_rsrc_t rB0 = make_rsrc(B0 + boff, (uint32_t)ncols * kbytes);
-  const __amdgpu_buffer_rsrc_t rB1 = GATEUP ? make_rsrc(B1 + boff, (uint32_t)ncols * kbytes) : rB0;
-
-  uint32_t voff[IPW];
-  int kcol[IPW];
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int qi = wave + NWAVES * i;
-    const uint32_t R = qi * RPI + lane / CPR;
-    const uint32_t c = (lane % CPR) ^ swz<CPR>(R);
-    uint32_t row;
-    if (qi * RPI < BM) row = R;
-    else if (!GATEUP || qi * RPI < BM + BN) row = R - BM;
-    else row = R - BM - BN;
-    voff[i] = row * kbytes + c * 16;
-    kcol[i] = c * 8;
-  }
-  auto issue = [&](int stage, int kt) {
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int qi = wave + NWAVES * i;
-      uint32_t vo = voff[i] + (uint32_t)kt * RB;
-      if (ktail && kt * BK + kcol[i] >= K) vo = kOob;
-      char* dst = smem + stage * STAGE + qi * 1024;
-      if (qi * RPI < BM)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, MOE_LDS_PTR(dst), 16, vo, 0, 0, 0);
-      else if (!GATEUP || qi * RPI < BM + BN)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB0, MOE_LDS_PTR(dst), 16, vo, 0, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB1, MOE_LDS_PTR(dst), 16, vo, 0, 0, 0);
-    }
-  };
-
-  // Fragment addresses.  Row R = 32*j + l32 of a sub-tile: swz(R) depends on
-  // l32 and on the parity of j only, so two per-lane offsets per k-step serve
-  // every sub-tile (the rest is a compile-time row offset).
-  const int wm = wave % 2, wn = wave / 2;
-  const uint32_t l32 = lane & 31;
-  uint32_t loff[2][4];
-#pragma unroll
-  for (int par = 0; par < 2; ++par)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint32_t R = par * 32 + l32;
-      const uint32_t c = 2 * ks + (lane >> 5);
-      loff[par][ks] = l32 * RB + ((c ^ swz<CPR>(R)) * 16);
-    }
-  uint32_t a_row[TM], b_row[NB];
-#pragma unroll
-  for (int mi = 0; mi < TM; ++mi) a_row[mi] = wm * 128 + mi * 32;
-#pragma unroll
-  for (int nj = 0; nj < NB; ++nj) {
-    if (GATEUP) b_row[nj] = BM + ((nj < TN) ? wn * TN * 32 + nj * 32 : BN + wn * TN * 32 + (nj - TN) * 32);
-    else b_row[nj] = BM + wn * TN * 32 + nj * 32;
-  }
-  auto read_frags = [&](const char* st, int ks, bf16x8 (&fa)[TM], bf16x8 (&fb)[NB]) {
-#pragma unroll
-    for (int mi = 0; mi < TM; ++mi)
-      fa[mi] = *reinterpret_cast<const bf16x8*>(st + a_row[mi] * RB + loff[(a_row[mi] >> 5) & 1][ks]);
-#pragma unroll
-    for (int nj = 0; nj < NB; ++nj)
-      fb[nj] = *reinterpret_cast<const bf16x8*>(st + b_row[nj] * RB + loff[(b_row[nj] >> 5) & 1][ks]);
-  };
-
-  f32x16 acc[TM][NB];
-#pragma unroll
-  for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-    for (int nj = 0; nj < NB; ++nj)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.f;
-  auto mfma_half = [&](const bf16x8 (&fa)[TM], const bf16x8 (&fb)[NB], int h) {
-#pragma unroll
-    for (int mi = 2 * h; mi < 2 * h + 2; ++mi)
-#pragma unroll
-      for (int nj = 0; nj < NB; ++nj)
-        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[nj], acc[mi][nj], 0, 0, 0);
-  };
-
-  bf16x8 fa0[TM], fb0[NB], fa1[TM], fb1[NB];
-  issue(0, 0);
-  stage_barrier<0>();
-  if (nk > 1) issue(1, 1);
-  read_frags(smem, 0, fa0, fb0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const char* st = smem + (kt & 1) * STAGE;
-    read_frags(st, 1, fa1, fb1);
-    mfma_half(fa0, fb0, 0);
-    mfma_half(fa0, fb0, 1);
-    read_frags(st, 2, fa0, fb0);
-    mfma_half(fa1, fb1, 0);
-    mfma_half(fa1, fb1, 1);
-    read_frags(st, 3, fa1, fb1);
-    mfma_half(fa0, fb0, 0);
-    mfma_half(fa0, fb0, 1);
-    mfma_half(fa1, fb1, 0);
-    if (kt + 1 < nk) {
-      // stage kt+1 landed and every wave is done with stage kt
-      stage_barrier<0>();
-      if (kt + 2 < nk) issue(kt & 1, kt + 2);
-      read_frags(smem + ((kt + 1) & 1) * STAGE, 0, fa0, fb0);
-    }
-    mfma_half(fa1, fb1, 1);
-  }
-
-  const int col_l = lane & 31;
-  const int rbase = wm * TM * 32 + 4 * (lane >> 5);
-  if constexpr (GATEUP) {
-    uint16_t* H = static_cast<uint16_t*>(Cout);
-#pragma unroll
-    for (int nj = 0; nj < TN; ++nj) {
-      const int col = wn * TN * 32 + nj * 32 + col_l;
-      if (col >= ncols) continue;
-#pragma unroll
-      for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rbase + mi * 32 + 8 * (r >> 2) + (r & 3);
-          if (row < rows) {
-            const float g = acc[mi][nj][r], u = acc[mi][nj + TN][r];
-            const float h = g / (1.f + __expf(-g)) * u;
-            H[(int64_t)(m_start + row) * N + n0 + col] = f32_to_bf16_bits(h);
-          }
-        }
-    }
-  } else {
-    float* Y = static_cast<float*>(Cout);
-#pragma unroll
-    for (int nj = 0; nj < TN; ++nj) {
-      const int col = wn * TN * 32 + nj * 32 + col_l;
-      if (col >= ncols) continue;
-#pragma unroll
-      for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rbase + mi * 32 + 8 * (r >> 2) + (r & 3);
-          if (row < rows) Y[(int64_t)(m_start + row) * N + n0 + col] = acc[mi][nj][r];
-        }
-    }
-  }
-}
-
 // ---- fp32 path (plain FMA; for fp32 layers, which are small) ---------------
 __device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int r) {
   int lo = 0, hi = E;  // offsets[lo] <= r < offsets[hi]
@@ -603,27 +404,6 @@ hipError_t launch_gemm(const void* A, const void* B0, const void* B1, int N,
   return hipGetLastError();
 }
 
-template <int TN, bool GATEUP>
-hipError_t launch_gemm_w4(const void* A, const void* B0, const void* B1, int N,
-                          int K, int E, int64_t R, const int32_t* offsets,
-                          const int32_t* mt_prefix, void* C, hipStream_t stream) {
-  constexpr int BM = 256, BN = 2 * TN * 32;
-  constexpr int LDS = 2 * 512 * 128 + 1040;
-  auto kern = grouped_gemm_w4_kernel<TN, GATEUP>;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-  if (attr != hipSuccess) return attr;
-  const int64_t mt_max = (R + BM - 1) / BM + std::min<int64_t>(E, R);
-  const int64_t tiles = mt_max * ((N + BN - 1) / BN);
-  const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
-  if (grid == 0) return hipSuccess;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), LDS, stream,
-                     static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B0),
-                     static_cast<const uint16_t*>(B1), N, K, E, offsets, mt_prefix, C);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 size_t ffn_scratch_bytes(int64_t R, int E, int d_ff, bool bf16) {
@@ -633,8 +413,9 @@ size_t ffn_scratch_bytes(int64_t R, int E, int d_ff, bool bf16) {
 hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
                               const int32_t* offsets, const void* W_gate,
                               const void* W_up, const void* W_down, int64_t R,
-                              int d, int E, int d_ff, bool small_m,
+                              int d, int E, int d_ff, int rows_per_expert,
                               float* Y_perm, void* scratch, hipStream_t stream) {
+  const bool small_m = rows_per_expert <= 64;
   if (R == 0) return hipSuccess;
   int32_t* mt_prefix = static_cast<int32_t*>(scratch);
   void* H = static_cast<char*>(scratch) + align256((size_t)(E + 1) * 4);
@@ -661,15 +442,9 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
   }
   ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, 256, mt_prefix);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-#if MOE_PP
-  err = launch_gemm_w4<2, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
-  if (err != hipSuccess) return err;
-  return launch_gemm_w4<4, false>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
-#else
   err = launch_gemm<2, MOE_NW, 4, 4 / MOE_NW, true, MOE_BK, MOE_NS>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
   if (err != hipSuccess) return err;
   return launch_gemm<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
-#endif
 }
 
 }  // namespace moe

@@ -25,13 +25,13 @@ hipError_t launch_permute(const void* X, bool x_bf16, const int32_t* topk_idx,
                           int32_t* dest_row, int32_t* row_token, void* X_perm,
                           void* scratch, hipStream_t stream);
 
-// Grouped SwiGLU FFN.  `small_m` picks the 32-row tile shape meant for few
-// rows per expert.
+// Grouped SwiGLU FFN.  `rows_per_expert` (the mean, known on the host from
+// the shape alone) picks the tile shape: 32-row or 256-row tiles.
 size_t ffn_scratch_bytes(int64_t R, int E, int d_ff, bool bf16);
 hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
                               const int32_t* offsets, const void* W_gate,
                               const void* W_up, const void* W_down,
-                              int64_t R, int d, int E, int d_ff, bool small_m,
+                              int64_t R, int d, int E, int d_ff, int rows_per_expert,
                               float* Y_perm, void* scratch, hipStream_t stream);
 
 // Gate-weighted gather-combine back to token order.

@@ -47,12 +47,13 @@ int capacity_int(const moe_problem_t* p) {
   return C < 0 ? INT_MAX : (int)C;
 }
 
-bool use_small_m(const moe_problem_t* p) {
-  // mean rows per expert, known on the host without reading device data
+// Mean rows per expert, known on the host without reading device data; it
+// picks the grouped GEMM's tile shape.
+int mean_rows_per_expert(const moe_problem_t* p) {
   double mean = (double)p->T * p->top_k / p->E;
   const int64_t C = moe_capacity(p);
   if (C >= 0 && (double)C < mean) mean = (double)C;
-  return mean <= 64.0;
+  return (int)std::ceil(mean);
 }
 
 struct ForwardLayout {
@@ -165,7 +166,7 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* X_perm,
   if (!workspace || ws_bytes < moe_grouped_ffn_workspace_bytes(p)) return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_grouped_ffn(X_perm, is_bf16(p), expert_offsets, W_gate, W_up,
                                             W_down, R, p->d_model, p->E, p->d_ff,
-                                            use_small_m(p), Y_perm, workspace, stream));
+                                            mean_rows_per_expert(p), Y_perm, workspace, stream));
 }
 
 moe_status_t moe_combine(const moe_problem_t* p, const float* Y_perm,
@@ -211,7 +212,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* X, const float* W_r
                           x_perm, ws + L.perm_scratch, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_grouped_ffn(x_perm, bf, offsets, W_gate, W_up, W_down, moe_rows_bound(p),
-                              p->d_model, p->E, p->d_ff, use_small_m(p), y_perm,
+                              p->d_model, p->E, p->d_ff, mean_rows_per_expert(p), y_perm,
                               ws + L.ffn_scratch, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_combine(y_perm, dest_row, topk_w, p->T, p->d_model, p->top_k,
