@@ -33,8 +33,50 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=64)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling the "
+                         "FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def _calibrate_copy():
+    """A plain device-to-device copy of 1 GiB, three times: the counter
+    reference for HBM traffic (each copy reads and writes 1 GiB)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": n,
+                      "bytes_written_per_copy": n, "copies": 3}), flush=True)
+
+
+def _traffic(workload):
+    """HBM traffic per grouped-FFN launch from the committed counter summary
+    (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated), or None when there is
+    none for this workload or the GEMM source changed since it was taken."""
+    import hashlib
+    f = os.path.join(ROOT, "profiles", f"grouped_ffn_{workload}_traffic.md")
+    src = os.path.join(ROOT, "mixture_experts_layer_wavefront_amd", "csrc",
+                       "grouped_gemm.hip")
+    if not os.path.exists(f):
+        return None
+    vals = {}
+    for line in open(f):
+        if ":" in line and not line.startswith(("|", "#", " ")):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if vals.get("source_sha256") != sha:
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def _time_loop(fn, steps, stream):
@@ -82,6 +124,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        _calibrate_copy()
+        return
 
     import mixture_experts_layer_wavefront_amd as M
     from mixture_experts_layer_wavefront_amd import workloads as W
@@ -169,7 +215,7 @@ def main():
                      "(gate/up GEMM + SwiGLU epilogue, down GEMM)",
                      "achieved": ffn_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": ffn_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": None,
+                     "traffic": _traffic(args.workload),
                      "flops_per_launch": ffn_flops, "ms_per_launch": t_ffn},
         "stages_ms": {"route": t_route, "permute": t_perm, "grouped_ffn": t_ffn,
                       "combine": t_comb},
