@@ -33,7 +33,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -91,28 +91,35 @@ def _time_loop(fn, steps, stream):
     return s.elapsed_time(e) / steps  # ms per call
 
 
-def _cpu_baseline(wl, dev, ntok):
+def _cpu_baseline(wl, dev, ntok, min_s=10.0, max_s=30.0):
     """The CPU oracle (as it stands) on the first `ntok` tokens of the same
-    batch with the same weights; returns the dict for the JSON line."""
-    import torch
+    batch with the same weights, repeated until at least `min_s` seconds of
+    CPU work (stopping before `max_s`); returns the dict for the JSON line."""
     from threadpoolctl import threadpool_info
 
     import oracle as O
 
     host = {k: (None if v is None else v.float().cpu().numpy())
             for k, v in dev.items()}
+    ntok = min(ntok, wl.T)
     X = host["X"][:ntok]
     cf = float(np.float32(wl.capacity_factor))
-    t0 = time.perf_counter()
-    O.moe_forward(X, host["W_r"], host["bias"], host["W_gate"], host["W_up"],
-                  host["W_down"], wl.top_k, cf if cf > 0 else None, wl.gating)
-    dt = time.perf_counter() - t0
+    runs, total = 0, 0.0
+    while total < min_s:
+        t0 = time.perf_counter()
+        O.moe_forward(X, host["W_r"], host["bias"], host["W_gate"], host["W_up"],
+                      host["W_down"], wl.top_k, cf if cf > 0 else None, wl.gating)
+        dt = time.perf_counter() - t0
+        runs += 1
+        total += dt
+        if total + dt > max_s:
+            break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": ntok / dt, "unit": "tokens/s", "cores": int(threads),
+    return {"value": ntok * runs / total, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"first {ntok} of the {wl.T} tokens, all {wl.E} experts "
-                      f"(full weights), fp64 NumPy per-expert loop, "
-                      f"{dt:.1f} s wall"}
+                      f"(full weights), fp64 NumPy per-expert loop, {runs} run(s), "
+                      f"{total:.1f} s wall"}
 
 
 def main():
