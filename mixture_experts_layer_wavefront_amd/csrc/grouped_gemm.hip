@@ -65,11 +65,27 @@
 #ifndef MOE_NW
 #define MOE_NW 4   // waves across N in the 256-row tile (2 x MOE_NW waves)
 #endif
+#ifndef MOE_SNW
+#define MOE_SNW 4  // 32-row tiles: waves across N (one 32-column sub-tile each)
+#endif
+#ifndef MOE_SBK
+#define MOE_SBK 64 // 32-row tiles: K per stage
+#endif
+#ifndef MOE_SNS
+#define MOE_SNS 3  // 32-row tiles: stages
+#endif
+#ifndef MOE_SBAUX
+#define MOE_SBAUX kNonTemporal  // 32-row tiles: weight loads stream (nt)
+#endif
+#ifndef MOE_BNT_ROWS
+#define MOE_BNT_ROWS 256  // 256-row tiles: stream the weights up to this many rows per expert
+#endif
 
 namespace moe {
 namespace {
 
 constexpr int kXcds = 8;
+constexpr int kNonTemporal = 2;  // "nt" bit of a buffer load's cache policy
 
 // Chunk swizzle of LDS row R (16-byte chunks).  128-byte rows (BK = 64, 8
 // chunks) and 64-byte rows (BK = 32, 4 chunks): 8 or 16 consecutive rows
@@ -134,8 +150,10 @@ struct GemmCfg {
 };
 
 // A [R, K] bf16 rows; B0/B1 [E, N, K] bf16 (gate/up, or down with B1 unused).
-// GATEUP: C = H bf16 [R, N].  Otherwise C = Y fp32 [R, N].
-template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS>
+// GATEUP: C = H bf16 [R, N].  Otherwise C = Y fp32 [R, N].  BAUX: cache-policy
+// bits of the weight loads (kNonTemporal when each weight tile is read by
+// about one workgroup: the loads then stream past the caches).
+template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS, int BAUX>
 __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, int N, int K, int E,
@@ -216,9 +234,9 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(
       if (qi * RPI < BM)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, MOE_LDS_PTR(dst), 16, vo, 0, 0, 0);
       else if (!GATEUP || qi * RPI < BM + BN)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB0, MOE_LDS_PTR(dst), 16, vo, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB0, MOE_LDS_PTR(dst), 16, vo, 0, 0, BAUX);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB1, MOE_LDS_PTR(dst), 16, vo, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB1, MOE_LDS_PTR(dst), 16, vo, 0, 0, BAUX);
     }
   };
 
@@ -381,12 +399,12 @@ __global__ __launch_bounds__(256) void ffn_f32_down_kernel(
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS>
+template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS, int BAUX>
 hipError_t launch_gemm(const void* A, const void* B0, const void* B1, int N,
                        int K, int E, int64_t R, const int32_t* offsets,
                        const int32_t* mt_prefix, void* C, hipStream_t stream) {
   using Cfg = GemmCfg<MW, NW, TM, TN, GATEUP, BK, NS>;
-  auto kern = grouped_gemm_kernel<MW, NW, TM, TN, GATEUP, BK, NS>;
+  auto kern = grouped_gemm_kernel<MW, NW, TM, TN, GATEUP, BK, NS, BAUX>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
       Cfg::LDS_BYTES);
@@ -406,6 +424,11 @@ hipError_t launch_gemm(const void* A, const void* B0, const void* B1, int N,
 
 }  // namespace
 
+int ffn_tile_rows(bool bf16, int rows_per_expert) {
+  if (!bf16) return 0;
+  return rows_per_expert <= 64 ? 32 : 256;
+}
+
 size_t ffn_scratch_bytes(int64_t R, int E, int d_ff, bool bf16) {
   return align256((size_t)(E + 1) * 4) + align256((size_t)R * d_ff * (bf16 ? 2 : 4));
 }
@@ -414,8 +437,9 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
                               const int32_t* offsets, const void* W_gate,
                               const void* W_up, const void* W_down, int64_t R,
                               int d, int E, int d_ff, int rows_per_expert,
-                              float* Y_perm, void* scratch, hipStream_t stream) {
-  const bool small_m = rows_per_expert <= 64;
+                              float* Y_perm, void* scratch, bool prefix_ready,
+                              hipStream_t stream) {
+  const bool small_m = ffn_tile_rows(bf16, rows_per_expert) == 32;
   if (R == 0) return hipSuccess;
   int32_t* mt_prefix = static_cast<int32_t*>(scratch);
   void* H = static_cast<char*>(scratch) + align256((size_t)(E + 1) * 4);
@@ -434,17 +458,27 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
   hipError_t err;
   if (small_m) {
     // 32-row tiles: few rows per expert, the weights dominate the traffic
-    ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, 32, mt_prefix);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    err = launch_gemm<1, 4, 1, 1, true, 64, 2>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
+    if (!prefix_ready) {
+      ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, 32, mt_prefix);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    err = launch_gemm<1, MOE_SNW, 1, 1, true, MOE_SBK, MOE_SNS, MOE_SBAUX>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
     if (err != hipSuccess) return err;
-    return launch_gemm<1, 4, 1, 1, false, 64, 2>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
+    return launch_gemm<1, MOE_SNW, 1, 1, false, MOE_SBK, MOE_SNS, MOE_SBAUX>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
   }
-  ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, 256, mt_prefix);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  err = launch_gemm<2, MOE_NW, 4, 4 / MOE_NW, true, MOE_BK, MOE_NS>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
+  if (!prefix_ready) {
+    ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, 256, mt_prefix);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (rows_per_expert <= MOE_BNT_ROWS) {
+    // about one M-tile per expert: every weight tile is read once
+    err = launch_gemm<2, MOE_NW, 4, 4 / MOE_NW, true, MOE_BK, MOE_NS, kNonTemporal>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
+    if (err != hipSuccess) return err;
+    return launch_gemm<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, kNonTemporal>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
+  }
+  err = launch_gemm<2, MOE_NW, 4, 4 / MOE_NW, true, MOE_BK, MOE_NS, 0>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
   if (err != hipSuccess) return err;
-  return launch_gemm<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
+  return launch_gemm<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, 0>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
 }
 
 }  // namespace moe

@@ -17,22 +17,30 @@ hipError_t launch_route(const void* X, bool x_bf16, const float* W_r,
                         void* scratch, hipStream_t stream);
 
 // Permute, three kernels: per-block counts and in-block ranks; one-block
-// scan with capacity; destination rows and the row copy.
+// scan with capacity; destination rows and the row copy (one kernel for few
+// copies).  With mt_prefix != nullptr it also writes the grouped FFN's tile
+// schedule for tiles of bm rows (see launch_grouped_ffn).
 size_t permute_scratch_bytes(int T, int k, int E);
 hipError_t launch_permute(const void* X, bool x_bf16, const int32_t* topk_idx,
                           int T, int d, int E, int k, int C,
                           int32_t* counts, int32_t* offsets, int32_t* dropped,
                           int32_t* dest_row, int32_t* row_token, void* X_perm,
-                          void* scratch, hipStream_t stream);
+                          void* scratch, int32_t* mt_prefix, int bm,
+                          hipStream_t stream);
 
 // Grouped SwiGLU FFN.  `rows_per_expert` (the mean, known on the host from
-// the shape alone) picks the tile shape: 32-row or 256-row tiles.
+// the shape alone) picks the tile shape: ffn_tile_rows() rows per tile (0:
+// fp32 layers, no tile schedule).  The tile schedule (exclusive prefix over
+// experts of their tile counts, E + 1 ints) lives at the start of `scratch`;
+// with prefix_ready the caller has already written it there.
+int ffn_tile_rows(bool bf16, int rows_per_expert);
 size_t ffn_scratch_bytes(int64_t R, int E, int d_ff, bool bf16);
 hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
                               const int32_t* offsets, const void* W_gate,
                               const void* W_up, const void* W_down,
                               int64_t R, int d, int E, int d_ff, int rows_per_expert,
-                              float* Y_perm, void* scratch, hipStream_t stream);
+                              float* Y_perm, void* scratch, bool prefix_ready,
+                              hipStream_t stream);
 
 // Gate-weighted gather-combine back to token order.
 hipError_t launch_combine(const float* Y_perm, const int32_t* dest_row,

@@ -150,7 +150,7 @@ moe_status_t moe_permute(const moe_problem_t* p, const void* X,
   return hip_status(moe::launch_permute(X, is_bf16(p), topk_idx, p->T, p->d_model, p->E,
                                         p->top_k, capacity_int(p), expert_counts,
                                         expert_offsets, num_dropped, dest_row, row_token,
-                                        X_perm, workspace, stream));
+                                        X_perm, workspace, nullptr, 0, stream));
 }
 
 moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* X_perm,
@@ -166,7 +166,8 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* X_perm,
   if (!workspace || ws_bytes < moe_grouped_ffn_workspace_bytes(p)) return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_grouped_ffn(X_perm, is_bf16(p), expert_offsets, W_gate, W_up,
                                             W_down, R, p->d_model, p->E, p->d_ff,
-                                            mean_rows_per_expert(p), Y_perm, workspace, stream));
+                                            mean_rows_per_expert(p), Y_perm, workspace, false,
+                                            stream));
 }
 
 moe_status_t moe_combine(const moe_problem_t* p, const float* Y_perm,
@@ -207,13 +208,16 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* X, const float* W_r
                                    (int)p->gating, topk_idx, topk_w, ws + L.route_scratch,
                                    stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
+  // the permute also writes the FFN's tile schedule (start of its scratch)
+  const int bm = moe::ffn_tile_rows(bf, mean_rows_per_expert(p));
+  int32_t* mt_prefix = bm > 0 ? reinterpret_cast<int32_t*>(ws + L.ffn_scratch) : nullptr;
   e = moe::launch_permute(X, bf, topk_idx, p->T, p->d_model, p->E, p->top_k,
                           capacity_int(p), counts, offsets, dropped, dest_row, row_token,
-                          x_perm, ws + L.perm_scratch, stream);
+                          x_perm, ws + L.perm_scratch, mt_prefix, bm, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_grouped_ffn(x_perm, bf, offsets, W_gate, W_up, W_down, moe_rows_bound(p),
                               p->d_model, p->E, p->d_ff, mean_rows_per_expert(p), y_perm,
-                              ws + L.ffn_scratch, stream);
+                              ws + L.ffn_scratch, mt_prefix != nullptr, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_combine(y_perm, dest_row, topk_w, p->T, p->d_model, p->top_k,
                           out_bf16(p), out, stream);

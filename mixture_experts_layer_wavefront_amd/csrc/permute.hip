@@ -26,6 +26,12 @@
 //   K3 scatter     one wavefront per token: destination rows, the inverse
 //                  map, then the X row is read once and written to each of
 //                  its kept destinations.
+//
+// Few copies (T*k <= kSmallCopies): one kernel.  Every workgroup ranks all
+// copies itself (one copy per lane, 256 per round, token-major), so no
+// workgroup waits for another; workgroup 0 publishes counts, offsets, the
+// drop count, dest_row and row_token, and each workgroup copies the X rows
+// of its own tokens.
 #include "common.h"
 #include "launch.h"
 
@@ -106,9 +112,10 @@ __global__ __launch_bounds__(kPermThreads) void count_rank_kernel(
 __global__ __launch_bounds__(256) void scan_kernel(
     int32_t* __restrict__ block_counts, int nblk, int E, int C,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ dropped) {
+    int32_t* __restrict__ dropped, int32_t* __restrict__ mt_prefix, int bm) {
   __shared__ int32_t s_kept[256];
   __shared__ int32_t s_drop[256];
+  __shared__ int32_t s_mt[256];
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
@@ -120,24 +127,30 @@ __global__ __launch_bounds__(256) void scan_kernel(
     }
   }
   const int kept = (e < E) ? min(run, C) : 0;
+  const int mt = (mt_prefix != nullptr) ? (kept + bm - 1) / bm : 0;
   s_kept[e] = kept;
   s_drop[e] = (e < E) ? run - kept : 0;
+  s_mt[e] = mt;
   __syncthreads();
   // inclusive Hillis-Steele scan over 256 entries
   for (int o = 1; o < 256; o <<= 1) {
     const int a = (e >= o) ? s_kept[e - o] : 0;
     const int b = (e >= o) ? s_drop[e - o] : 0;
+    const int c = (e >= o) ? s_mt[e - o] : 0;
     __syncthreads();
     s_kept[e] += a;
     s_drop[e] += b;
+    s_mt[e] += c;
     __syncthreads();
   }
   if (e < E) {
     counts[e] = run;
     offsets[e] = s_kept[e] - kept;
+    if (mt_prefix != nullptr) mt_prefix[e] = s_mt[e] - mt;
     if (e == E - 1) {
       offsets[E] = s_kept[e];
       dropped[0] = s_drop[e];
+      if (mt_prefix != nullptr) mt_prefix[E] = s_mt[e];
     }
   }
 }
@@ -189,18 +202,126 @@ __global__ __launch_bounds__(256) void scatter_kernel(
   }
 }
 
+constexpr int kSmallCopies = 2048;
+
+__global__ __launch_bounds__(256) void permute_small_kernel(
+    const i32x4* __restrict__ X, const int32_t* __restrict__ topk_idx, int T, int E,
+    int k, int C, int row_chunks, int tok_per_block, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ dropped,
+    int32_t* __restrict__ dest_row, int32_t* __restrict__ row_token,
+    i32x4* __restrict__ X_perm, int32_t* __restrict__ mt_prefix, int bm) {
+  __shared__ int32_t s_run[256];        // copies of each expert ranked so far
+  __shared__ int32_t s_mt[256];         // tiles of bm rows per expert
+  __shared__ int32_t s_wcnt[4][256];    // per-wave copies of each expert in a round
+  __shared__ int32_t s_off[256];        // kept-row offsets
+  __shared__ int32_t s_drop[256];
+  __shared__ int32_t s_rank[kSmallCopies];
+  __shared__ int32_t s_exp[kSmallCopies];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int n = T * k;
+  s_run[tid] = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) s_wcnt[w][tid] = 0;
+  __syncthreads();
+
+  const int nb = (E <= 1) ? 0 : 32 - __clz(E - 1);  // bits of an expert id
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c0 = 0; c0 < n; c0 += 256) {
+    const int q = c0 + tid;
+    const bool valid = q < n;
+    const int e = valid ? topk_idx[q] : 0;
+    // lanes of this wave holding the same expert id: AND over the id's bits
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < nb; ++b) {
+      const uint64_t ones = __ballot(valid && ((e >> b) & 1));
+      m &= ((e >> b) & 1) ? ones : ~ones;
+    }
+    const int rw = __popcll(m & below), cw = __popcll(m);
+    if (valid && rw == cw - 1) s_wcnt[wave][e] = cw;
+    __syncthreads();
+    if (valid) {
+      int r = s_run[e] + rw;
+      for (int w = 0; w < wave; ++w) r += s_wcnt[w][e];
+      s_rank[q] = r;
+      s_exp[q] = e;
+    }
+    __syncthreads();
+    if (tid < E) {
+      s_run[tid] += s_wcnt[0][tid] + s_wcnt[1][tid] + s_wcnt[2][tid] + s_wcnt[3][tid];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) s_wcnt[w][tid] = 0;
+    }
+    __syncthreads();
+  }
+
+  // capacity, exclusive scan of the kept counts, dropped total
+  const int cnt = (tid < E) ? s_run[tid] : 0;
+  const int kept = min(cnt, C);
+  const int mt = (mt_prefix != nullptr) ? (kept + bm - 1) / bm : 0;
+  s_off[tid] = kept;
+  s_drop[tid] = cnt - kept;
+  s_mt[tid] = mt;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int a = (tid >= o) ? s_off[tid - o] : 0;
+    const int b = (tid >= o) ? s_drop[tid - o] : 0;
+    const int c = (tid >= o) ? s_mt[tid - o] : 0;
+    __syncthreads();
+    s_off[tid] += a;
+    s_drop[tid] += b;
+    s_mt[tid] += c;
+    __syncthreads();
+  }
+  const int incl = s_off[tid];
+  __syncthreads();
+  s_off[tid] = incl - kept;  // exclusive
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    if (tid < E) {
+      counts[tid] = cnt;
+      offsets[tid] = s_off[tid];
+      if (mt_prefix != nullptr) mt_prefix[tid] = s_mt[tid] - mt;
+    }
+    if (tid == E - 1) {
+      offsets[E] = incl;
+      dropped[0] = s_drop[tid];
+      if (mt_prefix != nullptr) mt_prefix[E] = s_mt[tid];
+    }
+    for (int q = tid; q < n; q += 256) {
+      const int r = s_rank[q], e = s_exp[q];
+      const int dest = (r < C) ? s_off[e] + r : -1;
+      dest_row[q] = dest;
+      if (dest >= 0) row_token[dest] = q / k;
+    }
+  }
+
+  // X rows of this workgroup's tokens, one wavefront per (token, slot)
+  const int t0 = blockIdx.x * tok_per_block;
+  const int nq = min(tok_per_block, T - t0) * k;
+  for (int i = wave; i < nq; i += 4) {
+    const int q = t0 * k + i;
+    const int r = s_rank[q];
+    if (r >= C) continue;
+    const int dest = s_off[s_exp[q]] + r;
+    const i32x4* src = X + (int64_t)(q / k) * row_chunks;
+    i32x4* out = X_perm + (int64_t)dest * row_chunks;
+    for (int c = lane; c < row_chunks; c += kWave) out[c] = src[c];
+  }
+}
+
 template <int KMAX>
 hipError_t launch_k(const void* X, bool x_bf16, const int32_t* topk_idx, int T,
                     int d, int E, int k, int C, int32_t* counts,
                     int32_t* offsets, int32_t* dropped, int32_t* dest_row,
                     int32_t* row_token, void* X_perm, int32_t* local_rank,
-                    int32_t* block_counts, hipStream_t stream) {
+                    int32_t* block_counts, int32_t* mt_prefix, int bm, hipStream_t stream) {
   const int nblk = (T + kPermThreads - 1) / kPermThreads;
   count_rank_kernel<KMAX><<<nblk, kPermThreads, 0, stream>>>(
       topk_idx, T, E, k, local_rank, block_counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  scan_kernel<<<1, 256, 0, stream>>>(block_counts, nblk, E, C, counts, offsets, dropped);
+  scan_kernel<<<1, 256, 0, stream>>>(block_counts, nblk, E, C, counts, offsets, dropped,
+                                     mt_prefix, bm);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int row_chunks = d * (x_bf16 ? 2 : 4) / 16;
@@ -224,19 +345,29 @@ hipError_t launch_permute(const void* X, bool x_bf16, const int32_t* topk_idx,
                           int T, int d, int E, int k, int C, int32_t* counts,
                           int32_t* offsets, int32_t* dropped, int32_t* dest_row,
                           int32_t* row_token, void* X_perm, void* scratch,
-                          hipStream_t stream) {
+                          int32_t* mt_prefix, int bm, hipStream_t stream) {
   int32_t* local_rank = static_cast<int32_t*>(scratch);
   int32_t* block_counts = reinterpret_cast<int32_t*>(
       static_cast<char*>(scratch) + align256((size_t)T * k * 4));
   if (T == 0) {
     // still publish empty counts/offsets so callers see a consistent state
-    scan_kernel<<<1, 256, 0, stream>>>(block_counts, 0, E, C, counts, offsets, dropped);
+    scan_kernel<<<1, 256, 0, stream>>>(block_counts, 0, E, C, counts, offsets, dropped,
+                                       mt_prefix, bm);
+    return hipGetLastError();
+  }
+  if ((int64_t)T * k <= kSmallCopies) {
+    const int row_chunks = d * (x_bf16 ? 2 : 4) / 16;
+    const int tpb = (T + 255) / 256;  // tokens per workgroup: at most 256 workgroups
+    permute_small_kernel<<<(unsigned)((T + tpb - 1) / tpb), 256, 0, stream>>>(
+        static_cast<const i32x4*>(X), topk_idx, T, E, k, C, row_chunks, tpb, counts,
+        offsets, dropped, dest_row, row_token, static_cast<i32x4*>(X_perm), mt_prefix, bm);
     return hipGetLastError();
   }
 #define MOE_PERM_CASE(KM)                                                                 \
   if (k <= KM)                                                                            \
     return launch_k<KM>(X, x_bf16, topk_idx, T, d, E, k, C, counts, offsets, dropped,     \
-                        dest_row, row_token, X_perm, local_rank, block_counts, stream);
+                        dest_row, row_token, X_perm, local_rank, block_counts,       \
+                        mt_prefix, bm, stream);
   MOE_PERM_CASE(1)
   MOE_PERM_CASE(2)
   MOE_PERM_CASE(4)

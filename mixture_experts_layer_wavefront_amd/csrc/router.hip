@@ -110,11 +110,15 @@ __device__ __forceinline__ void topk_softmax_store(float (&v)[VPL], int E, int k
 // fp32 layers: one fused kernel.  TX threads across experts (expert
 // e = tx + TX*j, j < RE), TY = 256/TX
 // threads across tokens (token row = ty + TY*i, i < RT).
-template <int TX, int RE, int RT, typename XT>
+// PARTIAL (bf16 layers with few tokens): workgroup (x, s) covers K range
+// [s*ks, (s+1)*ks) only and writes its partial logits (no bias) to
+// partial[s][t][e] (row stride EP); a select kernel adds the S partials.
+template <int TX, int RE, int RT, typename XT, bool PARTIAL>
 __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(
     const XT* __restrict__ X, const float* __restrict__ W_r,
     const float* __restrict__ bias, int T, int d, int E, int k, int gating,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int ks,
+    float* __restrict__ partial) {
   constexpr int TY = kRouterThreads / TX;
   constexpr int TT = TY * RT;
   constexpr int EP = TX * RE;
@@ -138,31 +142,60 @@ __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(
 #pragma unroll
     for (int j = 0; j < RE; ++j) acc[i][j] = 0.f;
 
-  for (int k0 = 0; k0 < d; k0 += DK) {
-    // stage X[t0:t0+TT, k0:k0+DK] transposed into Xs (zero outside)
-    for (int c = tid; c < TT * CPR; c += kRouterThreads) {
+  const int kbeg = PARTIAL ? (int)blockIdx.y * ks : 0;
+  const int kend = PARTIAL ? min(d, kbeg + ks) : d;
+  // Slices of DK along K go global -> registers -> LDS; the next slice's
+  // loads are in flight while the current one is multiplied.
+  constexpr int XN = (TT * CPR + kRouterThreads - 1) / kRouterThreads;
+  constexpr int WN = (EP * (DK / 4) + kRouterThreads - 1) / kRouterThreads;
+  float xr[XN][VE];
+  f32x4 wr[WN];
+  auto load_slice = [&](int k0) {
+#pragma unroll
+    for (int n = 0; n < XN; ++n) {
+      const int c = tid + n * kRouterThreads;
       const int row = c / CPR, kc = c % CPR;
       const int t = t0 + row, kk = k0 + kc * VE;
-      float v[VE];
-      if (t < T && kk < d) {
-        XLoad<XT>::load(X + (int64_t)t * d + kk, v);
+      if (c < TT * CPR && t < T && kk < kend) {
+        XLoad<XT>::load(X + (int64_t)t * d + kk, xr[n]);
       } else {
 #pragma unroll
-        for (int i = 0; i < VE; ++i) v[i] = 0.f;
+        for (int i = 0; i < VE; ++i) xr[n][i] = 0.f;
       }
-#pragma unroll
-      for (int i = 0; i < VE; ++i) Xs[kc * VE + i][row] = v[i];
     }
-    // stage W_r[:, k0:k0+DK] transposed into Ws (zero outside)
-    for (int c = tid; c < EP * (DK / 4); c += kRouterThreads) {
+#pragma unroll
+    for (int n = 0; n < WN; ++n) {
+      const int c = tid + n * kRouterThreads;
       const int e = c / (DK / 4), kc = c % (DK / 4);
       const int kk = k0 + kc * 4;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (e < E && kk < d) v = *reinterpret_cast<const f32x4*>(W_r + (int64_t)e * d + kk);
+      wr[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (c < EP * (DK / 4) && e < E && kk < kend)
+        wr[n] = *reinterpret_cast<const f32x4*>(W_r + (int64_t)e * d + kk);
+    }
+  };
+  if (kbeg < kend) load_slice(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += DK) {
+    // X[t0:t0+TT, k0:k0+DK] and W_r[:, k0:k0+DK], transposed, into LDS
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Ws[kc * 4 + i][e] = v[i];
+    for (int n = 0; n < XN; ++n) {
+      const int c = tid + n * kRouterThreads;
+      if (c < TT * CPR) {
+        const int row = c / CPR, kc = c % CPR;
+#pragma unroll
+        for (int i = 0; i < VE; ++i) Xs[kc * VE + i][row] = xr[n][i];
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < WN; ++n) {
+      const int c = tid + n * kRouterThreads;
+      if (c < EP * (DK / 4)) {
+        const int e = c / (DK / 4), kc = c % (DK / 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Ws[kc * 4 + i][e] = wr[n][i];
+      }
     }
     __syncthreads();
+    if (k0 + DK < kend) load_slice(k0 + DK);
 #pragma unroll 8
     for (int kk = 0; kk < DK; ++kk) {
       float xv[RT], wv[RE];
@@ -176,6 +209,18 @@ __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(
         for (int j = 0; j < RE; ++j) acc[i][j] = fmaf(xv[i], wv[j], acc[i][j]);
     }
     __syncthreads();
+  }
+
+  if constexpr (PARTIAL) {
+    float* out = partial + (int64_t)blockIdx.y * T * EP;
+#pragma unroll
+    for (int j = 0; j < RE; ++j)
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        const int t = t0 + ty + TY * i;
+        if (t < T) out[(int64_t)t * EP + tx + TX * j] = acc[i][j];
+      }
+    return;
   }
 
   // logits (+ bias, an fp32 add) into LDS
@@ -357,8 +402,17 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + kWave * i;
     if (e < E) {
+      // loads issued sixteen at a time, added in the order s = 0, 1, ...
       float acc = 0.f;
-      for (int s = 0; s < S; ++s) acc += partial[((int64_t)s * T + t) * EP + e];
+      for (int s0 = 0; s0 < S; s0 += 16) {
+        float pv[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          pv[u] = (s0 + u < S) ? partial[((int64_t)(s0 + u) * T + t) * EP + e] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (s0 + u < S) acc += pv[u];
+      }
       v[i] = acc + (bias != nullptr ? bias[e] : 0.f);
     } else {
       v[i] = -INFINITY;
@@ -367,8 +421,16 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   topk_softmax_store<VPL>(v, E, k, gating, lane, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
 }
 
+// Few tokens (bf16): K-split FMA partial logits (no W_r split) + select.
+constexpr int kSmallT = 64;
+#ifndef MOE_RKS
+#define MOE_RKS 128
+#endif
+constexpr int kSmallKS = MOE_RKS;  // K per workgroup
+
 struct RoutePlan {
   int NTE, EP, d32, S, tiles;
+  bool small;
   size_t split_bytes, partial_bytes;
 };
 
@@ -376,6 +438,14 @@ size_t a256r(size_t x) { return (x + 255) & ~size_t(255); }
 
 RoutePlan route_plan(int T, int E, int d) {
   RoutePlan P{};
+  if (T <= kSmallT) {
+    P.small = true;
+    P.EP = E <= 8 ? 8 : E <= 16 ? 16 : E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256;
+    P.S = (d + kSmallKS - 1) / kSmallKS;
+    P.split_bytes = 0;
+    P.partial_bytes = a256r((size_t)P.S * T * P.EP * 4);
+    return P;
+  }
   int nte = (E + 15) / 16, p2 = 1;
   while (p2 < nte) p2 <<= 1;
   P.NTE = p2;
@@ -399,11 +469,22 @@ hipError_t launch_cfg(const void* X, bool x_bf16, const float* W_r,
   constexpr int TT = (kRouterThreads / TX) * RT;
   const dim3 grid((T + TT - 1) / TT);
   if (x_bf16)
-    router_topk_kernel<TX, RE, RT, uint16_t><<<grid, kRouterThreads, 0, stream>>>(
-        static_cast<const uint16_t*>(X), W_r, bias, T, d, E, k, gating, topk_idx, topk_w);
+    router_topk_kernel<TX, RE, RT, uint16_t, false><<<grid, kRouterThreads, 0, stream>>>(
+        static_cast<const uint16_t*>(X), W_r, bias, T, d, E, k, gating, topk_idx, topk_w, 0, nullptr);
   else
-    router_topk_kernel<TX, RE, RT, float><<<grid, kRouterThreads, 0, stream>>>(
-        static_cast<const float*>(X), W_r, bias, T, d, E, k, gating, topk_idx, topk_w);
+    router_topk_kernel<TX, RE, RT, float, false><<<grid, kRouterThreads, 0, stream>>>(
+        static_cast<const float*>(X), W_r, bias, T, d, E, k, gating, topk_idx, topk_w, 0, nullptr);
+  return hipGetLastError();
+}
+
+// bf16 X, few tokens: K-split partial logits (EP = TX * RE columns)
+template <int TX, int RE, int RT>
+hipError_t launch_partial(const uint16_t* X, const float* W_r, int T, int d, int E,
+                          int S, float* partial, hipStream_t stream) {
+  constexpr int TT = (kRouterThreads / TX) * RT;
+  const dim3 grid((T + TT - 1) / TT, S);
+  router_topk_kernel<TX, RE, RT, uint16_t, true><<<grid, kRouterThreads, 0, stream>>>(
+      X, W_r, nullptr, T, d, E, 0, 0, nullptr, nullptr, kSmallKS, partial);
   return hipGetLastError();
 }
 
@@ -420,6 +501,29 @@ hipError_t launch_route(const void* X, bool x_bf16, const float* W_r,
                         int gating, int32_t* topk_idx, float* topk_w,
                         void* scratch, hipStream_t stream) {
   if (T == 0) return hipSuccess;
+  if (x_bf16 && T <= kSmallT) {
+    const RoutePlan P = route_plan(T, E, d);
+    float* partial = static_cast<float*>(scratch);
+    const uint16_t* Xb = static_cast<const uint16_t*>(X);
+    hipError_t err;
+    switch (P.EP) {
+      case 8: err = launch_partial<8, 1, 2>(Xb, W_r, T, d, E, P.S, partial, stream); break;
+      case 16: err = launch_partial<16, 1, 2>(Xb, W_r, T, d, E, P.S, partial, stream); break;
+      case 32: err = launch_partial<32, 1, 2>(Xb, W_r, T, d, E, P.S, partial, stream); break;
+      case 64: err = launch_partial<64, 1, 4>(Xb, W_r, T, d, E, P.S, partial, stream); break;
+      case 128: err = launch_partial<64, 2, 4>(Xb, W_r, T, d, E, P.S, partial, stream); break;
+      default: err = launch_partial<64, 4, 4>(Xb, W_r, T, d, E, P.S, partial, stream); break;
+    }
+    if (err != hipSuccess) return err;
+    const unsigned gs = (unsigned)((T + 3) / 4);
+    if (E <= 64)
+      router_select_kernel<1><<<gs, 256, 0, stream>>>(partial, bias, T, E, P.EP, P.S, k, gating, topk_idx, topk_w);
+    else if (E <= 128)
+      router_select_kernel<2><<<gs, 256, 0, stream>>>(partial, bias, T, E, P.EP, P.S, k, gating, topk_idx, topk_w);
+    else
+      router_select_kernel<4><<<gs, 256, 0, stream>>>(partial, bias, T, E, P.EP, P.S, k, gating, topk_idx, topk_w);
+    return hipGetLastError();
+  }
   if (x_bf16) {
     const RoutePlan P = route_plan(T, E, d);
     uint16_t* Wsplit = static_cast<uint16_t*>(scratch);
