@@ -113,6 +113,24 @@ def test_layer_parity(name):
     _run_and_check(SMALL[name])
 
 
+# Shapes on either side of the few-token / few-copy paths: the K-split router
+# (T <= 64, bf16) and the one-kernel permute (T*k <= 2048), with K not a
+# multiple of the router's K split and expert counts for every router width.
+BOUNDARY = {
+    "copies_2048": WL("copies_2048", 64, 200, 64, 32, 96, W.BF16, TK, 0.0, 0.0, 31),
+    "copies_2080": WL("copies_2080", 65, 200, 64, 32, 96, W.BF16, TK, 0.0, 0.0, 32),
+    "k1_2048_tokens": WL("k1_2048_tokens", 2048, 64, 16, 1, 64, W.BF16, TK, 0.0, 0.0, 33),
+    "few_tokens_E256": WL("few_tokens_E256", 40, 256, 256, 8, 64, W.BF16, ST, 0.0, 0.0, 34),
+    "few_tokens_E4": WL("few_tokens_E4", 10, 136, 4, 2, 64, W.BF16, TK, 0.0, 0.0, 35),
+    "few_tokens_cap": WL("few_tokens_cap", 48, 128, 16, 4, 64, W.BF16, TK, 0.5, 1.2, 36),
+}
+
+
+@pytest.mark.parametrize("name", list(BOUNDARY))
+def test_path_boundaries(name):
+    _run_and_check(BOUNDARY[name])
+
+
 def test_bf16_output_is_the_rounded_fp32_output():
     """out_dtype BF16 stores the same fp32 sum rounded once to bf16 (round to
     nearest even); against the oracle the error is the 2e-2 RMS bar plus that
