@@ -302,6 +302,33 @@ def moe_forward(X, W_r, bias, W_gate, W_up, W_down, k, capacity_factor=None,
     return res
 
 
+# ---------------------------------------------------------------------------
+# Shared expert (the DeepSeek-V3 layer form)
+#     [EP] section "최적화 1: 공유 전문가를 통한 연산-통신 오버랩": next to the
+#     N routed experts the layer has one shared expert that every token goes
+#     through; its output is computed while the routed tokens are dispatched.
+#     Reading (the page gives no formula): the shared expert is the same
+#     SwiGLU FFN applied to every row, added to the routed mixture with weight
+#     one, ``out = shared(x) + sum_j w_j expert_j(x)``.
+# ---------------------------------------------------------------------------
+def shared_expert_ffn(X, Ws_gate, Ws_up, Ws_down):
+    """The shared expert on every token: ``expert_ffn`` over all rows, fp64."""
+    return expert_ffn(X, Ws_gate, Ws_up, Ws_down)
+
+
+def moe_forward_shared(X, W_r, bias, W_gate, W_up, W_down, Ws_gate, Ws_up,
+                       Ws_down, k, capacity_factor=None,
+                       gating=TOPK_THEN_SOFTMAX):
+    """The routed layer plus the shared expert: ``moe_forward`` with
+    ``out += shared_expert_ffn(X)``; the dict also holds ``shared``."""
+    res = moe_forward(X, W_r, bias, W_gate, W_up, W_down, k, capacity_factor,
+                      gating)
+    sh = shared_expert_ffn(X, Ws_gate, Ws_up, Ws_down)
+    res["shared"] = sh
+    res["out"] = res["out"] + sh
+    return res
+
+
 def moe_forward_tokens(tokens, X, idx, w, dest, expert_weights, d_out):
     """Layer output for a subset of tokens, given the full routing.
 

@@ -365,6 +365,55 @@ def test_forward_tokens_matches_full_forward():
 
 
 # ------------------------------------------------------ input generators --
+# ----------------------------------------------------------- shared expert --
+def _torch_swiglu(X, Wg, Wu, Wd):
+    F = torch.nn.functional
+    Xt = torch.from_numpy(np.asarray(X, dtype=np.float64))
+    g, u, dn = (torch.from_numpy(np.asarray(v, dtype=np.float64)) for v in (Wg, Wu, Wd))
+    return F.linear(F.silu(F.linear(Xt, g)) * F.linear(Xt, u), dn).numpy()
+
+
+def test_shared_expert_is_library_swiglu_on_every_token():
+    X, W_r, b, Wg, Wu, Wd = _rand_layer(17, 16, 4, 2, 12, seed=41)
+    rng = np.random.default_rng(42)
+    Sg, Su = rng.standard_normal((2, 20, 16)) / 4
+    Sd = rng.standard_normal((16, 20)) / 4
+    np.testing.assert_allclose(O.shared_expert_ffn(X, Sg, Su, Sd),
+                               _torch_swiglu(X, Sg, Su, Sd), rtol=1e-12,
+                               atol=1e-12)
+
+
+def test_shared_expert_is_a_one_expert_routed_layer():
+    """An E = 1, k = 1 routed layer sends every token to its expert with gate
+    weight exactly 1: the same map as the shared expert."""
+    X, W_r, b, Wg, Wu, Wd = _rand_layer(13, 8, 1, 1, 10, seed=43)
+    routed = O.moe_forward(X, W_r, b, Wg, Wu, Wd, 1)["out"]
+    np.testing.assert_allclose(O.shared_expert_ffn(X, Wg[0], Wu[0], Wd[0]),
+                               routed, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("cf", [None, 0.5])
+def test_layer_with_shared_expert_matches_brute_force(cf):
+    X, W_r, b, Wg, Wu, Wd = _rand_layer(30, 8, 5, 2, 12, seed=44,
+                                        bias_scale=1.0)
+    rng = np.random.default_rng(45)
+    Sg, Su = rng.standard_normal((2, 6, 8)) / 3
+    Sd = rng.standard_normal((8, 6)) / 3
+    res = O.moe_forward_shared(X, W_r, b, Wg, Wu, Wd, Sg, Su, Sd, 2, cf)
+    ref = (_brute_force(X, W_r, b, Wg, Wu, Wd, 2, cf, O.TOPK_THEN_SOFTMAX)
+           + _torch_swiglu(X, Sg, Su, Sd))
+    np.testing.assert_allclose(res["out"], ref, rtol=1e-10, atol=1e-12)
+    # a zero shared expert leaves the routed layer unchanged; tokens whose
+    # copies were all dropped still get the shared expert's output
+    z = O.moe_forward_shared(X, W_r, b, Wg, Wu, Wd, 0 * Sg, 0 * Su, 0 * Sd, 2, cf)
+    np.testing.assert_array_equal(z["out"], O.moe_forward(X, W_r, b, Wg, Wu, Wd, 2, cf)["out"])
+    if cf is not None:
+        empty = np.all(res["dest"] < 0, axis=1)
+        assert empty.any()
+        np.testing.assert_allclose(res["out"][empty], _torch_swiglu(X[empty], Sg, Su, Sd),
+                                   rtol=1e-12, atol=1e-12)
+
+
 def test_round_bf16_matches_torch_conversion():
     rng = np.random.default_rng(16)
     x = (rng.standard_normal(100000) * 10.0 ** rng.integers(-5, 5, 100000)
