@@ -34,6 +34,9 @@ def _parse():
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--shared-dff", type=int, default=0,
+                    help="add a shared expert of this hidden size (the "
+                         "DeepSeek-V3 layer form; moe_forward_shared)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -91,7 +94,7 @@ def _time_loop(fn, steps, stream):
     return s.elapsed_time(e) / steps  # ms per call
 
 
-def _cpu_baseline(wl, dev, ntok, min_s=10.0, max_s=30.0):
+def _cpu_baseline(wl, dev, ntok, min_s=10.0, max_s=30.0, shared=None):
     """The CPU oracle (as it stands) on the first `ntok` tokens of the same
     batch with the same weights, repeated until at least `min_s` seconds of
     CPU work (stopping before `max_s`); returns the dict for the JSON line."""
@@ -107,8 +110,13 @@ def _cpu_baseline(wl, dev, ntok, min_s=10.0, max_s=30.0):
     runs, total = 0, 0.0
     while total < min_s:
         t0 = time.perf_counter()
-        O.moe_forward(X, host["W_r"], host["bias"], host["W_gate"], host["W_up"],
-                      host["W_down"], wl.top_k, cf if cf > 0 else None, wl.gating)
+        if shared is None:
+            O.moe_forward(X, host["W_r"], host["bias"], host["W_gate"], host["W_up"],
+                          host["W_down"], wl.top_k, cf if cf > 0 else None, wl.gating)
+        else:
+            O.moe_forward_shared(X, host["W_r"], host["bias"], host["W_gate"],
+                                 host["W_up"], host["W_down"], *shared, wl.top_k,
+                                 cf if cf > 0 else None, wl.gating)
         dt = time.perf_counter() - t0
         runs += 1
         total += dt
@@ -118,8 +126,8 @@ def _cpu_baseline(wl, dev, ntok, min_s=10.0, max_s=30.0):
     return {"value": ntok * runs / total, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"first {ntok} of the {wl.T} tokens, all {wl.E} experts "
-                      f"(full weights), fp64 NumPy per-expert loop, {runs} run(s), "
-                      f"{total:.1f} s wall"}
+                      f"(full weights{', plus the shared expert' if shared is not None else ''}), "
+                      f"fp64 NumPy per-expert loop, {runs} run(s), {total:.1f} s wall"}
 
 
 def main():
@@ -153,6 +161,21 @@ def main():
 
     def step():
         M.moe_forward(p, *a, out=out, stats=stats, workspace=ws)
+
+    shared = None
+    if args.shared_dff > 0:
+        S = W.make_shared_device(wl, args.shared_dff, "cuda")
+        ws_sh = torch.empty(M.forward_shared_workspace_bytes(p, args.shared_dff),
+                            dtype=torch.uint8, device="cuda")
+
+        def step():  # noqa: F811
+            M.moe_forward_shared(p, args.shared_dff, *a, *S, out=out, stats=stats,
+                                 workspace=ws_sh)
+
+        def step_serial():
+            M.moe_forward_shared(p, args.shared_dff, *a, *S, out=out, stats=stats,
+                                 workspace=ws_sh, side_stream=None)
+        shared = (S, ws_sh, step_serial)
 
     for _ in range(args.warmup):
         step()
@@ -235,8 +258,23 @@ def main():
                     "max_over_mean_load": float(counts.max() / max(counts.mean(), 1e-9))},
         "wall_s_timed": wall,
     }
+    if shared is not None:
+        S, ws_sh, step_serial = shared
+        for _ in range(2):
+            step_serial()
+        t_serial = _time_loop(step_serial, n, stream)
+        t_routed = _time_loop(lambda: M.moe_forward(p, *a, out=out, stats=stats,
+                                                    workspace=ws), n, stream)
+        sh_flops = 6.0 * T * d * args.shared_dff
+        line["config"]["shared_d_ff"] = args.shared_dff
+        line["config"]["workload"] += f", plus a shared expert (SwiGLU d_ff={args.shared_dff}) on every token"
+        line["shared_expert"] = {
+            "ms_per_step_side_stream": ms, "ms_per_step_one_stream": t_serial,
+            "ms_routed_layer_alone": t_routed, "shared_ffn_flops": sh_flops}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = _cpu_baseline(wl, dev, args.cpu_sample_tokens)
+        line["cpu_baseline"] = _cpu_baseline(
+            wl, dev, args.cpu_sample_tokens,
+            shared=None if shared is None else [t.float().cpu().numpy() for t in shared[0]])
     print(json.dumps(line), flush=True)
 
 

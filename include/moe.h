@@ -195,6 +195,34 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* X,
                          const void* W_down, void* out, int32_t* stats,
                          void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* The layer with a shared expert (the DeepSeek-V3 layer form; "5.3 Expert
+ * Parallelism", section "최적화 1: 공유 전문가를 통한 연산-통신 오버랩": next
+ * to the routed experts one shared expert processes every token, and its
+ * computation overlaps the routed experts' dispatch on another stream).
+ *   out[t] = shared(X[t]) + moe(X)[t], shared = the same SwiGLU FFN on every
+ *   row, with weights
+ *     Ws_gate, Ws_up [shared_d_ff, d_model], Ws_down [d_model, shared_d_ff]
+ *     (act dtype, like the expert weights).
+ * The shared FFN's output (fp32) is the first term of each output row's fp32
+ * sum, then the routed copies in slot order; one rounding at the store.
+ * side_stream: NULL runs everything on `stream`; otherwise the shared FFN runs
+ * on side_stream, ordered after the work already queued on `stream` and
+ * joined back into `stream` before the combine (two events created and
+ * released inside the call).  The result is bit-identical either way.
+ * shared_d_ff: 8 <= shared_d_ff <= 2^20, a multiple of 8, else
+ * MOE_ERR_UNSUPPORTED.  stats as in moe_forward.
+ *   workspace >= moe_forward_shared_workspace_bytes(p, shared_d_ff) bytes */
+size_t moe_forward_shared_workspace_bytes(const moe_problem_t* p,
+                                          int32_t shared_d_ff);
+moe_status_t moe_forward_shared(const moe_problem_t* p, int32_t shared_d_ff,
+                                const void* X, const float* W_r,
+                                const float* bias, const void* W_gate,
+                                const void* W_up, const void* W_down,
+                                const void* Ws_gate, const void* Ws_up,
+                                const void* Ws_down, void* out, int32_t* stats,
+                                void* workspace, size_t ws_bytes,
+                                hipStream_t stream, hipStream_t side_stream);
+
 /* Static string naming a status code. */
 const char* moe_status_string(moe_status_t s);
 

@@ -6,8 +6,10 @@ script (``build``) and the seeded synthetic inputs (``workloads``).
 """
 from .binding import (MOE_BF16, MOE_F32, MOE_SOFTMAX_THEN_TOPK,  # noqa: F401
                       MOE_TOPK_THEN_SOFTMAX, MoeError, Problem, capacity,
+                      forward_shared_workspace_bytes,
                       grouped_ffn_workspace_bytes, load, moe_combine,
-                      moe_forward, moe_grouped_ffn, moe_permute, moe_route,
+                      moe_forward, moe_forward_shared, moe_grouped_ffn,
+                      moe_permute, moe_route,
                       permute_workspace_bytes, problem, route_workspace_bytes,
                       rows_bound,
                       workspace_bytes)

@@ -29,7 +29,8 @@ SYMBOLS = ("moe_capacity", "moe_rows_bound", "moe_route_workspace_bytes",
            "moe_permute_workspace_bytes",
            "moe_grouped_ffn_workspace_bytes", "moe_workspace_bytes",
            "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
-           "moe_forward", "moe_status_string")
+           "moe_forward", "moe_forward_shared_workspace_bytes",
+           "moe_forward_shared", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -78,6 +79,10 @@ def load(path: str = LIB_PATH):
         "moe_combine": (ctypes.c_int, [P, vp, vp, vp, vp, st]),
         "moe_forward": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        sz, st]),
+        "moe_forward_shared_workspace_bytes": (sz, [P, ctypes.c_int32]),
+        "moe_forward_shared": (ctypes.c_int, [P, ctypes.c_int32, vp, vp, vp, vp,
+                                              vp, vp, vp, vp, vp, vp, vp, vp,
+                                              sz, st, st]),
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -272,4 +277,47 @@ def moe_forward(p, X, W_r, bias, W_gate, W_up, W_down, out=None, stats=None,
         _ptr(out, _out_dtype(p), "out"), _ptr(stats, torch.int32, "stats"),
         _ptr(ws),
         ws.numel(), _stream(stream)), "moe_forward")
+    return out
+
+
+def forward_shared_workspace_bytes(p: Problem, shared_d_ff: int) -> int:
+    return load().moe_forward_shared_workspace_bytes(ctypes.byref(p),
+                                                     int(shared_d_ff))
+
+
+_side_streams = {}
+
+
+def _side_stream(device):
+    """One extra stream per device (default priority) for the shared expert."""
+    torch = _torch()
+    key = torch.device(device).index
+    if key not in _side_streams:
+        _side_streams[key] = torch.cuda.Stream(device=device)
+    return _side_streams[key]
+
+
+def moe_forward_shared(p, shared_d_ff, X, W_r, bias, W_gate, W_up, W_down,
+                       Ws_gate, Ws_up, Ws_down, out=None, stats=None,
+                       workspace=None, stream=None, side_stream="auto"):
+    """The layer plus a shared expert (Ws_gate/Ws_up [shared_d_ff, d],
+    Ws_down [d, shared_d_ff]).  side_stream: "auto" (a per-device extra
+    stream), None (everything on `stream`) or a torch stream."""
+    torch = _torch()
+    dev = X.device
+    if out is None:
+        out = torch.empty((p.T, p.d_model), dtype=_out_dtype(p), device=dev)
+    ws = _workspace(forward_shared_workspace_bytes(p, shared_d_ff), dev, workspace)
+    wt = _act_dtype(p)
+    if isinstance(side_stream, str):
+        side_stream = _side_stream(dev)
+    side = None if side_stream is None else ctypes.c_void_p(side_stream.cuda_stream)
+    _check(load().moe_forward_shared(
+        ctypes.byref(p), int(shared_d_ff), _ptr(X, wt, "X"),
+        _ptr(W_r, torch.float32, "W_r"), _ptr(bias, torch.float32, "bias"),
+        _ptr(W_gate, wt, "W_gate"), _ptr(W_up, wt, "W_up"),
+        _ptr(W_down, wt, "W_down"), _ptr(Ws_gate, wt, "Ws_gate"),
+        _ptr(Ws_up, wt, "Ws_up"), _ptr(Ws_down, wt, "Ws_down"),
+        _ptr(out, _out_dtype(p), "out"), _ptr(stats, torch.int32, "stats"),
+        _ptr(ws), ws.numel(), _stream(stream), side), "moe_forward_shared")
     return out

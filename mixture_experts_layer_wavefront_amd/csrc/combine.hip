@@ -28,7 +28,7 @@ template <bool OUT_BF16>
 __global__ __launch_bounds__(kTokPerBlock * kWave) void combine_kernel(
     const float* __restrict__ Y, const int32_t* __restrict__ dest_row,
     const float* __restrict__ topk_w, int T, int d, int k,
-    void* __restrict__ out) {
+    const float* __restrict__ add_rows, void* __restrict__ out) {
   __shared__ int32_t s_dest[kTokPerBlock][32];
   __shared__ float s_w[kTokPerBlock][32];
   const int lane = threadIdx.x % kWave;
@@ -46,8 +46,18 @@ __global__ __launch_bounds__(kTokPerBlock * kWave) void combine_kernel(
   const int c = blockIdx.y * kWave + lane;  // 8-column chunk
   if (c >= d / 8) return;
   float acc[8];
+  if (add_rows != nullptr) {
+    const f32x4* a0 = reinterpret_cast<const f32x4*>(add_rows + (int64_t)t * d) + 2 * c;
+    const f32x4 u = a0[0], v = a0[1];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int i = 0; i < 4; ++i) {
+      acc[i] = u[i];
+      acc[4 + i] = v[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  }
   for (int j0 = 0; j0 < k; j0 += 8) {
     f32x4 a[8], b[8];
     int r[8];
@@ -89,13 +99,14 @@ __global__ __launch_bounds__(kTokPerBlock * kWave) void combine_kernel(
 
 hipError_t launch_combine(const float* Y_perm, const int32_t* dest_row,
                           const float* topk_w, int T, int d, int k,
-                          bool out_bf16, void* out, hipStream_t stream) {
+                          const float* add_rows, bool out_bf16, void* out,
+                          hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const dim3 grid((T + kTokPerBlock - 1) / kTokPerBlock, (d + kColsPerWave - 1) / kColsPerWave);
   if (out_bf16)
-    combine_kernel<true><<<grid, kTokPerBlock * kWave, 0, stream>>>(Y_perm, dest_row, topk_w, T, d, k, out);
+    combine_kernel<true><<<grid, kTokPerBlock * kWave, 0, stream>>>(Y_perm, dest_row, topk_w, T, d, k, add_rows, out);
   else
-    combine_kernel<false><<<grid, kTokPerBlock * kWave, 0, stream>>>(Y_perm, dest_row, topk_w, T, d, k, out);
+    combine_kernel<false><<<grid, kTokPerBlock * kWave, 0, stream>>>(Y_perm, dest_row, topk_w, T, d, k, add_rows, out);
   return hipGetLastError();
 }
 

@@ -42,9 +42,14 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
                               float* Y_perm, void* scratch, bool prefix_ready,
                               hipStream_t stream);
 
-// Gate-weighted gather-combine back to token order.
+// Expert offsets {0, T} of a dense FFN over all T rows (one "expert").
+hipError_t launch_dense_offsets(int32_t* offsets, int T, hipStream_t stream);
+
+// Gate-weighted gather-combine back to token order.  add_rows ([T, d] fp32 or
+// nullptr) is the first term of every output row's sum.
 hipError_t launch_combine(const float* Y_perm, const int32_t* dest_row,
                           const float* topk_w, int T, int d, int k,
-                          bool out_bf16, void* out, hipStream_t stream);
+                          const float* add_rows, bool out_bf16, void* out,
+                          hipStream_t stream);
 
 }  // namespace moe

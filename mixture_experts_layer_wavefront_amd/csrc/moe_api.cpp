@@ -82,6 +82,68 @@ ForwardLayout forward_layout(const moe_problem_t* p) {
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Shared expert region, after the routed layer's workspace.
+struct SharedLayout {
+  size_t offsets, ffn_scratch, y_shared, total;
+};
+
+SharedLayout shared_layout(const moe_problem_t* p, int sdff, size_t base) {
+  SharedLayout S{};
+  size_t o = base;
+  S.offsets = o; o += 256;
+  S.ffn_scratch = o; o += a256(moe::ffn_scratch_bytes(p->T, 1, sdff, is_bf16(p)));
+  S.y_shared = o; o += a256((size_t)p->T * p->d_model * 4);
+  S.total = o;
+  return S;
+}
+
+moe_status_t validate_shared(int sdff) {
+  if (sdff <= 0) return MOE_ERR_INVALID_ARG;
+  if (sdff % 8 != 0 || sdff > kMaxDim) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Route, permute and the grouped FFN of the whole layer on `stream`; the
+// combine's inputs are left in the workspace (see forward_layout).
+struct RoutedOut {
+  int32_t* dest_row;
+  float* topk_w;
+  float* y_perm;
+};
+
+hipError_t enqueue_routed(const moe_problem_t* p, const void* X, const float* W_r,
+                          const float* bias, const void* W_gate, const void* W_up,
+                          const void* W_down, int32_t* stats, char* ws,
+                          const ForwardLayout& L, hipStream_t stream, RoutedOut* r) {
+  int32_t* topk_idx = reinterpret_cast<int32_t*>(ws + L.topk_idx);
+  float* topk_w = reinterpret_cast<float*>(ws + L.topk_w);
+  int32_t* st_buf = stats ? stats : reinterpret_cast<int32_t*>(ws + L.stats);
+  int32_t* counts = st_buf;
+  int32_t* offsets = st_buf + p->E;
+  int32_t* dropped = st_buf + 2 * p->E + 1;
+  int32_t* dest_row = reinterpret_cast<int32_t*>(ws + L.dest_row);
+  int32_t* row_token = reinterpret_cast<int32_t*>(ws + L.row_token);
+  void* x_perm = ws + L.x_perm;
+  float* y_perm = reinterpret_cast<float*>(ws + L.y_perm);
+  const bool bf = is_bf16(p);
+  *r = RoutedOut{dest_row, topk_w, y_perm};
+
+  hipError_t e = moe::launch_route(X, bf, W_r, bias, p->T, p->d_model, p->E, p->top_k,
+                                   (int)p->gating, topk_idx, topk_w, ws + L.route_scratch,
+                                   stream);
+  if (e != hipSuccess) return e;
+  // the permute also writes the FFN's tile schedule (start of its scratch)
+  const int bm = moe::ffn_tile_rows(bf, mean_rows_per_expert(p));
+  int32_t* mt_prefix = bm > 0 ? reinterpret_cast<int32_t*>(ws + L.ffn_scratch) : nullptr;
+  e = moe::launch_permute(X, bf, topk_idx, p->T, p->d_model, p->E, p->top_k,
+                          capacity_int(p), counts, offsets, dropped, dest_row, row_token,
+                          x_perm, ws + L.perm_scratch, mt_prefix, bm, stream);
+  if (e != hipSuccess) return e;
+  return moe::launch_grouped_ffn(x_perm, bf, offsets, W_gate, W_up, W_down, moe_rows_bound(p),
+                                 p->d_model, p->E, p->d_ff, mean_rows_per_expert(p), y_perm,
+                                 ws + L.ffn_scratch, mt_prefix != nullptr, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -178,7 +240,7 @@ moe_status_t moe_combine(const moe_problem_t* p, const float* Y_perm,
   if (p->T == 0) return MOE_OK;
   if (!Y_perm || !dest_row || !topk_w || !out) return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_combine(Y_perm, dest_row, topk_w, p->T, p->d_model,
-                                        p->top_k, out_bf16(p), out, stream));
+                                        p->top_k, nullptr, out_bf16(p), out, stream));
 }
 
 moe_status_t moe_forward(const moe_problem_t* p, const void* X, const float* W_r,
@@ -192,35 +254,65 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* X, const float* W_r
   const ForwardLayout L = forward_layout(p);
   if (!workspace || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
-  int32_t* topk_idx = reinterpret_cast<int32_t*>(ws + L.topk_idx);
-  float* topk_w = reinterpret_cast<float*>(ws + L.topk_w);
-  int32_t* st_buf = stats ? stats : reinterpret_cast<int32_t*>(ws + L.stats);
-  int32_t* counts = st_buf;
-  int32_t* offsets = st_buf + p->E;
-  int32_t* dropped = st_buf + 2 * p->E + 1;
-  int32_t* dest_row = reinterpret_cast<int32_t*>(ws + L.dest_row);
-  int32_t* row_token = reinterpret_cast<int32_t*>(ws + L.row_token);
-  void* x_perm = ws + L.x_perm;
-  float* y_perm = reinterpret_cast<float*>(ws + L.y_perm);
-  const bool bf = is_bf16(p);
+  RoutedOut r{};
+  hipError_t e = enqueue_routed(p, X, W_r, bias, W_gate, W_up, W_down, stats, ws, L, stream, &r);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_combine(r.y_perm, r.dest_row, r.topk_w, p->T, p->d_model, p->top_k,
+                          nullptr, out_bf16(p), out, stream);
+  return hip_status(e);
+}
 
-  hipError_t e = moe::launch_route(X, bf, W_r, bias, p->T, p->d_model, p->E, p->top_k,
-                                   (int)p->gating, topk_idx, topk_w, ws + L.route_scratch,
-                                   stream);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  // the permute also writes the FFN's tile schedule (start of its scratch)
-  const int bm = moe::ffn_tile_rows(bf, mean_rows_per_expert(p));
-  int32_t* mt_prefix = bm > 0 ? reinterpret_cast<int32_t*>(ws + L.ffn_scratch) : nullptr;
-  e = moe::launch_permute(X, bf, topk_idx, p->T, p->d_model, p->E, p->top_k,
-                          capacity_int(p), counts, offsets, dropped, dest_row, row_token,
-                          x_perm, ws + L.perm_scratch, mt_prefix, bm, stream);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  e = moe::launch_grouped_ffn(x_perm, bf, offsets, W_gate, W_up, W_down, moe_rows_bound(p),
-                              p->d_model, p->E, p->d_ff, mean_rows_per_expert(p), y_perm,
-                              ws + L.ffn_scratch, mt_prefix != nullptr, stream);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  e = moe::launch_combine(y_perm, dest_row, topk_w, p->T, p->d_model, p->top_k,
-                          out_bf16(p), out, stream);
+size_t moe_forward_shared_workspace_bytes(const moe_problem_t* p, int32_t shared_d_ff) {
+  if (validate(p) != MOE_OK || validate_shared(shared_d_ff) != MOE_OK) return 0;
+  return shared_layout(p, shared_d_ff, forward_layout(p).total).total;
+}
+
+moe_status_t moe_forward_shared(const moe_problem_t* p, int32_t shared_d_ff,
+                                const void* X, const float* W_r, const float* bias,
+                                const void* W_gate, const void* W_up, const void* W_down,
+                                const void* Ws_gate, const void* Ws_up, const void* Ws_down,
+                                void* out, int32_t* stats, void* workspace, size_t ws_bytes,
+                                hipStream_t stream, hipStream_t side_stream) {
+  moe_status_t st = validate(p);
+  if (st != MOE_OK) return st;
+  if ((st = validate_shared(shared_d_ff)) != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;
+  if (!X || !W_r || !W_gate || !W_up || !W_down || !Ws_gate || !Ws_up || !Ws_down || !out)
+    return MOE_ERR_INVALID_ARG;
+  const ForwardLayout L = forward_layout(p);
+  const SharedLayout S = shared_layout(p, shared_d_ff, L.total);
+  if (!workspace || ws_bytes < S.total) return MOE_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* s_offsets = reinterpret_cast<int32_t*>(ws + S.offsets);
+  float* y_shared = reinterpret_cast<float*>(ws + S.y_shared);
+
+  // fork: the shared FFN on side_stream after what `stream` already holds
+  hipEvent_t fork = nullptr, join = nullptr;
+  hipStream_t ss = stream;
+  hipError_t e = hipSuccess;
+  if (side_stream != nullptr) {
+    ss = side_stream;
+    if ((e = hipEventCreateWithFlags(&fork, hipEventDisableTiming)) == hipSuccess &&
+        (e = hipEventCreateWithFlags(&join, hipEventDisableTiming)) == hipSuccess &&
+        (e = hipEventRecord(fork, stream)) == hipSuccess)
+      e = hipStreamWaitEvent(side_stream, fork, 0);
+  }
+  if (e == hipSuccess) e = moe::launch_dense_offsets(s_offsets, p->T, ss);
+  if (e == hipSuccess)
+    e = moe::launch_grouped_ffn(X, is_bf16(p), s_offsets, Ws_gate, Ws_up, Ws_down, p->T,
+                                p->d_model, 1, shared_d_ff, p->T, y_shared,
+                                ws + S.ffn_scratch, false, ss);
+  if (e == hipSuccess && side_stream != nullptr) e = hipEventRecord(join, side_stream);
+  RoutedOut r{};
+  if (e == hipSuccess)
+    e = enqueue_routed(p, X, W_r, bias, W_gate, W_up, W_down, stats, ws, L, stream, &r);
+  // join before the combine adds the shared rows
+  if (e == hipSuccess && side_stream != nullptr) e = hipStreamWaitEvent(stream, join, 0);
+  if (e == hipSuccess)
+    e = moe::launch_combine(r.y_perm, r.dest_row, r.topk_w, p->T, p->d_model, p->top_k,
+                            y_shared, out_bf16(p), out, stream);
+  if (fork) (void)hipEventDestroy(fork);
+  if (join) (void)hipEventDestroy(join);
   return hip_status(e);
 }
 

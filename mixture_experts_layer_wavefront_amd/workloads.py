@@ -48,6 +48,7 @@ SOFTMAX_THEN_TOPK = 1
 
 # tensor ids of the per-tensor random streams
 _X, _WR, _WG, _WU, _WD, _PERM = 0, 1, 2, 3, 4, 5
+_SG, _SU, _SD = 6, 7, 8   # shared-expert projections
 
 
 @dataclass(frozen=True)
@@ -147,6 +148,34 @@ def make_expert(w: Workload, e: int):
     Wd = _normal(_rng(w.seed, _WD, e), (w.d_model, w.d_ff),
                  _std(w, w.d_ff), bf)
     return Wg, Wu, Wd
+
+
+def make_shared(w: Workload, shared_d_ff: int):
+    """Host weights of a shared expert with hidden size shared_d_ff:
+    (Ws_gate [sdff, d], Ws_up [sdff, d], Ws_down [d, sdff]), drawn like the
+    expert weights from their own streams."""
+    bf = w.dtype == BF16
+    Sg = _normal(_rng(w.seed, _SG), (shared_d_ff, w.d_model), _std(w, w.d_model), bf)
+    Su = _normal(_rng(w.seed, _SU), (shared_d_ff, w.d_model), _std(w, w.d_model), bf)
+    Sd = _normal(_rng(w.seed, _SD), (w.d_model, shared_d_ff), _std(w, shared_d_ff), bf)
+    return Sg, Su, Sd
+
+
+def make_shared_device(w: Workload, shared_d_ff: int, device="cuda"):
+    """Shared-expert weights drawn on the device (one seeded torch generator
+    per projection), in the activation dtype."""
+    import torch
+
+    tdt = torch.bfloat16 if w.dtype == BF16 else torch.float32
+    g = torch.Generator(device=device)
+    out = []
+    for tid, shape, fan in ((_SG, (shared_d_ff, w.d_model), w.d_model),
+                            (_SU, (shared_d_ff, w.d_model), w.d_model),
+                            (_SD, (w.d_model, shared_d_ff), shared_d_ff)):
+        g.manual_seed((w.seed * 1_000_003 + tid * 65_537) & (2**63 - 1))
+        t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        out.append(t.mul_(_std(w, fan)).to(tdt))
+    return tuple(out)
 
 
 def make_host(w: Workload):

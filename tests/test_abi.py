@@ -122,6 +122,31 @@ def test_null_pointers_and_small_workspace_rejected():
     assert r == B.MOE_ERR_WORKSPACE
 
 
+def test_shared_expert_arguments_checked_on_the_host():
+    lib = B.load()
+    p = B.problem(8, 64, 4, 2, 64)
+    fake = ctypes.c_void_p(0x1000)
+    base = lib.moe_workspace_bytes(ctypes.byref(p))
+    need = lib.moe_forward_shared_workspace_bytes(ctypes.byref(p), 96)
+    # the routed layer's workspace plus the shared FFN's H, schedule and rows
+    assert need >= base + 8 * 96 * 2 + 8 * 64 * 4
+    assert lib.moe_forward_shared_workspace_bytes(ctypes.byref(p), 12) == 0
+    args = [fake] * 9
+    for sdff, status in ((0, B.MOE_ERR_INVALID_ARG), (-8, B.MOE_ERR_INVALID_ARG),
+                         (12, B.MOE_ERR_UNSUPPORTED), ((1 << 20) + 8, B.MOE_ERR_UNSUPPORTED)):
+        assert lib.moe_forward_shared(ctypes.byref(p), sdff, *args, fake, None,
+                                      fake, 1 << 40, None, None) == status
+    # a missing shared weight, then a workspace one byte short
+    bad = [fake] * 6 + [None] + [fake] * 2
+    assert lib.moe_forward_shared(ctypes.byref(p), 96, *bad, fake, None, fake,
+                                  need, None, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward_shared(ctypes.byref(p), 96, *args, fake, None, fake,
+                                  need - 1, None, None) == B.MOE_ERR_WORKSPACE
+    p0 = B.problem(0, 64, 4, 2, 64)
+    assert lib.moe_forward_shared(ctypes.byref(p0), 96, *([None] * 9), None, None,
+                                  None, 0, None, None) == B.MOE_OK
+
+
 def test_empty_batch_is_a_noop_without_device_work():
     lib = B.load()
     p = B.problem(0, 64, 4, 2, 64)
