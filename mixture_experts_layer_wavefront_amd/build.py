@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
 
-SOURCES = ["router.hip", "permute.hip", "grouped_gemm.hip", "combine.hip",
+SOURCES = ["router.hip", "permute.hip", "grouped_gemm.hip", "combine.hip", "dense_offsets.hip",
            "moe_api.cpp"]
 ARCH = "gfx950"
 

@@ -424,15 +424,6 @@ hipError_t launch_gemm(const void* A, const void* B0, const void* B1, int N,
 
 }  // namespace
 
-__global__ void dense_offsets_kernel(int32_t* __restrict__ offsets, int T) {
-  if (threadIdx.x < 2) offsets[threadIdx.x] = threadIdx.x == 0 ? 0 : T;
-}
-
-hipError_t launch_dense_offsets(int32_t* offsets, int T, hipStream_t stream) {
-  dense_offsets_kernel<<<1, 64, 0, stream>>>(offsets, T);
-  return hipGetLastError();
-}
-
 int ffn_tile_rows(bool bf16, int rows_per_expert) {
   if (!bf16) return 0;
   return rows_per_expert <= 64 ? 32 : 256;
