@@ -303,6 +303,50 @@ def moe_forward(X, W_r, bias, W_gate, W_up, W_down, k, capacity_factor=None,
 
 
 # ---------------------------------------------------------------------------
+# Router statistics (monitoring; forward values only, no gradients)
+#     [SG] "로드 밸런싱 손실과 용량은 별개": the Sparsely-Gated MoE auxiliary
+#     loss balances expert importance and load; GShard's auxiliary loss uses
+#     the dispatch fraction and the mean gate value; ST-MoE's router z-loss
+#     keeps router logits small.  [HF] "라우팅 분포와 학습 안정성" asks for
+#     routing-distribution monitoring hooks.  Readings (the pages print no
+#     formula; these are the published definitions the names refer to):
+#       importance[e] = sum_t of the gate weight token t gives expert e
+#                       (0 when e is not selected)
+#       count[e]      = copies routed to e (top-k selections, before capacity)
+#       mean_prob[e]  = mean over tokens of softmax over all E logits
+#       aux_loss      = E * sum_e (count[e] / (T k)) * mean_prob[e]
+#                       (1 for a uniform router with any routing)
+#       z_loss        = mean over tokens of (logsumexp_e logit[t, e])^2
+#     The logits are the router's fp32 logits (bias included).
+# ---------------------------------------------------------------------------
+def router_stats(logits, idx, w):
+    """Router statistics from fp32 logits [T, E], selected ids [T, k] and gate
+    weights [T, k]; fp64.  Returns dict importance, count, mean_prob [E] and
+    aux_loss, z_loss (floats)."""
+    lg = _f64(logits)
+    T, E = lg.shape
+    idx = np.asarray(idx)
+    w = _f64(w)
+    k = idx.shape[1] if idx.ndim == 2 else 0
+    importance = np.zeros(E)
+    count = np.zeros(E)
+    for t in range(T):
+        for j in range(k):
+            importance[idx[t, j]] += w[t, j]
+            count[idx[t, j]] += 1.0
+    m = lg.max(axis=1, keepdims=True)
+    ex = np.exp(lg - m)
+    Z = ex.sum(axis=1, keepdims=True)
+    prob = ex / Z
+    lse = (m + np.log(Z))[:, 0]
+    mean_prob = prob.mean(axis=0) if T else np.zeros(E)
+    aux = float(E * np.sum(count / max(T * k, 1) * mean_prob))
+    z = float(np.mean(lse ** 2)) if T else 0.0
+    return dict(importance=importance, count=count, mean_prob=mean_prob,
+                aux_loss=aux, z_loss=z)
+
+
+# ---------------------------------------------------------------------------
 # Shared expert (the DeepSeek-V3 layer form)
 #     [EP] section "최적화 1: 공유 전문가를 통한 연산-통신 오버랩": next to the
 #     N routed experts the layer has one shared expert that every token goes

@@ -365,6 +365,78 @@ def test_forward_tokens_matches_full_forward():
 
 
 # ------------------------------------------------------ input generators --
+# ------------------------------------------------------- router statistics --
+def test_router_stats_uniform_router_closed_forms():
+    """Equal logits: every mean probability is 1/E, the z-loss is (ln E)^2
+    and the auxiliary loss is exactly 1 whatever the routing."""
+    T, E, k = 7, 6, 2
+    lg = np.full((T, E), 0.75, dtype=np.float32)
+    idx, _ = O.select_topk(lg, k)
+    w = O.gate_weights(lg, idx, O.TOPK_THEN_SOFTMAX)
+    st = O.router_stats(lg, idx, w)
+    np.testing.assert_allclose(st["mean_prob"], 1.0 / E, rtol=1e-14)
+    np.testing.assert_allclose(st["z_loss"], (0.75 + math.log(E)) ** 2, rtol=1e-14)
+    assert abs(st["aux_loss"] - 1.0) < 1e-14
+    # ties go to the lower ids: experts 0 and 1 take every token at weight 1/2
+    np.testing.assert_array_equal(st["count"], [T, T, 0, 0, 0, 0])
+    np.testing.assert_allclose(st["importance"], [T / 2, T / 2, 0, 0, 0, 0])
+
+
+def test_router_stats_worked_example():
+    """The pages' top-2 token: logits 2.0 (id 3) and 1.6 (id 5) give
+    importance sigma(0.4) and sigma(-0.4); z from the library logsumexp."""
+    g = _gold("worked_example_top2.json")
+    lg = np.array([g["logits"]], dtype=np.float32)
+    idx, _ = O.select_topk(lg, 2)
+    w = O.gate_weights(lg, idx, O.TOPK_THEN_SOFTMAX)
+    st = O.router_stats(lg, idx, w)
+    s = 1.0 / (1.0 + math.exp(-0.4))
+    np.testing.assert_allclose(st["importance"][3], s, rtol=1e-7)
+    np.testing.assert_allclose(st["importance"][5], 1 - s, rtol=1e-7)
+    lse = scipy.special.logsumexp(lg.astype(np.float64)[0])
+    np.testing.assert_allclose(st["z_loss"], lse ** 2, rtol=1e-13)
+    np.testing.assert_allclose(st["mean_prob"],
+                               scipy.special.softmax(lg.astype(np.float64)[0]), rtol=1e-13)
+
+
+@pytest.mark.parametrize("gating", [O.TOPK_THEN_SOFTMAX, O.SOFTMAX_THEN_TOPK])
+def test_router_stats_invariants_and_library(gating):
+    rng = np.random.default_rng(61)
+    T, E, k = 50, 9, 3
+    lg = (rng.standard_normal((T, E)) * 3).astype(np.float32)
+    idx, _ = O.select_topk(lg, k)
+    w = O.gate_weights(lg, idx, gating)
+    st = O.router_stats(lg, idx, w)
+    # every token's weights sum to one, probabilities sum to one, counts to T k
+    np.testing.assert_allclose(st["importance"].sum(), T, rtol=1e-12)
+    np.testing.assert_allclose(st["mean_prob"].sum(), 1.0, rtol=1e-12)
+    assert st["count"].sum() == T * k
+    np.testing.assert_array_equal(st["count"], np.bincount(idx.ravel(), minlength=E))
+    l64 = lg.astype(np.float64)
+    np.testing.assert_allclose(st["mean_prob"], scipy.special.softmax(l64, axis=1).mean(0),
+                               rtol=1e-12)
+    np.testing.assert_allclose(st["z_loss"], np.mean(scipy.special.logsumexp(l64, axis=1) ** 2),
+                               rtol=1e-12)
+    imp = np.zeros(E)
+    np.add.at(imp, idx.ravel(), w.ravel())
+    np.testing.assert_allclose(st["importance"], imp, rtol=1e-12)
+    f = np.bincount(idx.ravel(), minlength=E) / (T * k)
+    np.testing.assert_allclose(st["aux_loss"], E * np.dot(f, st["mean_prob"]), rtol=1e-12)
+
+
+def test_router_stats_all_to_one_expert():
+    """k = 1 and every token on expert 0: aux = E * mean_prob[0]."""
+    T, E = 11, 4
+    lg = np.zeros((T, E), dtype=np.float32)
+    lg[:, 0] = 5.0
+    idx, _ = O.select_topk(lg, 1)
+    w = O.gate_weights(lg, idx, O.TOPK_THEN_SOFTMAX)
+    st = O.router_stats(lg, idx, w)
+    p0 = math.exp(5.0) / (math.exp(5.0) + 3.0)
+    np.testing.assert_allclose(st["aux_loss"], E * p0, rtol=1e-12)
+    np.testing.assert_allclose(st["importance"], [T, 0, 0, 0])
+
+
 # ----------------------------------------------------------- shared expert --
 def _torch_swiglu(X, Wg, Wu, Wd):
     F = torch.nn.functional
