@@ -34,6 +34,9 @@ def _parse():
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--router-stats", action="store_true",
+                    help="also time moe_forward_stats (router statistics "
+                         "computed in the routing step) against moe_forward")
     ap.add_argument("--shared-dff", type=int, default=0,
                     help="add a shared expert of this hidden size (the "
                          "DeepSeek-V3 layer form; moe_forward_shared)")
@@ -258,6 +261,24 @@ def main():
                     "max_over_mean_load": float(counts.max() / max(counts.mean(), 1e-9))},
         "wall_s_timed": wall,
     }
+    if args.router_stats:
+        ws_st = torch.empty(M.forward_stats_workspace_bytes(p), dtype=torch.uint8,
+                            device="cuda")
+        rstats = torch.empty(2 * wl.E + 2, dtype=torch.float32, device="cuda")
+
+        def step_stats():
+            M.moe_forward_stats(p, *a, out=out, stats=stats, router_stats=rstats,
+                                workspace=ws_st)
+        for _ in range(2):
+            step_stats()
+        t_stats = _time_loop(step_stats, n, stream)
+        t_plain = _time_loop(lambda: M.moe_forward(p, *a, out=out, stats=stats,
+                                                   workspace=ws), n, stream)
+        rs = rstats.cpu().numpy()
+        line["router_stats"] = {"ms_per_step_with_stats": t_stats,
+                                "ms_per_step_without": t_plain,
+                                "aux_loss": float(rs[2 * wl.E]),
+                                "z_loss": float(rs[2 * wl.E + 1])}
     if shared is not None:
         S, ws_sh, step_serial = shared
         for _ in range(2):

@@ -195,6 +195,35 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* X,
                          const void* W_down, void* out, int32_t* stats,
                          void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Router statistics for monitoring (forward values only), computed by the
+ * router's selection kernel while it reads the logits and reduced in a fixed
+ * order ("Sparsely-Gated MoE 구현 관점에서 살펴보기", section "로드 밸런싱
+ * 손실과 용량은 별개": importance and load of the Sparsely-Gated MoE
+ * auxiliary loss, GShard's dispatch fraction and mean gate, ST-MoE's router
+ * z-loss).  router_stats [2E + 2] fp32 out:
+ *   [0, E)   importance[e] = sum over tokens of the gate weight given to e
+ *   [E, 2E)  mean_prob[e]  = mean over tokens of softmax(logits)[e] over all E
+ *   [2E]     aux_loss      = E * sum_e (count[e] / (T k)) * mean_prob[e],
+ *                            count[e] = tokens selecting e (before capacity)
+ *   [2E+1]   z_loss        = mean over tokens of logsumexp(logits)^2
+ * (logits are the fp32 router logits, bias included).  Routing outputs are
+ * identical to moe_route's / moe_forward's.
+ *   workspace >= moe_route_stats_workspace_bytes(p) (route), or
+ *   >= moe_forward_stats_workspace_bytes(p) (whole layer) bytes */
+size_t moe_route_stats_workspace_bytes(const moe_problem_t* p);
+moe_status_t moe_route_stats(const moe_problem_t* p, const void* X,
+                             const float* W_r, const float* bias,
+                             int32_t* topk_idx, float* topk_w,
+                             float* router_stats, void* workspace,
+                             size_t ws_bytes, hipStream_t stream);
+size_t moe_forward_stats_workspace_bytes(const moe_problem_t* p);
+moe_status_t moe_forward_stats(const moe_problem_t* p, const void* X,
+                               const float* W_r, const float* bias,
+                               const void* W_gate, const void* W_up,
+                               const void* W_down, void* out, int32_t* stats,
+                               float* router_stats, void* workspace,
+                               size_t ws_bytes, hipStream_t stream);
+
 /* The layer with a shared expert (the DeepSeek-V3 layer form; "5.3 Expert
  * Parallelism", section "최적화 1: 공유 전문가를 통한 연산-통신 오버랩": next
  * to the routed experts one shared expert processes every token, and its

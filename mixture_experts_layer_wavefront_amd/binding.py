@@ -29,8 +29,10 @@ SYMBOLS = ("moe_capacity", "moe_rows_bound", "moe_route_workspace_bytes",
            "moe_permute_workspace_bytes",
            "moe_grouped_ffn_workspace_bytes", "moe_workspace_bytes",
            "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
-           "moe_forward", "moe_forward_shared_workspace_bytes",
-           "moe_forward_shared", "moe_status_string")
+           "moe_forward", "moe_route_stats_workspace_bytes", "moe_route_stats",
+           "moe_forward_stats_workspace_bytes", "moe_forward_stats",
+           "moe_forward_shared_workspace_bytes", "moe_forward_shared",
+           "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -79,6 +81,11 @@ def load(path: str = LIB_PATH):
         "moe_combine": (ctypes.c_int, [P, vp, vp, vp, vp, st]),
         "moe_forward": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        sz, st]),
+        "moe_route_stats_workspace_bytes": (sz, [P]),
+        "moe_route_stats": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, sz, st]),
+        "moe_forward_stats_workspace_bytes": (sz, [P]),
+        "moe_forward_stats": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                             vp, sz, st]),
         "moe_forward_shared_workspace_bytes": (sz, [P, ctypes.c_int32]),
         "moe_forward_shared": (ctypes.c_int, [P, ctypes.c_int32, vp, vp, vp, vp,
                                               vp, vp, vp, vp, vp, vp, vp, vp,
@@ -321,3 +328,54 @@ def moe_forward_shared(p, shared_d_ff, X, W_r, bias, W_gate, W_up, W_down,
         _ptr(out, _out_dtype(p), "out"), _ptr(stats, torch.int32, "stats"),
         _ptr(ws), ws.numel(), _stream(stream), side), "moe_forward_shared")
     return out
+
+
+def route_stats_workspace_bytes(p: Problem) -> int:
+    return load().moe_route_stats_workspace_bytes(ctypes.byref(p))
+
+
+def forward_stats_workspace_bytes(p: Problem) -> int:
+    return load().moe_forward_stats_workspace_bytes(ctypes.byref(p))
+
+
+def moe_route_stats(p, X, W_r, bias=None, topk_idx=None, topk_w=None,
+                    router_stats=None, workspace=None, stream=None):
+    """moe_route plus the router statistics.  Returns (topk_idx, topk_w,
+    router_stats [2E+2]: importance | mean_prob | aux_loss | z_loss)."""
+    torch = _torch()
+    dev = X.device
+    if topk_idx is None:
+        topk_idx = torch.empty((p.T, p.top_k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((p.T, p.top_k), dtype=torch.float32, device=dev)
+    if router_stats is None:
+        router_stats = torch.empty(2 * p.E + 2, dtype=torch.float32, device=dev)
+    ws = _workspace(route_stats_workspace_bytes(p), dev, workspace)
+    _check(load().moe_route_stats(
+        ctypes.byref(p), _ptr(X, _act_dtype(p), "X"), _ptr(W_r, torch.float32, "W_r"),
+        _ptr(bias, torch.float32, "bias"), _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(topk_w, torch.float32, "topk_w"),
+        _ptr(router_stats, torch.float32, "router_stats"), _ptr(ws), ws.numel(),
+        _stream(stream)), "moe_route_stats")
+    return topk_idx, topk_w, router_stats
+
+
+def moe_forward_stats(p, X, W_r, bias, W_gate, W_up, W_down, out=None,
+                      stats=None, router_stats=None, workspace=None, stream=None):
+    """moe_forward plus the router statistics.  Returns (out, router_stats)."""
+    torch = _torch()
+    dev = X.device
+    if out is None:
+        out = torch.empty((p.T, p.d_model), dtype=_out_dtype(p), device=dev)
+    if router_stats is None:
+        router_stats = torch.empty(2 * p.E + 2, dtype=torch.float32, device=dev)
+    ws = _workspace(forward_stats_workspace_bytes(p), dev, workspace)
+    wt = _act_dtype(p)
+    _check(load().moe_forward_stats(
+        ctypes.byref(p), _ptr(X, wt, "X"), _ptr(W_r, torch.float32, "W_r"),
+        _ptr(bias, torch.float32, "bias"), _ptr(W_gate, wt, "W_gate"),
+        _ptr(W_up, wt, "W_up"), _ptr(W_down, wt, "W_down"),
+        _ptr(out, _out_dtype(p), "out"), _ptr(stats, torch.int32, "stats"),
+        _ptr(router_stats, torch.float32, "router_stats"), _ptr(ws), ws.numel(),
+        _stream(stream)), "moe_forward_stats")
+    return out, router_stats

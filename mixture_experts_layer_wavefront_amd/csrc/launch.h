@@ -8,13 +8,16 @@
 
 namespace moe {
 
-// Router: logits (bf16 X: split-bf16 MFMA with partial sums in `scratch`;
-// fp32 X: fused FMA kernel, no scratch), wavefront top-k, softmax.
-size_t route_scratch_bytes(int T, int E, int d, bool x_bf16);
+// Router: logits (bf16 X: split-bf16 MFMA, or K-split FMA for few tokens,
+// with partial sums in `scratch`; fp32 X: fused FMA kernel, no scratch),
+// wavefront top-k, softmax.  router_stats != nullptr also writes the router
+// statistics [2E + 2] (importance | mean probability | aux loss | z-loss);
+// the scratch size depends on whether statistics are wanted.
+size_t route_scratch_bytes(int T, int E, int d, bool x_bf16, bool stats);
 hipError_t launch_route(const void* X, bool x_bf16, const float* W_r,
                         const float* bias, int T, int d, int E, int k,
                         int gating, int32_t* topk_idx, float* topk_w,
-                        void* scratch, hipStream_t stream);
+                        void* scratch, float* router_stats, hipStream_t stream);
 
 // Permute, three kernels: per-block counts and in-block ranks; one-block
 // scan with capacity; destination rows and the row copy (one kernel for few

@@ -61,14 +61,15 @@ struct ForwardLayout {
       x_perm, ffn_scratch, y_perm, total;
 };
 
-ForwardLayout forward_layout(const moe_problem_t* p) {
+ForwardLayout forward_layout(const moe_problem_t* p, bool router_stats = false) {
   const size_t Tk = (size_t)p->T * p->top_k;
   const size_t R = (size_t)moe_rows_bound(p);
   ForwardLayout L{};
   size_t o = 0;
   L.topk_idx = o; o += a256(Tk * 4);
   L.topk_w = o; o += a256(Tk * 4);
-  L.route_scratch = o; o += a256(moe::route_scratch_bytes(p->T, p->E, p->d_model, is_bf16(p)));
+  L.route_scratch = o;
+  o += a256(moe::route_scratch_bytes(p->T, p->E, p->d_model, is_bf16(p), router_stats));
   L.perm_scratch = o; o += a256(moe::permute_scratch_bytes(p->T, p->top_k, p->E));
   L.stats = o; o += a256((size_t)(2 * p->E + 2) * 4);
   L.dest_row = o; o += a256(Tk * 4);
@@ -113,8 +114,9 @@ struct RoutedOut {
 
 hipError_t enqueue_routed(const moe_problem_t* p, const void* X, const float* W_r,
                           const float* bias, const void* W_gate, const void* W_up,
-                          const void* W_down, int32_t* stats, char* ws,
-                          const ForwardLayout& L, hipStream_t stream, RoutedOut* r) {
+                          const void* W_down, int32_t* stats, float* router_stats,
+                          char* ws, const ForwardLayout& L, hipStream_t stream,
+                          RoutedOut* r) {
   int32_t* topk_idx = reinterpret_cast<int32_t*>(ws + L.topk_idx);
   float* topk_w = reinterpret_cast<float*>(ws + L.topk_w);
   int32_t* st_buf = stats ? stats : reinterpret_cast<int32_t*>(ws + L.stats);
@@ -130,7 +132,7 @@ hipError_t enqueue_routed(const moe_problem_t* p, const void* X, const float* W_
 
   hipError_t e = moe::launch_route(X, bf, W_r, bias, p->T, p->d_model, p->E, p->top_k,
                                    (int)p->gating, topk_idx, topk_w, ws + L.route_scratch,
-                                   stream);
+                                   router_stats, stream);
   if (e != hipSuccess) return e;
   // the permute also writes the FFN's tile schedule (start of its scratch)
   const int bm = moe::ffn_tile_rows(bf, mean_rows_per_expert(p));
@@ -166,7 +168,7 @@ int64_t moe_rows_bound(const moe_problem_t* p) {
 
 size_t moe_route_workspace_bytes(const moe_problem_t* p) {
   if (validate(p) != MOE_OK) return 0;
-  return a256(moe::route_scratch_bytes(p->T, p->E, p->d_model, is_bf16(p)));
+  return a256(moe::route_scratch_bytes(p->T, p->E, p->d_model, is_bf16(p), false));
 }
 
 size_t moe_permute_workspace_bytes(const moe_problem_t* p) {
@@ -195,7 +197,27 @@ moe_status_t moe_route(const moe_problem_t* p, const void* X, const float* W_r,
   if (need > 0 && (!workspace || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_route(X, is_bf16(p), W_r, bias, p->T, p->d_model, p->E,
                                       p->top_k, (int)p->gating, topk_idx, topk_w, workspace,
-                                      stream));
+                                      nullptr, stream));
+}
+
+size_t moe_route_stats_workspace_bytes(const moe_problem_t* p) {
+  if (validate(p) != MOE_OK) return 0;
+  return a256(moe::route_scratch_bytes(p->T, p->E, p->d_model, is_bf16(p), true));
+}
+
+moe_status_t moe_route_stats(const moe_problem_t* p, const void* X, const float* W_r,
+                             const float* bias, int32_t* topk_idx, float* topk_w,
+                             float* router_stats, void* workspace, size_t ws_bytes,
+                             hipStream_t stream) {
+  moe_status_t st = validate(p);
+  if (st != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;
+  if (!X || !W_r || !topk_idx || !topk_w || !router_stats) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe_route_stats_workspace_bytes(p);
+  if (!workspace || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_route(X, is_bf16(p), W_r, bias, p->T, p->d_model, p->E,
+                                      p->top_k, (int)p->gating, topk_idx, topk_w, workspace,
+                                      router_stats, stream));
 }
 
 moe_status_t moe_permute(const moe_problem_t* p, const void* X,
@@ -255,7 +277,35 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* X, const float* W_r
   if (!workspace || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   RoutedOut r{};
-  hipError_t e = enqueue_routed(p, X, W_r, bias, W_gate, W_up, W_down, stats, ws, L, stream, &r);
+  hipError_t e = enqueue_routed(p, X, W_r, bias, W_gate, W_up, W_down, stats, nullptr, ws, L,
+                                stream, &r);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_combine(r.y_perm, r.dest_row, r.topk_w, p->T, p->d_model, p->top_k,
+                          nullptr, out_bf16(p), out, stream);
+  return hip_status(e);
+}
+
+size_t moe_forward_stats_workspace_bytes(const moe_problem_t* p) {
+  if (validate(p) != MOE_OK) return 0;
+  return forward_layout(p, true).total;
+}
+
+moe_status_t moe_forward_stats(const moe_problem_t* p, const void* X, const float* W_r,
+                               const float* bias, const void* W_gate, const void* W_up,
+                               const void* W_down, void* out, int32_t* stats,
+                               float* router_stats, void* workspace, size_t ws_bytes,
+                               hipStream_t stream) {
+  moe_status_t st = validate(p);
+  if (st != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;
+  if (!X || !W_r || !W_gate || !W_up || !W_down || !out || !router_stats)
+    return MOE_ERR_INVALID_ARG;
+  const ForwardLayout L = forward_layout(p, true);
+  if (!workspace || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  RoutedOut r{};
+  hipError_t e = enqueue_routed(p, X, W_r, bias, W_gate, W_up, W_down, stats, router_stats, ws,
+                                L, stream, &r);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_combine(r.y_perm, r.dest_row, r.topk_w, p->T, p->d_model, p->top_k,
                           nullptr, out_bf16(p), out, stream);
@@ -305,7 +355,7 @@ moe_status_t moe_forward_shared(const moe_problem_t* p, int32_t shared_d_ff,
   if (e == hipSuccess && side_stream != nullptr) e = hipEventRecord(join, side_stream);
   RoutedOut r{};
   if (e == hipSuccess)
-    e = enqueue_routed(p, X, W_r, bias, W_gate, W_up, W_down, stats, ws, L, stream, &r);
+    e = enqueue_routed(p, X, W_r, bias, W_gate, W_up, W_down, stats, nullptr, ws, L, stream, &r);
   // join before the combine adds the shared rows
   if (e == hipSuccess && side_stream != nullptr) e = hipStreamWaitEvent(stream, join, 0);
   if (e == hipSuccess)

@@ -58,7 +58,8 @@ struct XLoad<uint16_t> {
 template <int VPL>
 __device__ __forceinline__ void topk_softmax_store(float (&v)[VPL], int E, int k, int gating,
                                                    int lane, int32_t* __restrict__ idx_out,
-                                                   float* __restrict__ w_out) {
+                                                   float* __restrict__ w_out,
+                                                   int* sel_id = nullptr, float* sel_w = nullptr) {
   // softmax over all experts needs the untouched logits: its denominator first
   float M = v[0];
 #pragma unroll
@@ -104,6 +105,10 @@ __device__ __forceinline__ void topk_softmax_store(float (&v)[VPL], int E, int k
   if (lane < k) {
     idx_out[lane] = my_id;
     w_out[lane] = w;
+  }
+  if (sel_id != nullptr) {
+    *sel_id = my_id;
+    *sel_w = w;
   }
 }
 
@@ -428,17 +433,178 @@ constexpr int kSmallT = 64;
 #endif
 constexpr int kSmallKS = MOE_RKS;  // K per workgroup
 
+// Router statistics (monitoring).  Same selection as router_select_kernel,
+// one wavefront per token; each lane also forms, for the experts it holds,
+// the gate weight the token gives them (importance), whether the token
+// selected them, and their softmax probability over all E logits; lane 0
+// the squared log-sum-exp of the logits.  The four wavefronts' values are
+// added in order into one row per workgroup:
+//   stat_part[block][0:E) importance, [E:2E) probability sums,
+//   [2E:3E) selection counts, [3E] sum of squared log-sum-exp.
+// Rows are then added in fixed order: 64 at a time by router_stats_rows_kernel
+// (when there are more than 64), then by router_stats_reduce_kernel.
+constexpr int kStatBlockTok = 4;  // tokens per workgroup
+constexpr int kStatRows = 64;     // rows per partial sum
+
+template <int VPL>
+__global__ __launch_bounds__(256) void router_select_stats_kernel(
+    const float* __restrict__ partial, const float* __restrict__ bias, int T, int E,
+    int EP, int S, int k, int gating, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, float* __restrict__ stat_part) {
+  __shared__ float s_acc[4][3 * 256 + 1];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  float imp[VPL], cnt[VPL], prob[VPL], lse2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) imp[i] = cnt[i] = prob[i] = 0.f;
+  {
+    const int t = blockIdx.x * kStatBlockTok + wave;
+    if (t < T) {
+    float v[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + kWave * i;
+      if (e < E) {
+        float acc = 0.f;
+        for (int s0 = 0; s0 < S; s0 += 16) {
+          float pv[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            pv[u] = (s0 + u < S) ? partial[((int64_t)(s0 + u) * T + t) * EP + e] : 0.f;
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            if (s0 + u < S) acc += pv[u];
+        }
+        v[i] = acc + (bias != nullptr ? bias[e] : 0.f);
+      } else {
+        v[i] = -INFINITY;
+      }
+    }
+    // softmax over all experts and the log-sum-exp, from the untouched logits
+    float M = v[0];
+#pragma unroll
+    for (int i = 1; i < VPL; ++i) M = fmaxf(M, v[i]);
+    M = wave_max(M);
+    float ex[VPL], z = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      ex[i] = (lane + kWave * i < E) ? expf(v[i] - M) : 0.f;
+      z += ex[i];
+    }
+    const float Z = wave_sum(z);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) prob[i] += ex[i] / Z;
+    const float lse = M + logf(Z);
+    lse2 += lse * lse;
+    int my_id = 0;
+    float my_w = 0.f;
+    topk_softmax_store<VPL>(v, E, k, gating, lane, topk_idx + (int64_t)t * k,
+                            topk_w + (int64_t)t * k, &my_id, &my_w);
+    // slot j's (expert, weight) to the lane that holds that expert
+    for (int j = 0; j < k; ++j) {
+      const int e = __shfl(my_id, j, kWave);
+      const float wj = __shfl(my_w, j, kWave);
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (e == lane + kWave * i) {
+          imp[i] += wj;
+          cnt[i] += 1.f;
+        }
+    }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = lane + kWave * i;
+    if (e < E) {
+      s_acc[wave][e] = imp[i];
+      s_acc[wave][E + e] = prob[i];
+      s_acc[wave][2 * E + e] = cnt[i];
+    }
+  }
+  if (lane == 0) s_acc[wave][3 * E] = lse2;
+  __syncthreads();
+  for (int c = threadIdx.x; c <= 3 * E; c += 256)
+    stat_part[(int64_t)blockIdx.x * (3 * E + 1) + c] =
+        ((s_acc[0][c] + s_acc[1][c]) + s_acc[2][c]) + s_acc[3][c];
+}
+
+// Rows [64 x, 64 x + 64) of `in` added in order, column by column
+// (blockIdx.y picks 256 columns).
+__global__ __launch_bounds__(256) void router_stats_rows_kernel(
+    const float* __restrict__ in, int nrows, int C, float* __restrict__ out) {
+  const int c = blockIdx.y * 256 + threadIdx.x;
+  if (c >= C) return;
+  const int r0 = blockIdx.x * kStatRows, r1 = min(nrows, r0 + kStatRows);
+  float acc = 0.f;
+  for (int b0 = r0; b0 < r1; b0 += 16) {
+    float pv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      pv[u] = (b0 + u < r1) ? in[(int64_t)(b0 + u) * C + c] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (b0 + u < r1) acc += pv[u];
+  }
+  out[(int64_t)blockIdx.x * C + c] = acc;
+}
+
+// One workgroup: add the remaining rows in order (column c by thread c),
+// then importance | mean probability | aux loss | z-loss.
+__global__ __launch_bounds__(1024) void router_stats_reduce_kernel(
+    const float* __restrict__ stat_part, int nblk, int T, int E, int k,
+    float* __restrict__ router_stats) {
+  __shared__ float s_col[3 * 256 + 1];
+  const int C = 3 * E + 1;
+  for (int c = threadIdx.x; c < C; c += 1024) {
+    float acc = 0.f;
+    for (int b0 = 0; b0 < nblk; b0 += 16) {
+      float pv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        pv[u] = (b0 + u < nblk) ? stat_part[(int64_t)(b0 + u) * C + c] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (b0 + u < nblk) acc += pv[u];
+    }
+    s_col[c] = acc;
+  }
+  __syncthreads();
+  const float inv_t = 1.f / (float)T;
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    router_stats[e] = s_col[e];
+    router_stats[E + e] = s_col[E + e] * inv_t;
+  }
+  if (threadIdx.x == 0) {
+    float aux = 0.f;
+    const float inv_tk = 1.f / ((float)T * (float)k);
+    for (int e = 0; e < E; ++e) aux += (s_col[2 * E + e] * inv_tk) * (s_col[E + e] * inv_t);
+    router_stats[2 * E] = (float)E * aux;
+    router_stats[2 * E + 1] = s_col[3 * E] * inv_t;
+  }
+}
+
 struct RoutePlan {
   int NTE, EP, d32, S, tiles;
-  bool small;
-  size_t split_bytes, partial_bytes;
+  bool fused;   // fp32 X without statistics: one fused kernel, no scratch
+  bool small;   // K-split FMA partial logits (few bf16 tokens, or fp32 X
+                // with statistics)
+  size_t split_bytes, partial_bytes, stat_bytes;
 };
 
 size_t a256r(size_t x) { return (x + 255) & ~size_t(255); }
 
-RoutePlan route_plan(int T, int E, int d) {
+RoutePlan route_plan(int T, int E, int d, bool x_bf16, bool stats) {
   RoutePlan P{};
-  if (T <= kSmallT) {
+  if (stats) {
+    const size_t nblk = (size_t)(T + kStatBlockTok - 1) / kStatBlockTok;
+    const size_t ngrp = (nblk + kStatRows - 1) / kStatRows;
+    P.stat_bytes = a256r(nblk * (3 * E + 1) * 4) + a256r(ngrp * (3 * E + 1) * 4);
+  }
+  if (!x_bf16 && !stats) {
+    P.fused = true;
+    return P;
+  }
+  if (T <= kSmallT || !x_bf16) {
     P.small = true;
     P.EP = E <= 8 ? 8 : E <= 16 ? 16 : E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256;
     P.S = (d + kSmallKS - 1) / kSmallKS;
@@ -477,85 +643,116 @@ hipError_t launch_cfg(const void* X, bool x_bf16, const float* W_r,
   return hipGetLastError();
 }
 
-// bf16 X, few tokens: K-split partial logits (EP = TX * RE columns)
-template <int TX, int RE, int RT>
-hipError_t launch_partial(const uint16_t* X, const float* W_r, int T, int d, int E,
+// K-split partial logits with fp32 FMAs (EP = TX * RE columns)
+template <int TX, int RE, int RT, typename XT>
+hipError_t launch_partial(const XT* X, const float* W_r, int T, int d, int E,
                           int S, float* partial, hipStream_t stream) {
   constexpr int TT = (kRouterThreads / TX) * RT;
   const dim3 grid((T + TT - 1) / TT, S);
-  router_topk_kernel<TX, RE, RT, uint16_t, true><<<grid, kRouterThreads, 0, stream>>>(
+  router_topk_kernel<TX, RE, RT, XT, true><<<grid, kRouterThreads, 0, stream>>>(
       X, W_r, nullptr, T, d, E, 0, 0, nullptr, nullptr, kSmallKS, partial);
+  return hipGetLastError();
+}
+
+template <typename XT>
+hipError_t launch_partial_ep(const XT* X, const float* W_r, int T, int d, int E, int EP,
+                             int S, float* partial, hipStream_t stream) {
+  switch (EP) {
+    case 8: return launch_partial<8, 1, 2>(X, W_r, T, d, E, S, partial, stream);
+    case 16: return launch_partial<16, 1, 2>(X, W_r, T, d, E, S, partial, stream);
+    case 32: return launch_partial<32, 1, 2>(X, W_r, T, d, E, S, partial, stream);
+    case 64: return launch_partial<64, 1, 4>(X, W_r, T, d, E, S, partial, stream);
+    case 128: return launch_partial<64, 2, 4>(X, W_r, T, d, E, S, partial, stream);
+    default: return launch_partial<64, 4, 4>(X, W_r, T, d, E, S, partial, stream);
+  }
+}
+
+// Sum of the S partials, bias, top-k and gate weights (and the statistics).
+hipError_t launch_select(const float* partial, const float* bias, int T, int E, int EP,
+                         int S, int k, int gating, int32_t* topk_idx, float* topk_w,
+                         float* stat_part, float* router_stats, hipStream_t stream) {
+  if (router_stats == nullptr) {
+    const unsigned gs = (unsigned)((T + 3) / 4);
+    if (E <= 64)
+      router_select_kernel<1><<<gs, 256, 0, stream>>>(partial, bias, T, E, EP, S, k, gating, topk_idx, topk_w);
+    else if (E <= 128)
+      router_select_kernel<2><<<gs, 256, 0, stream>>>(partial, bias, T, E, EP, S, k, gating, topk_idx, topk_w);
+    else
+      router_select_kernel<4><<<gs, 256, 0, stream>>>(partial, bias, T, E, EP, S, k, gating, topk_idx, topk_w);
+    return hipGetLastError();
+  }
+  const int nblk = (T + kStatBlockTok - 1) / kStatBlockTok;
+  if (E <= 64)
+    router_select_stats_kernel<1><<<nblk, 256, 0, stream>>>(partial, bias, T, E, EP, S, k, gating, topk_idx, topk_w, stat_part);
+  else if (E <= 128)
+    router_select_stats_kernel<2><<<nblk, 256, 0, stream>>>(partial, bias, T, E, EP, S, k, gating, topk_idx, topk_w, stat_part);
+  else
+    router_select_stats_kernel<4><<<nblk, 256, 0, stream>>>(partial, bias, T, E, EP, S, k, gating, topk_idx, topk_w, stat_part);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int C = 3 * E + 1;
+  const float* rows = stat_part;
+  int nrows = nblk;
+  if (nblk > kStatRows) {
+    float* grp = stat_part + a256r((size_t)nblk * C * 4) / 4;
+    const int ngrp = (nblk + kStatRows - 1) / kStatRows;
+    router_stats_rows_kernel<<<dim3(ngrp, (C + 255) / 256), 256, 0, stream>>>(stat_part, nblk, C, grp);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    rows = grp;
+    nrows = ngrp;
+  }
+  router_stats_reduce_kernel<<<1, 1024, 0, stream>>>(rows, nrows, T, E, k, router_stats);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t route_scratch_bytes(int T, int E, int d, bool x_bf16) {
-  if (!x_bf16 || T == 0) return 0;
-  const RoutePlan P = route_plan(T, E, d);
-  return P.split_bytes + P.partial_bytes;
+size_t route_scratch_bytes(int T, int E, int d, bool x_bf16, bool stats) {
+  if (T == 0) return 0;
+  const RoutePlan P = route_plan(T, E, d, x_bf16, stats);
+  return P.split_bytes + P.partial_bytes + P.stat_bytes;
 }
 
 hipError_t launch_route(const void* X, bool x_bf16, const float* W_r,
                         const float* bias, int T, int d, int E, int k,
                         int gating, int32_t* topk_idx, float* topk_w,
-                        void* scratch, hipStream_t stream) {
+                        void* scratch, float* router_stats, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  if (x_bf16 && T <= kSmallT) {
-    const RoutePlan P = route_plan(T, E, d);
-    float* partial = static_cast<float*>(scratch);
-    const uint16_t* Xb = static_cast<const uint16_t*>(X);
-    hipError_t err;
-    switch (P.EP) {
-      case 8: err = launch_partial<8, 1, 2>(Xb, W_r, T, d, E, P.S, partial, stream); break;
-      case 16: err = launch_partial<16, 1, 2>(Xb, W_r, T, d, E, P.S, partial, stream); break;
-      case 32: err = launch_partial<32, 1, 2>(Xb, W_r, T, d, E, P.S, partial, stream); break;
-      case 64: err = launch_partial<64, 1, 4>(Xb, W_r, T, d, E, P.S, partial, stream); break;
-      case 128: err = launch_partial<64, 2, 4>(Xb, W_r, T, d, E, P.S, partial, stream); break;
-      default: err = launch_partial<64, 4, 4>(Xb, W_r, T, d, E, P.S, partial, stream); break;
-    }
-    if (err != hipSuccess) return err;
-    const unsigned gs = (unsigned)((T + 3) / 4);
-    if (E <= 64)
-      router_select_kernel<1><<<gs, 256, 0, stream>>>(partial, bias, T, E, P.EP, P.S, k, gating, topk_idx, topk_w);
-    else if (E <= 128)
-      router_select_kernel<2><<<gs, 256, 0, stream>>>(partial, bias, T, E, P.EP, P.S, k, gating, topk_idx, topk_w);
-    else
-      router_select_kernel<4><<<gs, 256, 0, stream>>>(partial, bias, T, E, P.EP, P.S, k, gating, topk_idx, topk_w);
-    return hipGetLastError();
+  const RoutePlan P = route_plan(T, E, d, x_bf16, router_stats != nullptr);
+  if (P.fused) {
+    if (E <= 8) return launch_cfg<8, 1, 1>(X, x_bf16, W_r, bias, T, d, E, k, gating, topk_idx, topk_w, stream);
+    if (E <= 16) return launch_cfg<16, 1, 1>(X, x_bf16, W_r, bias, T, d, E, k, gating, topk_idx, topk_w, stream);
+    if (E <= 32) return launch_cfg<32, 1, 2>(X, x_bf16, W_r, bias, T, d, E, k, gating, topk_idx, topk_w, stream);
+    if (E <= 64) return launch_cfg<64, 1, 4>(X, x_bf16, W_r, bias, T, d, E, k, gating, topk_idx, topk_w, stream);
+    if (E <= 128) return launch_cfg<64, 2, 4>(X, x_bf16, W_r, bias, T, d, E, k, gating, topk_idx, topk_w, stream);
+    return launch_cfg<64, 4, 4>(X, x_bf16, W_r, bias, T, d, E, k, gating, topk_idx, topk_w, stream);
   }
-  if (x_bf16) {
-    const RoutePlan P = route_plan(T, E, d);
-    uint16_t* Wsplit = static_cast<uint16_t*>(scratch);
-    float* partial = reinterpret_cast<float*>(static_cast<char*>(scratch) + P.split_bytes);
-    const int64_t nthr = (int64_t)P.EP * (P.d32 / 8);
-    router_split_kernel<<<(unsigned)((nthr + 255) / 256), 256, 0, stream>>>(W_r, E, d, P.EP, P.d32, Wsplit);
-    hipError_t err = hipGetLastError();
+  char* sp = static_cast<char*>(scratch);
+  uint16_t* Wsplit = reinterpret_cast<uint16_t*>(sp);
+  float* partial = reinterpret_cast<float*>(sp + P.split_bytes);
+  float* stat_part = reinterpret_cast<float*>(sp + P.split_bytes + P.partial_bytes);
+  hipError_t err;
+  if (P.small) {
+    err = x_bf16 ? launch_partial_ep(static_cast<const uint16_t*>(X), W_r, T, d, E, P.EP, P.S, partial, stream)
+                 : launch_partial_ep(static_cast<const float*>(X), W_r, T, d, E, P.EP, P.S, partial, stream);
     if (err != hipSuccess) return err;
-    const dim3 g(P.tiles, P.S);
-    switch (P.NTE) {
-      case 1: router_logits_kernel<1><<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(X), T, d, Wsplit, P.d32, P.S, partial); break;
-      case 2: router_logits_kernel<2><<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(X), T, d, Wsplit, P.d32, P.S, partial); break;
-      case 4: router_logits_kernel<4><<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(X), T, d, Wsplit, P.d32, P.S, partial); break;
-      case 8: router_logits_kernel<8><<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(X), T, d, Wsplit, P.d32, P.S, partial); break;
-      default: router_logits_kernel<16><<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(X), T, d, Wsplit, P.d32, P.S, partial); break;
-    }
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    const unsigned gs = (unsigned)((T + 3) / 4);
-    if (E <= 64)
-      router_select_kernel<1><<<gs, 256, 0, stream>>>(partial, bias, T, E, P.EP, P.S, k, gating, topk_idx, topk_w);
-    else if (E <= 128)
-      router_select_kernel<2><<<gs, 256, 0, stream>>>(partial, bias, T, E, P.EP, P.S, k, gating, topk_idx, topk_w);
-    else
-      router_select_kernel<4><<<gs, 256, 0, stream>>>(partial, bias, T, E, P.EP, P.S, k, gating, topk_idx, topk_w);
-    return hipGetLastError();
+    return launch_select(partial, bias, T, E, P.EP, P.S, k, gating, topk_idx, topk_w,
+                         stat_part, router_stats, stream);
   }
-  if (E <= 8) return launch_cfg<8, 1, 1>(X, x_bf16, W_r, bias, T, d, E, k, gating, topk_idx, topk_w, stream);
-  if (E <= 16) return launch_cfg<16, 1, 1>(X, x_bf16, W_r, bias, T, d, E, k, gating, topk_idx, topk_w, stream);
-  if (E <= 32) return launch_cfg<32, 1, 2>(X, x_bf16, W_r, bias, T, d, E, k, gating, topk_idx, topk_w, stream);
-  if (E <= 64) return launch_cfg<64, 1, 4>(X, x_bf16, W_r, bias, T, d, E, k, gating, topk_idx, topk_w, stream);
-  if (E <= 128) return launch_cfg<64, 2, 4>(X, x_bf16, W_r, bias, T, d, E, k, gating, topk_idx, topk_w, stream);
-  return launch_cfg<64, 4, 4>(X, x_bf16, W_r, bias, T, d, E, k, gating, topk_idx, topk_w, stream);
+  const int64_t nthr = (int64_t)P.EP * (P.d32 / 8);
+  router_split_kernel<<<(unsigned)((nthr + 255) / 256), 256, 0, stream>>>(W_r, E, d, P.EP, P.d32, Wsplit);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const dim3 g(P.tiles, P.S);
+  switch (P.NTE) {
+    case 1: router_logits_kernel<1><<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(X), T, d, Wsplit, P.d32, P.S, partial); break;
+    case 2: router_logits_kernel<2><<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(X), T, d, Wsplit, P.d32, P.S, partial); break;
+    case 4: router_logits_kernel<4><<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(X), T, d, Wsplit, P.d32, P.S, partial); break;
+    case 8: router_logits_kernel<8><<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(X), T, d, Wsplit, P.d32, P.S, partial); break;
+    default: router_logits_kernel<16><<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(X), T, d, Wsplit, P.d32, P.S, partial); break;
+  }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  return launch_select(partial, bias, T, E, P.EP, P.S, k, gating, topk_idx, topk_w,
+                       stat_part, router_stats, stream);
 }
 
 }  // namespace moe
