@@ -150,6 +150,72 @@ def make_expert(w: Workload, e: int):
     return Wg, Wu, Wd
 
 
+def _fp8_codes(W):
+    """Per-tensor power-of-two scale s (largest |W| / s <= 448) and the
+    nearest FP8 E4M3 codes of W / s (torch's conversion: round to nearest
+    even).  W: torch fp32 tensor.  Returns (uint8 codes, float scale)."""
+    import torch
+
+    amax = float(W.abs().max())
+    s = 2.0 ** np.ceil(np.log2(amax / 448.0)) if amax > 0 else 1.0
+    q = (W / s).to(torch.float8_e4m3fn).view(torch.uint8)
+    return q, float(s)
+
+
+def make_host_fp8(w: Workload):
+    """The layer's inputs with FP8 expert weights: X, W_r and bias as in
+    make_host; per expert and projection the fp32 normal draw of make_expert
+    (before any bf16 rounding) is stored as FP8 E4M3 codes with a
+    power-of-two scale.  Returns dict X, W_r, bias, Q_gate, Q_up, Q_down
+    (uint8 [E, out, in]) and scales (fp32 [E, 3]: gate, up, down)."""
+    import torch
+
+    X = make_x(w)
+    W_r, bias = make_router(w)
+    Qs = [np.empty((w.E, w.d_ff, w.d_model), np.uint8),
+          np.empty((w.E, w.d_ff, w.d_model), np.uint8),
+          np.empty((w.E, w.d_model, w.d_ff), np.uint8)]
+    scales = np.empty((w.E, 3), np.float32)
+    for e in range(w.E):
+        for j, (tid, shape, fan) in enumerate(((_WG, (w.d_ff, w.d_model), w.d_model),
+                                               (_WU, (w.d_ff, w.d_model), w.d_model),
+                                               (_WD, (w.d_model, w.d_ff), w.d_ff))):
+            W = _normal(_rng(w.seed, tid, e), shape, _std(w, fan), False)
+            q, sc = _fp8_codes(torch.from_numpy(W))
+            Qs[j][e] = q.numpy()
+            scales[e, j] = sc
+    return dict(X=X, W_r=W_r, bias=bias, Q_gate=Qs[0], Q_up=Qs[1], Q_down=Qs[2],
+                scales=scales)
+
+
+def make_device_fp8(w: Workload, device="cuda"):
+    """make_device's inputs with FP8 expert weights (uint8 codes [E, out, in]
+    and fp32 scales [E, 3]), drawn and quantised on the device with the same
+    per-(tensor, expert) generators as make_device."""
+    import torch
+
+    X = torch.from_numpy(make_x(w)).to(device=device).to(torch.bfloat16)
+    W_r, bias = make_router(w)
+    W_r = torch.from_numpy(W_r).to(device)
+    bias = None if bias is None else torch.from_numpy(bias).to(device)
+    Qg = torch.empty((w.E, w.d_ff, w.d_model), dtype=torch.uint8, device=device)
+    Qu = torch.empty_like(Qg)
+    Qd = torch.empty((w.E, w.d_model, w.d_ff), dtype=torch.uint8, device=device)
+    scales = torch.empty((w.E, 3), dtype=torch.float32)
+    g = torch.Generator(device=device)
+    for e in range(w.E):
+        for j, (tid, dst, fan) in enumerate(((_WG, Qg, w.d_model), (_WU, Qu, w.d_model),
+                                             (_WD, Qd, w.d_ff))):
+            g.manual_seed((w.seed * 1_000_003 + tid * 65_537 + e) & (2**63 - 1))
+            tmp = torch.randn(dst.shape[1:], generator=g, device=device,
+                              dtype=torch.float32).mul_(_std(w, fan))
+            q, sc = _fp8_codes(tmp)
+            dst[e].copy_(q)
+            scales[e, j] = sc
+    return dict(X=X, W_r=W_r, bias=bias, Q_gate=Qg, Q_up=Qu, Q_down=Qd,
+                scales=scales.to(device))
+
+
 def make_shared(w: Workload, shared_d_ff: int):
     """Host weights of a shared expert with hidden size shared_d_ff:
     (Ws_gate [sdff, d], Ws_up [sdff, d], Ws_down [d, sdff]), drawn like the

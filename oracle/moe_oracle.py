@@ -303,6 +303,49 @@ def moe_forward(X, W_r, bias, W_gate, W_up, W_down, k, capacity_factor=None,
 
 
 # ---------------------------------------------------------------------------
+# Expert weights stored as FP8 with a scale per expert and projection
+#     [HF] sections "Weight Loading에서 텐서 구조 맞추기" and "적재 변환과
+#     양자화 조합하기": once the experts sit in one packed tensor, a
+#     per-expert quantisation step fits into weight loading.  Reading (the
+#     page names no format): each expert's W_gate, W_up, W_down is stored as
+#     FP8 E4M3 codes (the OCP "FN" variant: bias 7, no infinities, one NaN
+#     pattern per sign, largest finite 448) times one fp32 scale per
+#     (expert, projection); the layer is the same SwiGLU layer on the decoded
+#     weights  W = scale * decode(code).  Activations stay as they are.
+# ---------------------------------------------------------------------------
+def fp8_e4m3_decode(codes):
+    """Values (fp64) of FP8 E4M3 codes: bit 7 sign, bits 6..3 exponent (bias
+    7), bits 2..0 mantissa; exponent 0 is subnormal (m/8 * 2^-6); exponent 15
+    with mantissa 7 is NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6,
+                   (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return sign * val
+
+
+def dequant_expert_weights(Q, scales):
+    """Decoded weights ``scales[e] * decode(Q[e])`` (fp64) for codes Q
+    [E, out, in] and one scale per expert [E]."""
+    dec = fp8_e4m3_decode(Q)
+    return dec * _f64(scales).reshape(-1, *([1] * (dec.ndim - 1)))
+
+
+def moe_forward_fp8(X, W_r, bias, Qg, Qu, Qd, scales, k, capacity_factor=None,
+                    gating=TOPK_THEN_SOFTMAX):
+    """The layer with FP8 expert weights: ``moe_forward`` on the decoded
+    weights; scales [E, 3] hold the (gate, up, down) scale of each expert."""
+    sc = _f64(scales)
+    return moe_forward(X, W_r, bias, dequant_expert_weights(Qg, sc[:, 0]),
+                       dequant_expert_weights(Qu, sc[:, 1]),
+                       dequant_expert_weights(Qd, sc[:, 2]), k, capacity_factor,
+                       gating)
+
+
+# ---------------------------------------------------------------------------
 # Router statistics (monitoring; forward values only, no gradients)
 #     [SG] "로드 밸런싱 손실과 용량은 별개": the Sparsely-Gated MoE auxiliary
 #     loss balances expert importance and load; GShard's auxiliary loss uses

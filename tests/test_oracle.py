@@ -365,6 +365,56 @@ def test_forward_tokens_matches_full_forward():
 
 
 # ------------------------------------------------------ input generators --
+# ------------------------------------------------------------ fp8 weights --
+def test_fp8_decode_closed_forms():
+    d = O.fp8_e4m3_decode
+    cases = {0x00: 0.0, 0x38: 1.0, 0x3C: 1.5, 0x40: 2.0, 0xC0: -2.0, 0x7E: 448.0,
+             0xFE: -448.0, 0x01: 2.0 ** -9, 0x07: 7 / 8 * 2.0 ** -6,
+             0x08: 2.0 ** -6, 0x30: 0.5, 0x37: 0.9375}
+    for code, v in cases.items():
+        assert d(np.uint8(code)) == v, hex(code)
+    assert np.isnan(d(np.uint8(0x7F))) and np.isnan(d(np.uint8(0xFF)))
+    assert np.signbit(d(np.uint8(0x80))) and d(np.uint8(0x80)) == 0.0
+
+
+def test_fp8_decode_matches_library_on_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = O.fp8_e4m3_decode(codes)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+    # positive codes increase strictly up to the largest finite value
+    pos = got[:0x7F]
+    assert np.all(np.diff(pos) > 0)
+
+
+def test_fp8_layer_is_the_layer_on_decoded_weights():
+    """Weights that are exactly scale * decode(code) give the same layer
+    whether passed decoded or as codes and scales."""
+    rng = np.random.default_rng(81)
+    T, d, E, k, dff = 20, 16, 4, 2, 12
+    X, W_r, b, _, _, _ = _rand_layer(T, d, E, k, dff, seed=82)
+    Qg = rng.integers(0, 256, (E, dff, d), dtype=np.uint8)
+    Qu = rng.integers(0, 256, (E, dff, d), dtype=np.uint8)
+    Qd = rng.integers(0, 256, (E, d, dff), dtype=np.uint8)
+    for Q in (Qg, Qu, Qd):  # no NaN codes
+        Q[(Q & 0x7F) == 0x7F] = 0x30
+    sc = np.exp2(rng.integers(-8, -3, (E, 3))).astype(np.float32)
+    res = O.moe_forward_fp8(X, W_r, b, Qg, Qu, Qd, sc, k)
+    lib = lambda Q, s: (torch.from_numpy(Q).view(torch.float8_e4m3fn).double().numpy()
+                        * s.reshape(-1, 1, 1))
+    ref = O.moe_forward(X, W_r, b, lib(Qg, sc[:, 0]), lib(Qu, sc[:, 1]),
+                        lib(Qd, sc[:, 2]), k)
+    np.testing.assert_array_equal(res["out"], ref["out"])
+    # a power-of-two scale is exact: halving the codes' values and doubling the
+    # scale changes nothing (codes 0x38 = 1.0 and 0x30 = 0.5)
+    one = np.full((E, dff, d), 0x38, np.uint8)
+    half = np.full((E, dff, d), 0x30, np.uint8)
+    np.testing.assert_array_equal(O.dequant_expert_weights(one, sc[:, 0]),
+                                  O.dequant_expert_weights(half, 2 * sc[:, 0]))
+
+
 # ------------------------------------------------------- router statistics --
 def test_router_stats_uniform_router_closed_forms():
     """Equal logits: every mean probability is 1/E, the z-loss is (ln E)^2
