@@ -34,6 +34,9 @@ def _parse():
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--fp8", action="store_true",
+                    help="FP8 E4M3 expert weights with per-expert scales "
+                         "(moe_forward_scaled) instead of bf16 weights")
     ap.add_argument("--router-stats", action="store_true",
                     help="also time moe_forward_stats (router statistics "
                          "computed in the routing step) against moe_forward")
@@ -97,15 +100,17 @@ def _time_loop(fn, steps, stream):
     return s.elapsed_time(e) / steps  # ms per call
 
 
-def _cpu_baseline(wl, dev, ntok, min_s=10.0, max_s=30.0, shared=None):
+def _cpu_baseline(wl, dev, ntok, min_s=10.0, max_s=30.0, shared=None, fp8_scales=None):
     """The CPU oracle (as it stands) on the first `ntok` tokens of the same
     batch with the same weights, repeated until at least `min_s` seconds of
     CPU work (stopping before `max_s`); returns the dict for the JSON line."""
+    import torch
     from threadpoolctl import threadpool_info
 
     import oracle as O
 
-    host = {k: (None if v is None else v.float().cpu().numpy())
+    host = {k: (None if v is None else
+                (v.cpu().numpy() if v.dtype == torch.uint8 else v.float().cpu().numpy()))
             for k, v in dev.items()}
     ntok = min(ntok, wl.T)
     X = host["X"][:ntok]
@@ -113,7 +118,11 @@ def _cpu_baseline(wl, dev, ntok, min_s=10.0, max_s=30.0, shared=None):
     runs, total = 0, 0.0
     while total < min_s:
         t0 = time.perf_counter()
-        if shared is None:
+        if fp8_scales is not None:
+            O.moe_forward_fp8(X, host["W_r"], host["bias"], host["W_gate"], host["W_up"],
+                              host["W_down"], fp8_scales, wl.top_k,
+                              cf if cf > 0 else None, wl.gating)
+        elif shared is None:
             O.moe_forward(X, host["W_r"], host["bias"], host["W_gate"], host["W_up"],
                           host["W_down"], wl.top_k, cf if cf > 0 else None, wl.gating)
         else:
@@ -152,9 +161,18 @@ def main():
 
     wl = W.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
-    dev = W.make_device(wl, "cuda")
+    if args.fp8:
+        if args.shared_dff or args.router_stats:
+            sys.exit("--fp8 combines with neither --shared-dff nor --router-stats")
+        d8 = W.make_device_fp8(wl, "cuda")
+        dev = dict(X=d8["X"], W_r=d8["W_r"], bias=d8["bias"], W_gate=d8["Q_gate"],
+                   W_up=d8["Q_up"], W_down=d8["Q_down"])
+        w_scales = d8["scales"]
+    else:
+        dev = W.make_device(wl, "cuda")
     p = M.problem(wl.T, wl.d_model, wl.E, wl.top_k, wl.d_ff,
-                  wl.capacity_factor, wl.dtype, wl.gating, "f32")
+                  wl.capacity_factor, wl.dtype, wl.gating, "f32",
+                  w_dtype="fp8" if args.fp8 else None)
     ws = torch.empty(M.workspace_bytes(p), dtype=torch.uint8, device="cuda")
     out = torch.empty((wl.T, wl.d_model), dtype=torch.float32, device="cuda")
     stats = torch.empty(2 * wl.E + 2, dtype=torch.int32, device="cuda")
@@ -163,7 +181,10 @@ def main():
          dev["W_down"])
 
     def step():
-        M.moe_forward(p, *a, out=out, stats=stats, workspace=ws)
+        if args.fp8:
+            M.moe_forward_scaled(p, *a, w_scales, out=out, stats=stats, workspace=ws)
+        else:
+            M.moe_forward(p, *a, out=out, stats=stats, workspace=ws)
 
     shared = None
     if args.shared_dff > 0:
@@ -195,8 +216,15 @@ def main():
     # ---- per stage (same kernels, called through the stage entry points) ----
     idx, w = M.moe_route(p, dev["X"], dev["W_r"], dev["bias"])
     perm = M.moe_permute(p, dev["X"], idx)
-    Y = M.moe_grouped_ffn(p, perm["X_perm"], perm["offsets"], dev["W_gate"],
-                          dev["W_up"], dev["W_down"])
+    if args.fp8:
+        ffn = lambda Yo=None, w=None: M.moe_grouped_ffn_scaled(  # noqa: E731
+            p, perm["X_perm"], perm["offsets"], dev["W_gate"], dev["W_up"],
+            dev["W_down"], w_scales, Yo, w)
+    else:
+        ffn = lambda Yo=None, w=None: M.moe_grouped_ffn(  # noqa: E731
+            p, perm["X_perm"], perm["offsets"], dev["W_gate"], dev["W_up"],
+            dev["W_down"], Yo, w)
+    Y = ffn()
     o2 = M.moe_combine(p, Y, perm["dest_row"], w)
     ffn_ws = torch.empty(M.grouped_ffn_workspace_bytes(p), dtype=torch.uint8,
                          device="cuda")
@@ -207,21 +235,20 @@ def main():
                                              idx, w), n, stream)
     t_perm = _time_loop(lambda: M.moe_permute(p, dev["X"], idx, perm_ws, out=perm),
                         n, stream)
-    t_ffn = _time_loop(lambda: M.moe_grouped_ffn(p, perm["X_perm"], perm["offsets"],
-                                                 dev["W_gate"], dev["W_up"],
-                                                 dev["W_down"], Y, ffn_ws), n, stream)
+    t_ffn = _time_loop(lambda: ffn(Y, ffn_ws), n, stream)
     t_comb = _time_loop(lambda: M.moe_combine(p, Y, perm["dest_row"], w, o2),
                         n, stream)
     torch.cuda.synchronize()
 
     a_b = 2 if wl.dtype == W.BF16 else 4
+    w_b = 1 if args.fp8 else a_b
     T, d, E, k, dff = wl.T, wl.d_model, wl.E, wl.top_k, wl.d_ff
     ffn_flops = 6.0 * N * d * dff
     ffn_tflops = ffn_flops / (t_ffn * 1e-3) / 1e12
     bytes_route = T * d * a_b + E * d * 4 + T * k * 8
     bytes_perm = T * d * a_b + N * d * a_b + T * k * 24 + N * 4
     bytes_comb = N * d * 4 + T * d * 4 + T * k * 8
-    bytes_ffn = 3 * active * d * dff * a_b + N * d * a_b + N * d * 4
+    bytes_ffn = 3 * active * d * dff * w_b + N * d * a_b + N * d * 4
 
     line = {
         "metric": "MoE-layer tokens/s + grouped-GEMM TFLOP/s (% bf16 MFMA peak), "
@@ -235,7 +262,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == W.BF16 else "f32",
+        "dtype": ("bf16 (fp8 e4m3 expert weights)" if args.fp8 else "bf16")
+                 if wl.dtype == W.BF16 else "f32",
         "data": "synthetic (seeded; random weights of the layer's shape)",
         "config": {"workload": f"{wl.name}: one MoE FFN layer forward, T={T}, "
                                f"d_model={d}, E={E}, top-{k}, SwiGLU d_ff={dff}, "
@@ -295,7 +323,8 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = _cpu_baseline(
             wl, dev, args.cpu_sample_tokens,
-            shared=None if shared is None else [t.float().cpu().numpy() for t in shared[0]])
+            shared=None if shared is None else [t.float().cpu().numpy() for t in shared[0]],
+            fp8_scales=w_scales.cpu().numpy() if args.fp8 else None)
     print(json.dumps(line), flush=True)
 
 

@@ -63,7 +63,12 @@ typedef enum {
   MOE_ERR_HIP = -4          /* a kernel launch failed */
 } moe_status_t;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+typedef enum {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_FP8_E4M3 = 2 /* expert weights only: OCP E4M3 codes, with scales
+                      (moe_grouped_ffn_scaled / moe_forward_scaled) */
+} moe_dtype_t;
 
 /* Order of softmax and top-k ("Sparsely-Gated MoE 구현 관점에서 살펴보기",
  * section "Top-2 라우팅의 수치 예시": implementations either take the top-k
@@ -84,7 +89,9 @@ typedef struct {
   int32_t d_ff;            /* expert FFN inner size                         */
   float capacity_factor;   /* <= 0: unlimited; else C = min(T, ceil(cf*T*k/E)) */
   moe_dtype_t act_dtype;   /* X, X_perm, H                                  */
-  moe_dtype_t w_dtype;     /* W_gate, W_up, W_down (W_r, bias: always fp32) */
+  moe_dtype_t w_dtype;     /* W_gate, W_up, W_down (W_r, bias: always fp32);
+                              equal to act_dtype, or FP8_E4M3 with BF16
+                              activations in the _scaled entry points      */
   moe_gating_t gating;
   moe_dtype_t out_dtype;   /* out: F32 (no rounding beyond fp32) or BF16    */
 } moe_problem_t;
@@ -251,6 +258,37 @@ moe_status_t moe_forward_shared(const moe_problem_t* p, int32_t shared_d_ff,
                                 const void* Ws_down, void* out, int32_t* stats,
                                 void* workspace, size_t ws_bytes,
                                 hipStream_t stream, hipStream_t side_stream);
+
+/* FP8 expert weights with a scale per expert and projection
+ * ("Expert를 똑같이 나눴는데도 GPU가 대기하는 이유: MoE의 토큰 쏠림", sections
+ * "Weight Loading에서 텐서 구조 맞추기" and "적재 변환과 양자화 조합하기":
+ * a per-expert quantisation step fits into loading the packed expert
+ * weights).  p->w_dtype = MOE_FP8_E4M3, p->act_dtype = MOE_BF16; W_gate,
+ * W_up, W_down hold one byte per weight (OCP FP8 E4M3 codes, same [E, out,
+ * in] layout) and
+ *   w_scales [E, 3] fp32 (device): gate, up, down scale of each expert,
+ * so that expert e's weight is w_scales[e, proj] * decode(code).  The codes
+ * are decoded exactly to bf16 for the bf16 MFMAs; the scale multiplies the
+ * fp32 accumulator.  Same results and outputs as moe_grouped_ffn /
+ * moe_forward on the decoded weights (up to fp32 rounding); half the weight
+ * bytes.  d_model and d_ff must be multiples of 16 (else
+ * MOE_ERR_UNSUPPORTED).  Workspace: moe_grouped_ffn_workspace_bytes(p) /
+ * moe_workspace_bytes(p) of the FP8 problem.  moe_route(_stats),
+ * moe_permute and moe_combine take FP8 problems too (they do not read expert
+ * weights); moe_grouped_ffn and the moe_forward variants without scales
+ * return MOE_ERR_UNSUPPORTED for them. */
+moe_status_t moe_grouped_ffn_scaled(const moe_problem_t* p, const void* X_perm,
+                                    const int32_t* expert_offsets,
+                                    const void* W_gate, const void* W_up,
+                                    const void* W_down, const float* w_scales,
+                                    float* Y_perm, void* workspace,
+                                    size_t ws_bytes, hipStream_t stream);
+moe_status_t moe_forward_scaled(const moe_problem_t* p, const void* X,
+                                const float* W_r, const float* bias,
+                                const void* W_gate, const void* W_up,
+                                const void* W_down, const float* w_scales,
+                                void* out, int32_t* stats, void* workspace,
+                                size_t ws_bytes, hipStream_t stream);
 
 /* Static string naming a status code. */
 const char* moe_status_string(moe_status_t s);

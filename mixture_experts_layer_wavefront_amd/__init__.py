@@ -9,7 +9,8 @@ from .binding import (MOE_BF16, MOE_F32, MOE_SOFTMAX_THEN_TOPK,  # noqa: F401
                       forward_shared_workspace_bytes,
                       grouped_ffn_workspace_bytes, load, moe_combine,
                       moe_forward, moe_forward_shared, moe_forward_stats,
-                      moe_grouped_ffn, moe_permute, moe_route, moe_route_stats,
+                      moe_grouped_ffn, moe_grouped_ffn_scaled, moe_forward_scaled,
+                      moe_permute, moe_route, moe_route_stats,
                       forward_stats_workspace_bytes, route_stats_workspace_bytes,
                       permute_workspace_bytes, problem, route_workspace_bytes,
                       rows_bound,

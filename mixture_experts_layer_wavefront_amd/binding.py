@@ -21,6 +21,7 @@ MOE_ERR_HIP = -4
 
 MOE_F32 = 0
 MOE_BF16 = 1
+MOE_FP8_E4M3 = 2
 MOE_TOPK_THEN_SOFTMAX = 0
 MOE_SOFTMAX_THEN_TOPK = 1
 
@@ -32,7 +33,7 @@ SYMBOLS = ("moe_capacity", "moe_rows_bound", "moe_route_workspace_bytes",
            "moe_forward", "moe_route_stats_workspace_bytes", "moe_route_stats",
            "moe_forward_stats_workspace_bytes", "moe_forward_stats",
            "moe_forward_shared_workspace_bytes", "moe_forward_shared",
-           "moe_status_string")
+           "moe_grouped_ffn_scaled", "moe_forward_scaled", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -90,6 +91,10 @@ def load(path: str = LIB_PATH):
         "moe_forward_shared": (ctypes.c_int, [P, ctypes.c_int32, vp, vp, vp, vp,
                                               vp, vp, vp, vp, vp, vp, vp, vp,
                                               sz, st, st]),
+        "moe_grouped_ffn_scaled": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp,
+                                                  vp, sz, st]),
+        "moe_forward_scaled": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp,
+                                              vp, vp, sz, st]),
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -105,17 +110,19 @@ def status_string(status: int) -> str:
 
 
 def _dt(x):
-    return {"bf16": MOE_BF16, "f32": MOE_F32}[x] if isinstance(x, str) \
-        else int(x)
+    return {"bf16": MOE_BF16, "f32": MOE_F32, "fp8": MOE_FP8_E4M3}[x] \
+        if isinstance(x, str) else int(x)
 
 
 def problem(T, d_model, E, top_k, d_ff, capacity_factor=0.0, dtype="bf16",
-            gating=MOE_TOPK_THEN_SOFTMAX, out_dtype="f32") -> Problem:
-    """moe_problem_t; `dtype` is the activation and expert-weight dtype,
+            gating=MOE_TOPK_THEN_SOFTMAX, out_dtype="f32", w_dtype=None) -> Problem:
+    """moe_problem_t; `dtype` is the activation dtype and, unless `w_dtype`
+    is given ("fp8": FP8 E4M3 expert weights), the expert-weight dtype;
     `out_dtype` the dtype of the layer output (fp32 by default)."""
     dt = _dt(dtype)
     return Problem(int(T), int(d_model), int(E), int(top_k), int(d_ff),
-                   float(capacity_factor or 0.0), dt, dt, int(gating),
+                   float(capacity_factor or 0.0), dt,
+                   dt if w_dtype is None else _dt(w_dtype), int(gating),
                    _dt(out_dtype))
 
 
@@ -379,3 +386,43 @@ def moe_forward_stats(p, X, W_r, bias, W_gate, W_up, W_down, out=None,
         _ptr(router_stats, torch.float32, "router_stats"), _ptr(ws), ws.numel(),
         _stream(stream)), "moe_forward_stats")
     return out, router_stats
+
+
+def moe_grouped_ffn_scaled(p, X_perm, offsets, W_gate, W_up, W_down, w_scales,
+                           Y_perm=None, workspace=None, stream=None):
+    """moe_grouped_ffn with FP8 E4M3 expert weights (uint8 codes) and scales
+    [E, 3] (gate, up, down).  Returns Y_perm (fp32)."""
+    torch = _torch()
+    dev = X_perm.device
+    R = rows_bound(p)
+    if Y_perm is None:
+        Y_perm = torch.empty((max(R, 1), p.d_model), dtype=torch.float32, device=dev)
+    ws = _workspace(grouped_ffn_workspace_bytes(p), dev, workspace)
+    u8 = torch.uint8
+    _check(load().moe_grouped_ffn_scaled(
+        ctypes.byref(p), _ptr(X_perm, torch.bfloat16, "X_perm"),
+        _ptr(offsets, torch.int32, "offsets"), _ptr(W_gate, u8, "W_gate"),
+        _ptr(W_up, u8, "W_up"), _ptr(W_down, u8, "W_down"),
+        _ptr(w_scales, torch.float32, "w_scales"),
+        _ptr(Y_perm, torch.float32, "Y_perm"), _ptr(ws), ws.numel(),
+        _stream(stream)), "moe_grouped_ffn_scaled")
+    return Y_perm
+
+
+def moe_forward_scaled(p, X, W_r, bias, W_gate, W_up, W_down, w_scales,
+                       out=None, stats=None, workspace=None, stream=None):
+    """moe_forward with FP8 E4M3 expert weights and scales [E, 3]."""
+    torch = _torch()
+    dev = X.device
+    if out is None:
+        out = torch.empty((p.T, p.d_model), dtype=_out_dtype(p), device=dev)
+    ws = _workspace(workspace_bytes(p), dev, workspace)
+    u8 = torch.uint8
+    _check(load().moe_forward_scaled(
+        ctypes.byref(p), _ptr(X, torch.bfloat16, "X"), _ptr(W_r, torch.float32, "W_r"),
+        _ptr(bias, torch.float32, "bias"), _ptr(W_gate, u8, "W_gate"),
+        _ptr(W_up, u8, "W_up"), _ptr(W_down, u8, "W_down"),
+        _ptr(w_scales, torch.float32, "w_scales"), _ptr(out, _out_dtype(p), "out"),
+        _ptr(stats, torch.int32, "stats"), _ptr(ws), ws.numel(), _stream(stream)),
+        "moe_forward_scaled")
+    return out

@@ -77,6 +77,15 @@
 #ifndef MOE_SBAUX
 #define MOE_SBAUX kNonTemporal  // 32-row tiles: weight loads stream (nt)
 #endif
+#ifndef MOE_F8SBK
+#define MOE_F8SBK 128  // 32-row tiles with FP8 weights: K per stage (128-byte weight rows)
+#endif
+#ifndef MOE_F8SNS
+#define MOE_F8SNS 2
+#endif
+#ifndef MOE_F8SNW
+#define MOE_F8SNW 2  // 32-row tiles with FP8 weights: 64 output columns
+#endif
 #ifndef MOE_BNT_ROWS
 #define MOE_BNT_ROWS 256  // 256-row tiles: stream the weights up to this many rows per expert
 #endif
@@ -87,14 +96,32 @@ namespace {
 constexpr int kXcds = 8;
 constexpr int kNonTemporal = 2;  // "nt" bit of a buffer load's cache policy
 
-// Chunk swizzle of LDS row R (16-byte chunks).  128-byte rows (BK = 64, 8
-// chunks) and 64-byte rows (BK = 32, 4 chunks): 8 or 16 consecutive rows
-// reading the same logical chunk land on distinct banks under both a 32- and
-// a 64-bank LDS.
+// Chunk swizzle of LDS row R (16-byte chunks).  256-byte rows (16 chunks),
+// 128-byte rows (8 chunks) and 64-byte rows (4 chunks): 16, 8 or 16
+// consecutive rows reading the same logical chunk land on distinct banks under
+// both a 32- and a 64-bank LDS.
 template <int CPR>
 __device__ __forceinline__ uint32_t swz(uint32_t R) {
-  if constexpr (CPR == 8) return (R ^ (R >> 3)) & 7u;
+  if constexpr (CPR == 16) return (R ^ (R >> 2)) & 15u;
+  else if constexpr (CPR == 8) return (R ^ (R >> 3)) & 7u;
   else return ((R >> 1) ^ (R >> 3)) & 3u;
+}
+
+// Eight FP8 E4M3 codes (little-endian bytes) -> eight bf16 values.  Every
+// E4M3 value is exactly representable in bf16: decode to fp32 with the
+// hardware conversion, keep the upper 16 bits.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint2 q) {
+  typedef __attribute__((ext_vector_type(2))) float f32x2;
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, false);
+  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, true);
+  auto pk = [](float lo, float hi) {
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+  };
+  const i32x4 w = {(int)pk(a[0], a[1]), (int)pk(b[0], b[1]), (int)pk(c[0], c[1]),
+                   (int)pk(d[0], d[1])};
+  return __builtin_bit_cast(bf16x8, w);
 }
 
 // Wait until at most N vector-memory loads of this wave are outstanding,
@@ -126,7 +153,7 @@ __global__ __launch_bounds__(256) void ffn_schedule_kernel(
   if (e == E - 1) mt_prefix[E] = s[e];
 }
 
-template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS>
+template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS, bool BF8>
 struct GemmCfg {
   static constexpr int NWAVES = MW * NW;
   static constexpr int NT = NWAVES * kWave;
@@ -134,35 +161,44 @@ struct GemmCfg {
   static constexpr int BN = NW * TN * 32;            // output columns per tile
   static constexpr int NB = GATEUP ? 2 * TN : TN;    // B sub-tiles per wave
   static constexpr int BROWS = GATEUP ? 2 * BN : BN;  // B rows staged per K step
-  static constexpr int ROWS = BM + BROWS;
-  static constexpr int RB = BK * 2;                  // bytes per LDS row
-  static constexpr int CPR = RB / 16;                // 16-byte chunks per row
-  static constexpr int RPI = 1024 / RB;              // rows per wave-level load
-  static constexpr int STAGE = ROWS * RB;
-  static constexpr int NINSTR = ROWS / RPI;
+  // LDS stage: BM rows of A (bf16, RBA bytes each), then BROWS rows of B
+  // (bf16, or FP8 codes when BF8: RBB bytes each)
+  static constexpr int RBA = BK * 2;
+  static constexpr int RBB = BF8 ? BK : BK * 2;
+  static constexpr int CPRA = RBA / 16, CPRB = RBB / 16;  // 16-byte chunks per row
+  static constexpr int RPIA = 1024 / RBA, RPIB = 1024 / RBB;  // rows per wave-level load
+  static constexpr int NIA = BM / RPIA, NIB = BROWS / RPIB;
+  static constexpr int AREG = BM * RBA;
+  static constexpr int STAGE = AREG + BROWS * RBB;
+  static constexpr int NINSTR = NIA + NIB;
   // the first LW waves issue the global -> LDS loads (LW <= NWAVES)
   static constexpr int LW = (MOE_LW < NWAVES) ? MOE_LW : NWAVES;
   static constexpr int IPW = NINSTR / LW;
   static_assert(NINSTR % LW == 0, "loads must split evenly over waves");
-  static_assert(BM % RPI == 0 && BN % RPI == 0, "a load must not straddle operands");
+  static_assert(BM % RPIA == 0 && BN % RPIB == 0, "a load must not straddle operands");
   static constexpr int KSUB = BK / 16;               // MFMA k-steps per stage
   static constexpr int LDS_BYTES = NS * STAGE + 1040;  // + the tile prefix
 };
 
-// A [R, K] bf16 rows; B0/B1 [E, N, K] bf16 (gate/up, or down with B1 unused).
-// GATEUP: C = H bf16 [R, N].  Otherwise C = Y fp32 [R, N].  BAUX: cache-policy
+// A [R, K] bf16 rows; B0/B1 [E, N, K] bf16, or FP8 E4M3 codes when BF8
+// (gate/up, or down with B1 unused).  GATEUP: C = H bf16 [R, N].  Otherwise
+// C = Y fp32 [R, N].  With FP8 weights, scales [E, 3] (gate, up, down) scale
+// the fp32 accumulators before the epilogue; the codes are decoded exactly to
+// bf16 for the MFMAs.  BAUX: cache-policy
 // bits of the weight loads (kNonTemporal when each weight tile is read by
 // about one workgroup: the loads then stream past the caches).
-template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS, int BAUX>
+template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS, int BAUX, bool BF8>
 __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
-    const uint16_t* __restrict__ B1, int N, int K, int E,
+    const uint16_t* __restrict__ A, const void* __restrict__ B0,
+    const void* __restrict__ B1, int N, int K, int E,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ mt_prefix,
-    void* __restrict__ Cout) {
-  using Cfg = GemmCfg<MW, NW, TM, TN, GATEUP, BK, NS>;
+    void* __restrict__ Cout, const float* __restrict__ scales) {
+  using Cfg = GemmCfg<MW, NW, TM, TN, GATEUP, BK, NS, BF8>;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, NB = Cfg::NB, IPW = Cfg::IPW;
-  constexpr int NWAVES = Cfg::NWAVES, STAGE = Cfg::STAGE, RB = Cfg::RB, LW = Cfg::LW;
-  constexpr int CPR = Cfg::CPR, RPI = Cfg::RPI, KSUB = Cfg::KSUB;
+  constexpr int NWAVES = Cfg::NWAVES, STAGE = Cfg::STAGE, LW = Cfg::LW;
+  constexpr int RBA = Cfg::RBA, RBB = Cfg::RBB, CPRA = Cfg::CPRA, CPRB = Cfg::CPRB;
+  constexpr int RPIA = Cfg::RPIA, RPIB = Cfg::RPIB, NIA = Cfg::NIA, AREG = Cfg::AREG;
+  constexpr int KSUB = Cfg::KSUB;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   int32_t* s_pref = reinterpret_cast<int32_t*>(smem + NS * STAGE);
 
@@ -196,28 +232,36 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(
   const int n0 = n_t * BN;
   const int ncols = min(BN, N - n0);
 
-  const uint32_t kbytes = (uint32_t)K * 2u;
+  const uint32_t kbytes = (uint32_t)K * 2u;                  // A row
+  const uint32_t kbytesB = (uint32_t)K * (BF8 ? 1u : 2u);    // B row
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(A + (int64_t)m_start * K, (uint32_t)rows * kbytes);
-  const int64_t boff = ((int64_t)e * N + n0) * K;
-  const __amdgpu_buffer_rsrc_t rB0 = make_rsrc(B0 + boff, (uint32_t)ncols * kbytes);
-  const __amdgpu_buffer_rsrc_t rB1 = GATEUP ? make_rsrc(B1 + boff, (uint32_t)ncols * kbytes) : rB0;
+  const int64_t boff = ((int64_t)e * N + n0) * K * (BF8 ? 1 : 2);  // bytes
+  const __amdgpu_buffer_rsrc_t rB0 =
+      make_rsrc(static_cast<const char*>(B0) + boff, (uint32_t)ncols * kbytesB);
+  const __amdgpu_buffer_rsrc_t rB1 =
+      GATEUP ? make_rsrc(static_cast<const char*>(B1) + boff, (uint32_t)ncols * kbytesB) : rB0;
 
   // ---- per-lane load offsets (one 16-byte chunk per wave-level load) -------
+  // Loads 0..NIA-1 fill the A rows, the rest the B rows (B-local row index
+  // for the swizzle); kcol = first K element of the lane's chunk.
   uint32_t voff[IPW];
   int kcol[IPW];
   {
-    const uint32_t p = lane % CPR;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int qi = wave + LW * i;
-      const uint32_t R = qi * RPI + lane / CPR;
-      const uint32_t c = p ^ swz<CPR>(R);
-      uint32_t row;
-      if (qi * RPI < BM) row = R;
-      else if (!GATEUP || qi * RPI < BM + BN) row = R - BM;
-      else row = R - BM - BN;
-      voff[i] = row * kbytes + c * 16;
-      kcol[i] = c * 8;
+      if (qi < NIA) {
+        const uint32_t R = qi * RPIA + lane / CPRA;
+        const uint32_t c = (lane % CPRA) ^ swz<CPRA>(R);
+        voff[i] = R * kbytes + c * 16;
+        kcol[i] = c * 8;
+      } else {
+        const uint32_t R = (qi - NIA) * RPIB + lane / CPRB;
+        const uint32_t c = (lane % CPRB) ^ swz<CPRB>(R);
+        const uint32_t row = (GATEUP && R >= (uint32_t)BN) ? R - BN : R;
+        voff[i] = row * kbytesB + c * 16;
+        kcol[i] = c * (BF8 ? 16 : 8);
+      }
     }
   }
   const int nk = (K + BK - 1) / BK;
@@ -228,12 +272,12 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int qi = wave + LW * i;
-      uint32_t vo = voff[i] + (uint32_t)kt * RB;
+      uint32_t vo = voff[i] + (uint32_t)kt * (qi < NIA ? RBA : RBB);
       if (ktail && kt * BK + kcol[i] >= K) vo = kOob;
       char* dst = smem + stage * STAGE + qi * 1024;
-      if (qi * RPI < BM)
+      if (qi < NIA)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, MOE_LDS_PTR(dst), 16, vo, 0, 0, 0);
-      else if (!GATEUP || qi * RPI < BM + BN)
+      else if (!GATEUP || (qi - NIA) * RPIB < BN)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rB0, MOE_LDS_PTR(dst), 16, vo, 0, 0, BAUX);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rB1, MOE_LDS_PTR(dst), 16, vo, 0, 0, BAUX);
@@ -259,15 +303,18 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(
 #pragma unroll
     for (int mi = 0; mi < TM; ++mi) {
       const uint32_t R = wm * TM * 32 + mi * 32 + (lane & 31);
-      offA[mi][ks] = R * RB + ((c ^ swz<CPR>(R)) * 16);
+      offA[mi][ks] = R * RBA + ((c ^ swz<CPRA>(R)) * 16);
     }
 #pragma unroll
     for (int nj = 0; nj < NB; ++nj) {
       uint32_t brow;
       if (GATEUP) brow = (nj < TN) ? wn * TN * 32 + nj * 32 : BN + wn * TN * 32 + (nj - TN) * 32;
       else brow = wn * TN * 32 + nj * 32;
-      const uint32_t R = BM + brow + (lane & 31);
-      offB[nj][ks] = R * RB + ((c ^ swz<CPR>(R)) * 16);
+      const uint32_t R = brow + (lane & 31);  // B-local row
+      if constexpr (BF8)  // 8 codes: half (lane >> 5) of 16-byte chunk ks
+        offB[nj][ks] = AREG + R * RBB + ((ks ^ swz<CPRB>(R)) * 16) + (lane >> 5) * 8;
+      else
+        offB[nj][ks] = AREG + R * RBB + ((c ^ swz<CPRB>(R)) * 16);
     }
   }
 
@@ -299,7 +346,10 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(
         for (int mi = 0; mi < TM; ++mi)
           if (!RAGGED || mi < tm_active) a[mi] = *reinterpret_cast<const bf16x8*>(st + offA[mi][ks]);
 #pragma unroll
-        for (int nj = 0; nj < NB; ++nj) b[nj] = *reinterpret_cast<const bf16x8*>(st + offB[nj][ks]);
+        for (int nj = 0; nj < NB; ++nj) {
+          if constexpr (BF8) b[nj] = fp8x8_to_bf16x8(*reinterpret_cast<const uint2*>(st + offB[nj][ks]));
+          else b[nj] = *reinterpret_cast<const bf16x8*>(st + offB[nj][ks]);
+        }
 #pragma unroll
         for (int mi = 0; mi < TM; ++mi)
           if (!RAGGED || mi < tm_active) {
@@ -312,6 +362,18 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(
   };
   if (!MOE_SKIP || tm_active == TM) kloop(std::false_type{});
   else kloop(std::true_type{});
+
+  // FP8 weights: the expert's scales multiply the accumulators
+  if constexpr (BF8) {
+    const float s0 = scales[e * 3 + (GATEUP ? 0 : 2)];
+    const float s1 = GATEUP ? scales[e * 3 + 1] : s0;
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < NB; ++nj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mi][nj][r] *= (GATEUP && nj >= TN) ? s1 : s0;
+  }
 
   // ---- epilogue ---------------------------------------------------------------
   // acc[mi][nj][r] is element (row, col) of the tile with
@@ -399,12 +461,13 @@ __global__ __launch_bounds__(256) void ffn_f32_down_kernel(
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS, int BAUX>
+template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS, int BAUX, bool BF8 = false>
 hipError_t launch_gemm(const void* A, const void* B0, const void* B1, int N,
                        int K, int E, int64_t R, const int32_t* offsets,
-                       const int32_t* mt_prefix, void* C, hipStream_t stream) {
-  using Cfg = GemmCfg<MW, NW, TM, TN, GATEUP, BK, NS>;
-  auto kern = grouped_gemm_kernel<MW, NW, TM, TN, GATEUP, BK, NS, BAUX>;
+                       const int32_t* mt_prefix, void* C, hipStream_t stream,
+                       const float* scales = nullptr) {
+  using Cfg = GemmCfg<MW, NW, TM, TN, GATEUP, BK, NS, BF8>;
+  auto kern = grouped_gemm_kernel<MW, NW, TM, TN, GATEUP, BK, NS, BAUX, BF8>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
       Cfg::LDS_BYTES);
@@ -417,16 +480,17 @@ hipError_t launch_gemm(const void* A, const void* B0, const void* B1, int N,
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::LDS_BYTES, stream,
-                     static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B0),
-                     static_cast<const uint16_t*>(B1), N, K, E, offsets, mt_prefix, C);
+                     static_cast<const uint16_t*>(A), B0, B1, N, K, E, offsets, mt_prefix, C,
+                     scales);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int ffn_tile_rows(bool bf16, int rows_per_expert) {
+int ffn_tile_rows(bool bf16, int rows_per_expert, bool fp8) {
   if (!bf16) return 0;
-  return rows_per_expert <= 64 ? 32 : 256;
+  if (rows_per_expert <= 64) return 32;
+  return (fp8 && rows_per_expert <= 512) ? 128 : 256;
 }
 
 size_t ffn_scratch_bytes(int64_t R, int E, int d_ff, bool bf16) {
@@ -438,8 +502,10 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
                               const void* W_up, const void* W_down, int64_t R,
                               int d, int E, int d_ff, int rows_per_expert,
                               float* Y_perm, void* scratch, bool prefix_ready,
-                              hipStream_t stream) {
-  const bool small_m = ffn_tile_rows(bf16, rows_per_expert) == 32;
+                              hipStream_t stream, const float* w_scales) {
+  const bool fp8 = w_scales != nullptr;
+  const int bm = ffn_tile_rows(bf16, rows_per_expert, fp8);
+  const bool small_m = bm == 32;
   if (R == 0) return hipSuccess;
   int32_t* mt_prefix = static_cast<int32_t*>(scratch);
   void* H = static_cast<char*>(scratch) + align256((size_t)(E + 1) * 4);
@@ -462,13 +528,38 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
       ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, 32, mt_prefix);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
+    if (fp8) {
+      err = launch_gemm<1, MOE_F8SNW, 1, 1, true, MOE_F8SBK, MOE_F8SNS, MOE_SBAUX, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales);
+      if (err != hipSuccess) return err;
+      return launch_gemm<1, MOE_F8SNW, 1, 1, false, MOE_F8SBK, MOE_F8SNS, MOE_SBAUX, true>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream, w_scales);
+    }
     err = launch_gemm<1, MOE_SNW, 1, 1, true, MOE_SBK, MOE_SNS, MOE_SBAUX>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
     if (err != hipSuccess) return err;
     return launch_gemm<1, MOE_SNW, 1, 1, false, MOE_SBK, MOE_SNS, MOE_SBAUX>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
   }
   if (!prefix_ready) {
-    ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, 256, mt_prefix);
+    ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, bm, mt_prefix);
     if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (fp8 && bm == 128) {
+    // FP8 weights, up to a few hundred rows per expert: 128-row tiles and
+    // K = 128 per stage, so each weight row is read 128 bytes (one cache
+    // line) at a time; 64 KB stages, two of them
+    if (rows_per_expert <= 128) {
+      err = launch_gemm<2, 4, 2, 1, true, 128, 2, kNonTemporal, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales);
+      if (err != hipSuccess) return err;
+      return launch_gemm<2, 4, 2, 2, false, 128, 2, kNonTemporal, true>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream, w_scales);
+    }
+    err = launch_gemm<2, 4, 2, 1, true, 128, 2, 0, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales);
+    if (err != hipSuccess) return err;
+    return launch_gemm<2, 4, 2, 2, false, 128, 2, 0, true>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream, w_scales);
+  }
+  if (fp8) {
+    // FP8 weights, many rows per expert: the 256-row tiles of the bf16 path
+    // (the weight tiles are shared by several M-tiles through L2)
+    err = launch_gemm<2, MOE_NW, 4, 4 / MOE_NW, true, MOE_BK, MOE_NS, 0, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales);
+    if (err != hipSuccess) return err;
+    return launch_gemm<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, 0, true>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream, w_scales);
   }
   if (rows_per_expert <= MOE_BNT_ROWS) {
     // about one M-tile per expert: every weight tile is read once

@@ -35,15 +35,16 @@ hipError_t launch_permute(const void* X, bool x_bf16, const int32_t* topk_idx,
 // the shape alone) picks the tile shape: ffn_tile_rows() rows per tile (0:
 // fp32 layers, no tile schedule).  The tile schedule (exclusive prefix over
 // experts of their tile counts, E + 1 ints) lives at the start of `scratch`;
-// with prefix_ready the caller has already written it there.
-int ffn_tile_rows(bool bf16, int rows_per_expert);
+// with prefix_ready the caller has already written it there.  w_scales !=
+// nullptr: the weights are FP8 E4M3 codes with scales [E, 3] (bf16 layers).
+int ffn_tile_rows(bool bf16, int rows_per_expert, bool fp8 = false);
 size_t ffn_scratch_bytes(int64_t R, int E, int d_ff, bool bf16);
 hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
                               const int32_t* offsets, const void* W_gate,
                               const void* W_up, const void* W_down,
                               int64_t R, int d, int E, int d_ff, int rows_per_expert,
                               float* Y_perm, void* scratch, bool prefix_ready,
-                              hipStream_t stream);
+                              hipStream_t stream, const float* w_scales = nullptr);
 
 // Expert offsets {0, T} of a dense FFN over all T rows (one "expert").
 hipError_t launch_dense_offsets(int32_t* offsets, int T, hipStream_t stream);

@@ -23,23 +23,34 @@ bool is_bf16(const moe_problem_t* p) { return p->act_dtype == MOE_BF16; }
 bool out_bf16(const moe_problem_t* p) { return p->out_dtype == MOE_BF16; }
 size_t act_bytes(const moe_problem_t* p) { return is_bf16(p) ? 2 : 4; }
 
-moe_status_t validate(const moe_problem_t* p) {
+// fp8_ok: FP8 expert weights (with bf16 activations) are accepted: the
+// scaled entry points and the workspace-size queries.
+moe_status_t validate(const moe_problem_t* p, bool fp8_ok = false) {
   if (p == nullptr) return MOE_ERR_INVALID_ARG;
   if (p->T < 0 || p->d_model <= 0 || p->E <= 0 || p->top_k <= 0 || p->d_ff <= 0)
     return MOE_ERR_INVALID_ARG;
   if (p->top_k > p->E) return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(p->capacity_factor)) return MOE_ERR_INVALID_ARG;
   if (p->act_dtype != MOE_F32 && p->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (p->w_dtype != MOE_F32 && p->w_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (p->w_dtype != MOE_F32 && p->w_dtype != MOE_BF16 && p->w_dtype != MOE_FP8_E4M3)
+    return MOE_ERR_INVALID_ARG;
+  if (p->act_dtype == MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
   if (p->gating != MOE_TOPK_THEN_SOFTMAX && p->gating != MOE_SOFTMAX_THEN_TOPK)
     return MOE_ERR_INVALID_ARG;
   if (p->out_dtype != MOE_F32 && p->out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (p->E > kMaxE || p->top_k > kMaxK || p->T >= kMaxT) return MOE_ERR_UNSUPPORTED;
   if (p->d_model % 8 != 0 || p->d_ff % 8 != 0) return MOE_ERR_UNSUPPORTED;
   if (p->d_model > kMaxDim || p->d_ff > kMaxDim) return MOE_ERR_UNSUPPORTED;
+  if (p->w_dtype == MOE_FP8_E4M3) {
+    if (!fp8_ok || p->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (p->d_model % 16 != 0 || p->d_ff % 16 != 0) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+  }
   if (p->act_dtype != p->w_dtype) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
+
+bool is_fp8(const moe_problem_t* p) { return p->w_dtype == MOE_FP8_E4M3; }
 
 // C as an int for the kernels: INT_MAX when unlimited.
 int capacity_int(const moe_problem_t* p) {
@@ -116,7 +127,7 @@ hipError_t enqueue_routed(const moe_problem_t* p, const void* X, const float* W_
                           const float* bias, const void* W_gate, const void* W_up,
                           const void* W_down, int32_t* stats, float* router_stats,
                           char* ws, const ForwardLayout& L, hipStream_t stream,
-                          RoutedOut* r) {
+                          RoutedOut* r, const float* w_scales = nullptr) {
   int32_t* topk_idx = reinterpret_cast<int32_t*>(ws + L.topk_idx);
   float* topk_w = reinterpret_cast<float*>(ws + L.topk_w);
   int32_t* st_buf = stats ? stats : reinterpret_cast<int32_t*>(ws + L.stats);
@@ -135,7 +146,7 @@ hipError_t enqueue_routed(const moe_problem_t* p, const void* X, const float* W_
                                    router_stats, stream);
   if (e != hipSuccess) return e;
   // the permute also writes the FFN's tile schedule (start of its scratch)
-  const int bm = moe::ffn_tile_rows(bf, mean_rows_per_expert(p));
+  const int bm = moe::ffn_tile_rows(bf, mean_rows_per_expert(p), w_scales != nullptr);
   int32_t* mt_prefix = bm > 0 ? reinterpret_cast<int32_t*>(ws + L.ffn_scratch) : nullptr;
   e = moe::launch_permute(X, bf, topk_idx, p->T, p->d_model, p->E, p->top_k,
                           capacity_int(p), counts, offsets, dropped, dest_row, row_token,
@@ -143,7 +154,7 @@ hipError_t enqueue_routed(const moe_problem_t* p, const void* X, const float* W_
   if (e != hipSuccess) return e;
   return moe::launch_grouped_ffn(x_perm, bf, offsets, W_gate, W_up, W_down, moe_rows_bound(p),
                                  p->d_model, p->E, p->d_ff, mean_rows_per_expert(p), y_perm,
-                                 ws + L.ffn_scratch, mt_prefix != nullptr, stream);
+                                 ws + L.ffn_scratch, mt_prefix != nullptr, stream, w_scales);
 }
 
 }  // namespace
@@ -151,14 +162,14 @@ hipError_t enqueue_routed(const moe_problem_t* p, const void* X, const float* W_
 extern "C" {
 
 int64_t moe_capacity(const moe_problem_t* p) {
-  if (validate(p) != MOE_OK) return -1;
+  if (validate(p, true) != MOE_OK) return -1;
   if (!(p->capacity_factor > 0.f)) return -1;
   const double c = std::ceil((double)p->capacity_factor * p->T * p->top_k / p->E);
   return c < (double)p->T ? (int64_t)c : (int64_t)p->T;
 }
 
 int64_t moe_rows_bound(const moe_problem_t* p) {
-  if (validate(p) != MOE_OK) return 0;
+  if (validate(p, true) != MOE_OK) return 0;
   const int64_t Tk = (int64_t)p->T * p->top_k;
   const int64_t C = moe_capacity(p);
   if (C < 0) return Tk;
@@ -167,29 +178,29 @@ int64_t moe_rows_bound(const moe_problem_t* p) {
 }
 
 size_t moe_route_workspace_bytes(const moe_problem_t* p) {
-  if (validate(p) != MOE_OK) return 0;
+  if (validate(p, true) != MOE_OK) return 0;
   return a256(moe::route_scratch_bytes(p->T, p->E, p->d_model, is_bf16(p), false));
 }
 
 size_t moe_permute_workspace_bytes(const moe_problem_t* p) {
-  if (validate(p) != MOE_OK) return 0;
+  if (validate(p, true) != MOE_OK) return 0;
   return a256(moe::permute_scratch_bytes(p->T, p->top_k, p->E));
 }
 
 size_t moe_grouped_ffn_workspace_bytes(const moe_problem_t* p) {
-  if (validate(p) != MOE_OK) return 0;
+  if (validate(p, true) != MOE_OK) return 0;
   return a256(moe::ffn_scratch_bytes(moe_rows_bound(p), p->E, p->d_ff, is_bf16(p)));
 }
 
 size_t moe_workspace_bytes(const moe_problem_t* p) {
-  if (validate(p) != MOE_OK) return 0;
+  if (validate(p, true) != MOE_OK) return 0;
   return forward_layout(p).total;
 }
 
 moe_status_t moe_route(const moe_problem_t* p, const void* X, const float* W_r,
                        const float* bias, int32_t* topk_idx, float* topk_w,
                        void* workspace, size_t ws_bytes, hipStream_t stream) {
-  moe_status_t st = validate(p);
+  moe_status_t st = validate(p, true);
   if (st != MOE_OK) return st;
   if (p->T == 0) return MOE_OK;
   if (!X || !W_r || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
@@ -201,7 +212,7 @@ moe_status_t moe_route(const moe_problem_t* p, const void* X, const float* W_r,
 }
 
 size_t moe_route_stats_workspace_bytes(const moe_problem_t* p) {
-  if (validate(p) != MOE_OK) return 0;
+  if (validate(p, true) != MOE_OK) return 0;
   return a256(moe::route_scratch_bytes(p->T, p->E, p->d_model, is_bf16(p), true));
 }
 
@@ -209,7 +220,7 @@ moe_status_t moe_route_stats(const moe_problem_t* p, const void* X, const float*
                              const float* bias, int32_t* topk_idx, float* topk_w,
                              float* router_stats, void* workspace, size_t ws_bytes,
                              hipStream_t stream) {
-  moe_status_t st = validate(p);
+  moe_status_t st = validate(p, true);
   if (st != MOE_OK) return st;
   if (p->T == 0) return MOE_OK;
   if (!X || !W_r || !topk_idx || !topk_w || !router_stats) return MOE_ERR_INVALID_ARG;
@@ -225,7 +236,7 @@ moe_status_t moe_permute(const moe_problem_t* p, const void* X,
                          int32_t* expert_offsets, int32_t* num_dropped,
                          int32_t* dest_row, int32_t* row_token, void* X_perm,
                          void* workspace, size_t ws_bytes, hipStream_t stream) {
-  moe_status_t st = validate(p);
+  moe_status_t st = validate(p, true);
   if (st != MOE_OK) return st;
   if (!expert_counts || !expert_offsets || !num_dropped) return MOE_ERR_INVALID_ARG;
   if (p->T > 0 && (!X || !topk_idx || !dest_row || !row_token || !X_perm))
@@ -257,7 +268,7 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* X_perm,
 moe_status_t moe_combine(const moe_problem_t* p, const float* Y_perm,
                          const int32_t* dest_row, const float* topk_w, void* out,
                          hipStream_t stream) {
-  moe_status_t st = validate(p);
+  moe_status_t st = validate(p, true);
   if (st != MOE_OK) return st;
   if (p->T == 0) return MOE_OK;
   if (!Y_perm || !dest_row || !topk_w || !out) return MOE_ERR_INVALID_ARG;
@@ -363,6 +374,48 @@ moe_status_t moe_forward_shared(const moe_problem_t* p, int32_t shared_d_ff,
                             y_shared, out_bf16(p), out, stream);
   if (fork) (void)hipEventDestroy(fork);
   if (join) (void)hipEventDestroy(join);
+  return hip_status(e);
+}
+
+moe_status_t moe_grouped_ffn_scaled(const moe_problem_t* p, const void* X_perm,
+                                    const int32_t* expert_offsets, const void* W_gate,
+                                    const void* W_up, const void* W_down,
+                                    const float* w_scales, float* Y_perm, void* workspace,
+                                    size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = validate(p, true);
+  if (st != MOE_OK) return st;
+  if (!is_fp8(p)) return MOE_ERR_UNSUPPORTED;
+  const int64_t R = moe_rows_bound(p);
+  if (R == 0) return MOE_OK;
+  if (!X_perm || !expert_offsets || !W_gate || !W_up || !W_down || !w_scales || !Y_perm)
+    return MOE_ERR_INVALID_ARG;
+  if (!workspace || ws_bytes < moe_grouped_ffn_workspace_bytes(p)) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_grouped_ffn(X_perm, true, expert_offsets, W_gate, W_up, W_down,
+                                            R, p->d_model, p->E, p->d_ff,
+                                            mean_rows_per_expert(p), Y_perm, workspace, false,
+                                            stream, w_scales));
+}
+
+moe_status_t moe_forward_scaled(const moe_problem_t* p, const void* X, const float* W_r,
+                                const float* bias, const void* W_gate, const void* W_up,
+                                const void* W_down, const float* w_scales, void* out,
+                                int32_t* stats, void* workspace, size_t ws_bytes,
+                                hipStream_t stream) {
+  moe_status_t st = validate(p, true);
+  if (st != MOE_OK) return st;
+  if (!is_fp8(p)) return MOE_ERR_UNSUPPORTED;
+  if (p->T == 0) return MOE_OK;
+  if (!X || !W_r || !W_gate || !W_up || !W_down || !w_scales || !out)
+    return MOE_ERR_INVALID_ARG;
+  const ForwardLayout L = forward_layout(p);
+  if (!workspace || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  RoutedOut r{};
+  hipError_t e = enqueue_routed(p, X, W_r, bias, W_gate, W_up, W_down, stats, nullptr, ws, L,
+                                stream, &r, w_scales);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_combine(r.y_perm, r.dest_row, r.topk_w, p->T, p->d_model, p->top_k,
+                          nullptr, out_bf16(p), out, stream);
   return hip_status(e);
 }
 

@@ -147,6 +147,37 @@ def test_shared_expert_arguments_checked_on_the_host():
                                   None, 0, None, None) == B.MOE_OK
 
 
+def test_fp8_weights_only_through_the_scaled_entry_points():
+    lib = B.load()
+    fake = ctypes.c_void_p(0x1000)
+    p = B.problem(8, 64, 4, 2, 64, w_dtype="fp8")
+    # sizes are defined; the unscaled entry points reject FP8 weights
+    assert lib.moe_workspace_bytes(ctypes.byref(p)) > 0
+    assert lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(p)) > 0
+    assert lib.moe_forward(ctypes.byref(p), fake, fake, None, fake, fake, fake,
+                           fake, None, fake, 1 << 40, None) == B.MOE_ERR_UNSUPPORTED
+    # FP8 needs bf16 activations and multiples of 16
+    for kw in (dict(dtype="f32"), dict(d_model=72), dict(d_ff=72)):
+        args = dict(T=8, d_model=64, E=4, top_k=2, d_ff=64, w_dtype="fp8")
+        args.update(kw)
+        q = B.problem(**args)
+        assert lib.moe_forward_scaled(ctypes.byref(q), fake, fake, None, fake, fake,
+                                      fake, fake, fake, None, fake, 1 << 40,
+                                      None) == B.MOE_ERR_UNSUPPORTED
+    # scales are required; the scaled entry points reject bf16 weights
+    assert lib.moe_forward_scaled(ctypes.byref(p), fake, fake, None, fake, fake, fake,
+                                  None, fake, None, fake, 1 << 40,
+                                  None) == B.MOE_ERR_INVALID_ARG
+    pb = B.problem(8, 64, 4, 2, 64)
+    assert lib.moe_grouped_ffn_scaled(ctypes.byref(pb), fake, fake, fake, fake, fake,
+                                      fake, fake, fake, 1 << 40,
+                                      None) == B.MOE_ERR_UNSUPPORTED
+    need = lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(p))
+    assert lib.moe_grouped_ffn_scaled(ctypes.byref(p), fake, fake, fake, fake, fake,
+                                      fake, fake, fake, need - 1,
+                                      None) == B.MOE_ERR_WORKSPACE
+
+
 def test_empty_batch_is_a_noop_without_device_work():
     lib = B.load()
     p = B.problem(0, 64, 4, 2, 64)
