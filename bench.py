@@ -250,6 +250,24 @@ def main():
     bytes_comb = N * d * 4 + T * d * 4 + T * k * 8
     bytes_ffn = 3 * active * d * dff * w_b + N * d * a_b + N * d * 4
 
+    # the FFN's bound: MFMA when its algorithmic flops per HBM byte exceed the
+    # machine balance (bf16 MFMA peak / HBM peak), else HBM
+    roofline = {"kernel": "grouped SwiGLU FFN (gate/up GEMM + SwiGLU epilogue, "
+                          "down GEMM)",
+                "traffic": None if args.fp8 else _traffic(args.workload),
+                "flops_per_launch": ffn_flops, "bytes_per_launch": bytes_ffn,
+                "ms_per_launch": t_ffn}
+    if ffn_flops / bytes_ffn >= PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3:
+        roofline.update(bound="mfma", achieved=ffn_tflops, peak=PEAK_BF16_TFLOPS,
+                        unit="TFLOP/s", frac=ffn_tflops / PEAK_BF16_TFLOPS)
+    else:
+        gbs = bytes_ffn / (t_ffn * 1e6)
+        roofline.update(bound="hbm", achieved=gbs, peak=PEAK_HBM_GBS, unit="GB/s",
+                        frac=gbs / PEAK_HBM_GBS)
+    roofline = {k: roofline[k] for k in ("bound", "kernel", "achieved", "peak", "unit",
+                                         "frac", "traffic", "flops_per_launch",
+                                         "bytes_per_launch", "ms_per_launch")}
+
     line = {
         "metric": "MoE-layer tokens/s + grouped-GEMM TFLOP/s (% bf16 MFMA peak), "
                   "Mixtral shape",
@@ -272,12 +290,7 @@ def main():
                    "T": T, "d_model": d, "E": E, "top_k": k, "d_ff": dff,
                    "capacity_factor": wl.capacity_factor,
                    "gating": ["topk_then_softmax", "softmax_then_topk"][wl.gating]},
-        "roofline": {"bound": "mfma", "kernel": "grouped SwiGLU FFN "
-                     "(gate/up GEMM + SwiGLU epilogue, down GEMM)",
-                     "achieved": ffn_tflops, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": ffn_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": _traffic(args.workload),
-                     "flops_per_launch": ffn_flops, "ms_per_launch": t_ffn},
+        "roofline": roofline,
         "stages_ms": {"route": t_route, "permute": t_perm, "grouped_ffn": t_ffn,
                       "combine": t_comb},
         "stages_gbs": {"route": bytes_route / (t_route * 1e6),

@@ -129,8 +129,8 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint2 q) {
 // __syncthreads() would also wait for the loads of the later stages.
 template <int N>
 __device__ __forceinline__ void stage_barrier() {
-  if constexpr (N >= 63) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+  static_assert(N >= 0 && N < 63, "vmcnt holds at most 63 outstanding loads");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
