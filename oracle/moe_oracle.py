@@ -1,4 +1,5 @@
-"""CPU oracle for the forward pass of one sparsely-gated MoE FFN layer.
+"""CPU oracle for the forward and backward passes of one sparsely-gated MoE
+FFN layer.
 
 TEST INFRASTRUCTURE ONLY.  This module is the slow, plain, fp64 statement of
 what the layer computes.  Only the test-suite, the package smoke check and the
@@ -444,3 +445,132 @@ def moe_forward_tokens(tokens, X, idx, w, dest, expert_weights, d_out):
             if (t, j) in y:
                 out[i] += w[t, j] * y[(t, j)]
     return out
+
+
+# ---------------------------------------------------------------------------
+# Backward pass of the layer
+#     [HF] "Unsloth와의 MoE 학습 경로": training runs the same grouped expert
+#     GEMMs as inference, now with gradients; [MOON] "이 기술은 무엇인가":
+#     in training the expert weights' gradients flow back in the backward
+#     pass.  The pages print no formula.  Reading: the gradients of a scalar
+#     loss whose gradient with respect to the layer output is ``dout``, by
+#     the chain rule through each forward step, with the top-k selection and
+#     the capacity assignment held fixed (both are piecewise constant in the
+#     inputs, so no gradient flows through them) and the fp32 rounding of the
+#     logits taken as the identity.
+#       combine     dY_perm[r] = w[t,j] dout[t] and dw[t,j] = <dout[t], Y_perm[r]>
+#                   for a kept copy r = dest[t,j]; a dropped copy has dw = 0
+#       expert FFN  on its rows A with G = A Wg^T, U = A Wu^T,
+#                   H = silu(G) U, Y = H Wd^T:
+#                   dH = dY Wd, dWd = dY^T H, dG = dH U silu'(G),
+#                   dU = dH silu(G), dWg = dG^T A, dWu = dU^T A,
+#                   dA = dG Wg + dU Wu;  silu'(z) = s (1 + z (1 - s)), s = sigmoid(z)
+#       permute     dX[t] = sum over t's kept copies of dA[dest[t,j]]
+#       gate        both orders give the softmax of the selected logits (the
+#                   renormalised top-k of the full softmax equals it), so
+#                   dl[t, idx[t,j]] = w[t,j] (dw[t,j] - sum_i w[t,i] dw[t,i])
+#                   and dl is zero at unselected experts
+#       router      dW_r = dl^T X, dbias = sum_t dl[t], dX[t] += dl[t] W_r
+# ---------------------------------------------------------------------------
+def silu_grad(z):
+    """Derivative of silu: ``s (1 + z (1 - s))`` with s = sigmoid(z), fp64."""
+    z = _f64(z)
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 + z * (1.0 - s))
+
+
+def expert_ffn_backward(A, Wg, Wu, Wd, dY):
+    """Gradients of one expert's SwiGLU FFN on rows A [n, d] given dY [n, d]:
+    returns (dA [n, d], dWg [d_ff, d], dWu [d_ff, d], dWd [d, d_ff]), fp64."""
+    A, Wg, Wu, Wd, dY = (_f64(v) for v in (A, Wg, Wu, Wd, dY))
+    G = A @ Wg.T
+    U = A @ Wu.T
+    H = silu(G) * U
+    dH = dY @ Wd
+    dWd = dY.T @ H
+    dG = dH * U * silu_grad(G)
+    dU = dH * silu(G)
+    dWg = dG.T @ A
+    dWu = dU.T @ A
+    dA = dG @ Wg + dU @ Wu
+    return dA, dWg, dWu, dWd
+
+
+def gate_weights_backward(w, dw):
+    """Logit gradient of the selected experts, ``w (dw - <w, dw>)`` per row
+    ([T, k] fp64), for gate weights w [T, k] that are the softmax of the
+    selected logits."""
+    w, dw = _f64(w), _f64(dw)
+    return w * (dw - np.sum(w * dw, axis=1, keepdims=True))
+
+
+def moe_backward(X, W_r, bias, W_gate, W_up, W_down, dout, k,
+                 capacity_factor=None, gating=TOPK_THEN_SOFTMAX, idx=None):
+    """Gradients of the layer: the forward steps are redone in fp64 (logits
+    in fp32 as in ``moe_forward``), then each step's backward in reverse
+    order.  ``idx`` [T, k], when given, replaces the top-k selection (tests
+    pass the ids another implementation selected, so that tokens with fp32
+    near-ties are routed alike); the gate weights still come from this
+    module's logits.
+
+    Returns a dict with dX [T, d], dW_r [E, d], dbias [E], dW_gate, dW_up
+    [E, d_ff, d], dW_down [E, d, d_ff] (all fp64) and the forward pieces
+    (idx, w, dest, offsets, Y_perm, dw, dl).
+    """
+    X = np.asarray(X)
+    T, d = X.shape
+    E = W_r.shape[0]
+    d_ff = W_gate.shape[1]
+    logits = router_logits(X, W_r, bias)
+    if idx is None:
+        idx, _ = select_topk(logits, k)
+    idx = np.asarray(idx, dtype=np.int64)
+    w = gate_weights(logits, idx, gating)
+    a = assign(idx, E, capacity(T, k, E, capacity_factor))
+    dest, offsets = a["dest"], a["offsets"]
+    X_perm = _f64(gather_rows(X, a["row_token"]))
+    Y_perm = grouped_ffn(X_perm, offsets, W_gate, W_up, W_down)
+    dout = _f64(dout)
+
+    # combine
+    N = int(offsets[E])
+    dY_perm = np.zeros((N, d))
+    dw = np.zeros((T, k))
+    for t in range(T):
+        for j in range(k):
+            r = dest[t, j]
+            if r >= 0:
+                dY_perm[r] = w[t, j] * dout[t]
+                dw[t, j] = np.dot(dout[t], Y_perm[r])
+
+    # experts, one at a time
+    dX_perm = np.zeros((N, d))
+    dWg = np.zeros((E, d_ff, d))
+    dWu = np.zeros((E, d_ff, d))
+    dWd = np.zeros((E, d, d_ff))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            dX_perm[lo:hi], dWg[e], dWu[e], dWd[e] = expert_ffn_backward(
+                X_perm[lo:hi], W_gate[e], W_up[e], W_down[e], dY_perm[lo:hi])
+
+    # permute (transpose of the gather)
+    dX = np.zeros((T, d))
+    for t in range(T):
+        for j in range(k):
+            if dest[t, j] >= 0:
+                dX[t] += dX_perm[dest[t, j]]
+
+    # gate weights, router
+    dl_sel = gate_weights_backward(w, dw)
+    dl = np.zeros((T, E))
+    for t in range(T):
+        for j in range(k):
+            dl[t, idx[t, j]] += dl_sel[t, j]
+    dW_r = dl.T @ _f64(X)
+    dbias = dl.sum(axis=0)
+    dX += dl @ _f64(W_r)
+    return dict(dX=dX, dW_r=dW_r, dbias=dbias, dW_gate=dWg, dW_up=dWu,
+                dW_down=dWd, idx=idx, w=w, dest=dest, offsets=offsets,
+                Y_perm=Y_perm, dw=dw, dl=dl)

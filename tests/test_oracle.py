@@ -558,3 +558,160 @@ def test_workloads_are_seeded_and_shaped():
     p = np.exp(bias.astype(np.float64))
     np.testing.assert_allclose(np.sort(p)[::-1] / p.max(),
                                np.arange(1, 33) ** -1.2, rtol=1e-5)
+
+
+# -------------------------------------------------------------- backward --
+def _fd_forward(X, W_r, b, Wg, Wu, Wd, idx, C, gating):
+    """The layer in fp64 with the selection ``idx`` held fixed and fp64
+    logits: the function whose derivatives the backward states."""
+    T, E = X.shape[0], W_r.shape[0]
+    l = np.asarray(X, np.float64) @ np.asarray(W_r, np.float64).T
+    if b is not None:
+        l = l + np.asarray(b, np.float64)
+    w = O.gate_weights(l, idx, gating)
+    a = O.assign(idx, E, C)
+    Xp = np.asarray(X, np.float64)[a["row_token"]]
+    Y = O.grouped_ffn(Xp, a["offsets"], Wg, Wu, Wd)
+    return O.combine(Y, a["dest"], w, T)
+
+
+@pytest.mark.parametrize("gating,cf,bias", [
+    (O.TOPK_THEN_SOFTMAX, None, 0.0),
+    (O.SOFTMAX_THEN_TOPK, None, 1.0),
+    (O.TOPK_THEN_SOFTMAX, 0.6, 1.5),
+])
+def test_backward_matches_central_differences(gating, cf, bias):
+    """Every coordinate of every gradient against a central difference of
+    the loss sum(dout * out), selection fixed."""
+    T, d, E, k, d_ff = 7, 6, 4, 2, 5
+    X, W_r, b, Wg, Wu, Wd = _rand_layer(T, d, E, k, d_ff, seed=71, bias_scale=bias)
+    if b is None:
+        b = np.zeros(E, np.float32)
+    X, W_r, b, Wg, Wu, Wd = (np.asarray(v, np.float64) for v in (X, W_r, b, Wg, Wu, Wd))
+    dout = np.random.default_rng(72).standard_normal((T, d))
+    g = O.moe_backward(X, W_r, b, Wg, Wu, Wd, dout, k, cf, gating)
+    C = O.capacity(T, k, E, cf)
+    if cf is not None:
+        assert (g["dest"] < 0).any()
+    params = dict(X=X, W_r=W_r, b=b, Wg=Wg, Wu=Wu, Wd=Wd)
+    names = dict(X="dX", W_r="dW_r", b="dbias", Wg="dW_gate", Wu="dW_up", Wd="dW_down")
+    h = 1e-6
+    for pname, arr in params.items():
+        fd = np.zeros_like(arr)
+        for i in np.ndindex(arr.shape):
+            old = arr[i]
+            arr[i] = old + h
+            lp = np.sum(dout * _fd_forward(**params, idx=g["idx"], C=C, gating=gating))
+            arr[i] = old - h
+            lm = np.sum(dout * _fd_forward(**params, idx=g["idx"], C=C, gating=gating))
+            arr[i] = old
+            fd[i] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g[names[pname]], fd, rtol=2e-5, atol=2e-7,
+                                   err_msg=pname)
+
+
+def _torch_layer(X, W_r, b, Wg, Wu, Wd, idx, dest, gating):
+    """Autograd reference: the layer written with torch ops (fp64), routing
+    given by ``idx`` and ``dest``; gating 1 takes the full softmax, gathers
+    the selected probabilities and renormalises them."""
+    l = X @ W_r.T + b
+    idx_t = torch.from_numpy(np.asarray(idx, np.int64))
+    if gating == O.TOPK_THEN_SOFTMAX:
+        w = torch.softmax(torch.gather(l, 1, idx_t), dim=1)
+    else:
+        p = torch.gather(torch.softmax(l, dim=1), 1, idx_t)
+        w = p / p.sum(dim=1, keepdim=True)
+    T, k = idx_t.shape
+    out = torch.zeros(T, Wd.shape[1], dtype=torch.float64)
+    for t in range(T):
+        for j in range(k):
+            if dest[t, j] >= 0:
+                e = int(idx_t[t, j])
+                x = X[t:t + 1]
+                h = torch.nn.functional.silu(x @ Wg[e].T) * (x @ Wu[e].T)
+                out[t] += w[t, j] * (h @ Wd[e].T)[0]
+    return out
+
+
+@pytest.mark.parametrize("gating,cf", [(O.TOPK_THEN_SOFTMAX, None),
+                                       (O.SOFTMAX_THEN_TOPK, 0.7)])
+def test_backward_matches_library_autograd(gating, cf):
+    T, d, E, k, d_ff = 20, 8, 5, 3, 6
+    X, W_r, b, Wg, Wu, Wd = _rand_layer(T, d, E, k, d_ff, seed=73, bias_scale=1.0)
+    dout = np.random.default_rng(74).standard_normal((T, d))
+    g = O.moe_backward(X, W_r, b, Wg, Wu, Wd, dout, k, cf, gating)
+    leaves = [torch.from_numpy(np.asarray(v, np.float64)).requires_grad_()
+              for v in (X, W_r, b, Wg, Wu, Wd)]
+    out = _torch_layer(*leaves, g["idx"], g["dest"], gating)
+    (out * torch.from_numpy(dout)).sum().backward()
+    for leaf, name in zip(leaves, ("dX", "dW_r", "dbias", "dW_gate", "dW_up", "dW_down")):
+        # the oracle's gate weights come from fp32-rounded logits
+        np.testing.assert_allclose(g[name], leaf.grad.numpy(), rtol=1e-5, atol=1e-7,
+                                   err_msg=name)
+
+
+def test_backward_single_expert_is_dense_swiglu_backward():
+    """E = 1, k = 1: every gate weight is 1, so the router gets no gradient
+    and the rest is the dense SwiGLU FFN's backward."""
+    X, W_r, b, Wg, Wu, Wd = _rand_layer(9, 8, 1, 1, 10, seed=75, bias_scale=1.0)
+    dout = np.random.default_rng(76).standard_normal((9, 8))
+    g = O.moe_backward(X, W_r, b, Wg, Wu, Wd, dout, 1)
+    assert np.all(g["dW_r"] == 0) and np.all(g["dbias"] == 0)
+    xs = [torch.from_numpy(np.asarray(v, np.float64)).requires_grad_()
+          for v in (X, Wg[0], Wu[0], Wd[0])]
+    y = torch.nn.functional.linear(
+        torch.nn.functional.silu(torch.nn.functional.linear(xs[0], xs[1]))
+        * torch.nn.functional.linear(xs[0], xs[2]), xs[3])
+    (y * torch.from_numpy(dout)).sum().backward()
+    for got, leaf in zip((g["dX"], g["dW_gate"][0], g["dW_up"][0], g["dW_down"][0]), xs):
+        np.testing.assert_allclose(got, leaf.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_backward_top1_softmax_gives_no_router_gradient():
+    """k = 1 with the softmax over the selected logits: w = 1 whatever the
+    logits, so dW_r and dbias are exactly zero."""
+    X, W_r, b, Wg, Wu, Wd = _rand_layer(15, 8, 4, 1, 6, seed=77, bias_scale=1.0)
+    dout = np.random.default_rng(78).standard_normal((15, 8))
+    g = O.moe_backward(X, W_r, b, Wg, Wu, Wd, dout, 1)
+    assert np.all(g["dl"] == 0) and np.all(g["dW_r"] == 0) and np.all(g["dbias"] == 0)
+
+
+def test_backward_identical_experts_match_dense_ffn():
+    """Identical experts, no capacity: the layer is the dense FFN for any
+    routing (the gate weights sum to 1), so the router gradient vanishes and
+    the experts' weight gradients sum to the dense FFN's."""
+    X, W_r, b, Wg, Wu, Wd = _rand_layer(16, 8, 4, 2, 6, seed=79, bias_scale=1.0)
+    Wg[:], Wu[:], Wd[:] = Wg[0], Wu[0], Wd[0]
+    dout = np.random.default_rng(80).standard_normal((16, 8))
+    for gating in (O.TOPK_THEN_SOFTMAX, O.SOFTMAX_THEN_TOPK):
+        g = O.moe_backward(X, W_r, b, Wg, Wu, Wd, dout, 2, None, gating)
+        dA, dWg, dWu, dWd = O.expert_ffn_backward(X, Wg[0], Wu[0], Wd[0], dout)
+        np.testing.assert_allclose(g["dW_r"], 0, atol=1e-12)
+        np.testing.assert_allclose(g["dbias"], 0, atol=1e-12)
+        np.testing.assert_allclose(g["dX"], dA, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(g["dW_gate"].sum(0), dWg, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(g["dW_up"].sum(0), dWu, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(g["dW_down"].sum(0), dWd, rtol=1e-10, atol=1e-12)
+
+
+def test_backward_invariants_with_drops():
+    """Each token's logit gradient sums to zero (so does dbias, and every
+    column of dW_r); a token whose copies were all dropped passes no gradient
+    through the experts and none to its logits; unused experts get zero
+    weight gradients."""
+    T, d, E, k, d_ff = 40, 8, 6, 2, 6
+    X, W_r, b, Wg, Wu, Wd = _rand_layer(T, d, E, k, d_ff, seed=81)
+    b = np.array([8, 7, -30, -30, -30, -30], np.float32)  # experts 0, 1 take everything
+    dout = np.random.default_rng(82).standard_normal((T, d))
+    g = O.moe_backward(X, W_r, b, Wg, Wu, Wd, dout, k, capacity_factor=0.9)
+    np.testing.assert_allclose(g["dl"].sum(axis=1), 0, atol=1e-12)
+    np.testing.assert_allclose(g["dbias"].sum(), 0, atol=1e-11)
+    np.testing.assert_allclose(g["dW_r"].sum(axis=0), 0, atol=1e-10)
+    gone = np.all(g["dest"] < 0, axis=1)
+    assert gone.any()
+    np.testing.assert_array_equal(g["dl"][gone], 0)
+    np.testing.assert_allclose(g["dX"][gone], 0, atol=0)
+    unused = np.diff(g["offsets"]) == 0
+    assert unused.any()
+    for name in ("dW_gate", "dW_up", "dW_down"):
+        assert np.all(g[name][unused] == 0)
