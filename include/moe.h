@@ -290,6 +290,53 @@ moe_status_t moe_forward_scaled(const moe_problem_t* p, const void* X,
                                 void* out, int32_t* stats, void* workspace,
                                 size_t ws_bytes, hipStream_t stream);
 
+/* Training: the forward pass that keeps what the backward needs, and the
+ * backward pass of the layer ("Expert를 똑같이 나눴는데도 GPU가 대기하는
+ * 이유: MoE의 토큰 쏠림", section "Unsloth와의 MoE 학습 경로": training
+ * runs the same grouped expert GEMMs; "가장 바쁜 랭크가 속도를 정합니다",
+ * section "이 기술은 무엇인가": the expert weights' gradients come back in
+ * the backward pass).  bf16 layers only (act_dtype = w_dtype = MOE_BF16,
+ * else MOE_ERR_UNSUPPORTED); rows bound R = moe_rows_bound(p) must satisfy
+ * R + 63 E < 2^22 - 64 (else MOE_ERR_UNSUPPORTED).
+ *
+ * moe_forward_train: moe_forward (same arguments, same out and stats) that
+ * also fills `state` (device, >= moe_train_state_bytes(p) bytes, else
+ * MOE_ERR_INVALID_ARG): routing, assignment, X_perm and the experts'
+ * G = X Wg^T, U = X Wu^T, H (bf16) and Y_perm (fp32).  The state's layout is
+ * private to the library; it stays valid until the caller reuses it.
+ * workspace >= moe_workspace_bytes(p) bytes.
+ *
+ * moe_backward: gradients of a loss L given dout = dL/d(out) [T, d_model]
+ * fp32, with the routing of the forward that wrote `state` held fixed (the
+ * top-k selection and the capacity assignment are piecewise constant):
+ *   dX [T, d_model], dW_r [E, d_model], dbias [E] (NULL: not computed),
+ *   dW_gate, dW_up [E, d_ff, d_model], dW_down [E, d_model, d_ff],
+ * all fp32, written (not accumulated).  X, W_r and the expert weights must
+ * be the forward's.  The gate weights are the softmax of the selected
+ * logits in both gating orders, so dl = w (dw - <w, dw>) at the selected
+ * experts and 0 elsewhere, with dw[t,j] = <dout[t], Y_perm[dest[t,j]]>
+ * (0 for a dropped copy).  The expert GEMMs take bf16 operands (G, U, H,
+ * w dout, dG, dU) with fp32 accumulation; every sum has a fixed order.
+ * workspace >= moe_backward_workspace_bytes(p) bytes (it holds transposed
+ * copies of the expert weights).  T = 0: nothing is written. */
+size_t moe_train_state_bytes(const moe_problem_t* p);
+moe_status_t moe_forward_train(const moe_problem_t* p, const void* X,
+                               const float* W_r, const float* bias,
+                               const void* W_gate, const void* W_up,
+                               const void* W_down, void* out, int32_t* stats,
+                               void* state, size_t state_bytes,
+                               void* workspace, size_t ws_bytes,
+                               hipStream_t stream);
+size_t moe_backward_workspace_bytes(const moe_problem_t* p);
+moe_status_t moe_backward(const moe_problem_t* p, const void* X,
+                          const float* W_r, const void* W_gate,
+                          const void* W_up, const void* W_down,
+                          const void* state, size_t state_bytes,
+                          const float* dout, float* dX, float* dW_r,
+                          float* dbias, float* dW_gate, float* dW_up,
+                          float* dW_down, void* workspace, size_t ws_bytes,
+                          hipStream_t stream);
+
 /* Static string naming a status code. */
 const char* moe_status_string(moe_status_t s);
 

@@ -1,4 +1,5 @@
-"""MI355X (gfx950) forward pass of one sparsely-gated MoE FFN layer.
+"""MI355X (gfx950) forward and backward passes of one sparsely-gated MoE FFN
+layer.
 
 The layer runs in the HIP library libmoe_mi355x.so behind the C ABI of
 include/moe.h; this package is its ctypes binding (``binding``), the build
@@ -13,5 +14,6 @@ from .binding import (MOE_BF16, MOE_F32, MOE_SOFTMAX_THEN_TOPK,  # noqa: F401
                       moe_permute, moe_route, moe_route_stats,
                       forward_stats_workspace_bytes, route_stats_workspace_bytes,
                       permute_workspace_bytes, problem, route_workspace_bytes,
-                      rows_bound,
-                      workspace_bytes)
+                      rows_bound, workspace_bytes,
+                      train_state_bytes, backward_workspace_bytes,
+                      moe_forward_train, moe_backward)

@@ -33,7 +33,9 @@ SYMBOLS = ("moe_capacity", "moe_rows_bound", "moe_route_workspace_bytes",
            "moe_forward", "moe_route_stats_workspace_bytes", "moe_route_stats",
            "moe_forward_stats_workspace_bytes", "moe_forward_stats",
            "moe_forward_shared_workspace_bytes", "moe_forward_shared",
-           "moe_grouped_ffn_scaled", "moe_forward_scaled", "moe_status_string")
+           "moe_grouped_ffn_scaled", "moe_forward_scaled",
+           "moe_train_state_bytes", "moe_forward_train",
+           "moe_backward_workspace_bytes", "moe_backward", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -95,6 +97,12 @@ def load(path: str = LIB_PATH):
                                                   vp, sz, st]),
         "moe_forward_scaled": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp,
                                               vp, vp, sz, st]),
+        "moe_train_state_bytes": (sz, [P]),
+        "moe_forward_train": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp,
+                                             vp, sz, vp, sz, st]),
+        "moe_backward_workspace_bytes": (sz, [P]),
+        "moe_backward": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, sz, vp, vp,
+                                        vp, vp, vp, vp, vp, vp, sz, st]),
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -426,3 +434,66 @@ def moe_forward_scaled(p, X, W_r, bias, W_gate, W_up, W_down, w_scales,
         _ptr(stats, torch.int32, "stats"), _ptr(ws), ws.numel(), _stream(stream)),
         "moe_forward_scaled")
     return out
+
+
+def train_state_bytes(p: Problem) -> int:
+    return int(load().moe_train_state_bytes(ctypes.byref(p)))
+
+
+def backward_workspace_bytes(p: Problem) -> int:
+    return int(load().moe_backward_workspace_bytes(ctypes.byref(p)))
+
+
+def moe_forward_train(p, X, W_r, bias, W_gate, W_up, W_down, out=None,
+                      stats=None, state=None, workspace=None, stream=None):
+    """moe_forward that also fills the state moe_backward needs.
+    Returns (out, state)."""
+    torch = _torch()
+    dev = X.device
+    if out is None:
+        out = torch.empty((p.T, p.d_model), dtype=_out_dtype(p), device=dev)
+    if state is None:
+        state = torch.empty(max(train_state_bytes(p), 1), dtype=torch.uint8,
+                            device=dev)
+    ws = _workspace(workspace_bytes(p), dev, workspace)
+    wt = _act_dtype(p)
+    _check(load().moe_forward_train(
+        ctypes.byref(p), _ptr(X, wt, "X"), _ptr(W_r, torch.float32, "W_r"),
+        _ptr(bias, torch.float32, "bias"), _ptr(W_gate, wt, "W_gate"),
+        _ptr(W_up, wt, "W_up"), _ptr(W_down, wt, "W_down"),
+        _ptr(out, _out_dtype(p), "out"), _ptr(stats, torch.int32, "stats"),
+        _ptr(state, torch.uint8, "state"), state.numel(), _ptr(ws), ws.numel(),
+        _stream(stream)), "moe_forward_train")
+    return out, state
+
+
+def moe_backward(p, X, W_r, W_gate, W_up, W_down, state, dout, grads=None,
+                 with_dbias=True, workspace=None, stream=None):
+    """Gradients of the layer given dout [T, d_model] fp32 and the state of
+    moe_forward_train.  Returns a dict dX, dW_r, dbias (None without
+    with_dbias), dW_gate, dW_up, dW_down (fp32), reusing ``grads`` when
+    given."""
+    torch = _torch()
+    dev = X.device
+    f32 = torch.float32
+    shapes = dict(dX=(p.T, p.d_model), dW_r=(p.E, p.d_model), dbias=(p.E,),
+                  dW_gate=(p.E, p.d_ff, p.d_model), dW_up=(p.E, p.d_ff, p.d_model),
+                  dW_down=(p.E, p.d_model, p.d_ff))
+    g = dict(grads) if grads is not None else {}
+    for name, shp in shapes.items():
+        if name == "dbias" and not with_dbias:
+            g[name] = None
+        elif g.get(name) is None:
+            g[name] = torch.empty(shp, dtype=f32, device=dev)
+    ws = _workspace(backward_workspace_bytes(p), dev, workspace)
+    wt = _act_dtype(p)
+    _check(load().moe_backward(
+        ctypes.byref(p), _ptr(X, wt, "X"), _ptr(W_r, f32, "W_r"),
+        _ptr(W_gate, wt, "W_gate"), _ptr(W_up, wt, "W_up"),
+        _ptr(W_down, wt, "W_down"), _ptr(state, torch.uint8, "state"),
+        state.numel(), _ptr(dout, f32, "dout"), _ptr(g["dX"], f32, "dX"),
+        _ptr(g["dW_r"], f32, "dW_r"), _ptr(g["dbias"], f32, "dbias"),
+        _ptr(g["dW_gate"], f32, "dW_gate"), _ptr(g["dW_up"], f32, "dW_up"),
+        _ptr(g["dW_down"], f32, "dW_down"), _ptr(ws), ws.numel(),
+        _stream(stream)), "moe_backward")
+    return g

@@ -21,6 +21,7 @@ OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
 
 SOURCES = ["router.hip", "permute.hip", "grouped_gemm.hip", "combine.hip", "dense_offsets.hip",
+           "backward.hip",
            "moe_api.cpp"]
 ARCH = "gfx950"
 

@@ -180,6 +180,29 @@ struct GemmCfg {
   static constexpr int LDS_BYTES = NS * STAGE + 1040;  // + the tile prefix
 };
 
+// Kernel arguments.  Modes 0-2 (rows grouped by expert):
+//   A [R, K] bf16 rows; B0/B1 [E, N, K] bf16 (or FP8 codes); offsets = the
+//   experts' row offsets [E + 1]; mt_prefix = tile schedule [E + 1].
+// Mode 3 (weight gradient, C_e = A_e B_e^T with K = the expert's rows):
+//   A [M, lda] and B0 [N, ldb] bf16 hold the transposed rows of all experts,
+//   expert e in columns [offsets[e], offsets[e + 1]) (a multiple of 64 wide,
+//   zero-padded); C rows m < msplit go to C [E, msplit, N], the others to
+//   C1 [E, M - msplit, N] (fp32).
+struct GemmArgs {
+  const uint16_t* A;
+  const void* B0;
+  const void* B1;
+  int N, K, E;
+  const int32_t* offsets;
+  const int32_t* mt_prefix;
+  void* C;
+  const float* scales;  // FP8 weights: [E, 3]
+  uint16_t* G;          // mode 1: G out; mode 2: G in ([R, N] bf16)
+  uint16_t* U;          // mode 1: U out; mode 2: U in
+  int M, lda, ldb, msplit;  // mode 3
+  void* C1;                 // mode 3
+};
+
 // A [R, K] bf16 rows; B0/B1 [E, N, K] bf16, or FP8 E4M3 codes when BF8
 // (gate/up, or down with B1 unused).  GATEUP: C = H bf16 [R, N].  Otherwise
 // C = Y fp32 [R, N].  With FP8 weights, scales [E, 3] (gate, up, down) scale
@@ -187,12 +210,24 @@ struct GemmCfg {
 // bf16 for the MFMAs.  BAUX: cache-policy
 // bits of the weight loads (kNonTemporal when each weight tile is read by
 // about one workgroup: the loads then stream past the caches).
-template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS, int BAUX, bool BF8>
-__global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(
-    const uint16_t* __restrict__ A, const void* __restrict__ B0,
-    const void* __restrict__ B1, int N, int K, int E,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ mt_prefix,
-    void* __restrict__ Cout, const float* __restrict__ scales) {
+// MODE 0: the forward FFN.  MODE 1 (GATEUP, training forward): also stores
+// G = A B0^T and U = A B1^T in bf16.  MODE 2 (not GATEUP, backward of the
+// down projection): the accumulator is dH; the epilogue applies the SwiGLU
+// backward with the saved G and U and stores dG | dU as bf16 [R, 2N].
+// MODE 3: weight gradient (see GemmArgs).
+template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS, int BAUX, bool BF8,
+          int MODE>
+__global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const GemmArgs g) {
+  const uint16_t* __restrict__ A = g.A;
+  const void* __restrict__ B0 = g.B0;
+  const void* __restrict__ B1 = g.B1;
+  const int N = g.N, E = g.E;
+  const int32_t* __restrict__ offsets = g.offsets;
+  const int32_t* __restrict__ mt_prefix = g.mt_prefix;
+  void* __restrict__ Cout = g.C;
+  const float* __restrict__ scales = g.scales;
+  static_assert(MODE != 1 || GATEUP, "mode 1 is a gate/up mode");
+  static_assert((MODE != 2 && MODE != 3) || (!GATEUP && !BF8), "modes 2, 3: one bf16 B");
   using Cfg = GemmCfg<MW, NW, TM, TN, GATEUP, BK, NS, BF8>;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, NB = Cfg::NB, IPW = Cfg::IPW;
   constexpr int NWAVES = Cfg::NWAVES, STAGE = Cfg::STAGE, LW = Cfg::LW;
@@ -206,36 +241,68 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
-  for (int i = tid; i <= E; i += Cfg::NT) s_pref[i] = mt_prefix[i];
-  __syncthreads();
-
   // ---- which tile is mine --------------------------------------------------
+  // e, the tile's first row (m_start: of X_perm / H; mode 3: of A) and
+  // column, its row and column counts, K of the tile, and the element
+  // offsets of its first A and B elements.
+  int e, m_start, rows, n0, ncols, K;
+  int64_t a_off, b_off;
+  uint32_t kbytes, kbytesB;  // A and B row strides in bytes
   const int n_nt = (N + BN - 1) / BN;
-  const int total = s_pref[E] * n_nt;
-  const int q = (total + kXcds - 1) / kXcds;
-  const int slot = blockIdx.x / kXcds;
-  if (slot >= q) return;
-  const int logical = (blockIdx.x % kXcds) * q + slot;
-  if (logical >= total) return;
-  int lo = 0, hi = E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (s_pref[mid] * n_nt <= logical) lo = mid; else hi = mid;
+  if constexpr (MODE == 3) {
+    const int n_mt = (g.M + BM - 1) / BM;
+    const int per_e = n_mt * n_nt;
+    const int total = E * per_e;
+    const int q = (total + kXcds - 1) / kXcds;
+    const int slot = blockIdx.x / kXcds;
+    if (slot >= q) return;
+    const int logical = (blockIdx.x % kXcds) * q + slot;
+    if (logical >= total) return;
+    e = logical / per_e;
+    const int local = logical - e * per_e;
+    const int n_t = local / n_mt, m_t = local - n_t * n_mt;
+    m_start = m_t * BM;
+    rows = min(BM, g.M - m_start);
+    n0 = n_t * BN;
+    ncols = min(BN, N - n0);
+    const int k0 = offsets[e];
+    K = offsets[e + 1] - k0;
+    a_off = (int64_t)m_start * g.lda + k0;
+    b_off = (int64_t)n0 * g.ldb + k0;
+    kbytes = (uint32_t)g.lda * 2u;
+    kbytesB = (uint32_t)g.ldb * 2u;
+  } else {
+    for (int i = tid; i <= E; i += Cfg::NT) s_pref[i] = mt_prefix[i];
+    __syncthreads();
+    const int total = s_pref[E] * n_nt;
+    const int q = (total + kXcds - 1) / kXcds;
+    const int slot = blockIdx.x / kXcds;
+    if (slot >= q) return;
+    const int logical = (blockIdx.x % kXcds) * q + slot;
+    if (logical >= total) return;
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pref[mid] * n_nt <= logical) lo = mid; else hi = mid;
+    }
+    e = lo;
+    const int mt_e = s_pref[e + 1] - s_pref[e];
+    const int local = logical - s_pref[e] * n_nt;
+    const int n_t = local / mt_e, m_t = local % mt_e;
+    const int row_end = offsets[e + 1];
+    m_start = offsets[e] + m_t * BM;
+    rows = min(BM, row_end - m_start);
+    n0 = n_t * BN;
+    ncols = min(BN, N - n0);
+    K = g.K;
+    a_off = (int64_t)m_start * K;
+    b_off = ((int64_t)e * N + n0) * K;
+    kbytes = (uint32_t)K * 2u;
+    kbytesB = (uint32_t)K * (BF8 ? 1u : 2u);
   }
-  const int e = lo;
-  const int mt_e = s_pref[e + 1] - s_pref[e];
-  const int local = logical - s_pref[e] * n_nt;
-  const int n_t = local / mt_e, m_t = local % mt_e;
-  const int row_end = offsets[e + 1];
-  const int m_start = offsets[e] + m_t * BM;
-  const int rows = min(BM, row_end - m_start);
-  const int n0 = n_t * BN;
-  const int ncols = min(BN, N - n0);
 
-  const uint32_t kbytes = (uint32_t)K * 2u;                  // A row
-  const uint32_t kbytesB = (uint32_t)K * (BF8 ? 1u : 2u);    // B row
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(A + (int64_t)m_start * K, (uint32_t)rows * kbytes);
-  const int64_t boff = ((int64_t)e * N + n0) * K * (BF8 ? 1 : 2);  // bytes
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(A + a_off, (uint32_t)rows * kbytes);
+  const int64_t boff = b_off * (BF8 ? 1 : 2);  // bytes
   const __amdgpu_buffer_rsrc_t rB0 =
       make_rsrc(static_cast<const char*>(B0) + boff, (uint32_t)ncols * kbytesB);
   const __amdgpu_buffer_rsrc_t rB1 =
@@ -392,9 +459,61 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(
         for (int r = 0; r < 16; ++r) {
           const int row = rbase + mi * 32 + 8 * (r >> 2) + (r & 3);
           if (row < rows) {
-            const float g = acc[mi][nj][r], u = acc[mi][nj + TN][r];
-            const float h = g / (1.f + __expf(-g)) * u;
-            H[(int64_t)(m_start + row) * N + n0 + col] = f32_to_bf16_bits(h);
+            const float gv = acc[mi][nj][r], u = acc[mi][nj + TN][r];
+            const float h = gv / (1.f + __expf(-gv)) * u;
+            const int64_t o = (int64_t)(m_start + row) * N + n0 + col;
+            H[o] = f32_to_bf16_bits(h);
+            if constexpr (MODE == 1) {
+              g.G[o] = f32_to_bf16_bits(gv);
+              g.U[o] = f32_to_bf16_bits(u);
+            }
+          }
+        }
+    }
+  } else if constexpr (MODE == 2) {
+    // SwiGLU backward: dG = dH U silu'(G), dU = dH silu(G) with
+    // silu'(z) = s (1 + z (1 - s)), s = 1 / (1 + e^-z)
+    uint16_t* dGU = static_cast<uint16_t*>(Cout);
+#pragma unroll
+    for (int nj = 0; nj < TN; ++nj) {
+      const int col = wn * TN * 32 + nj * 32 + col_l;
+      if (col >= ncols) continue;
+#pragma unroll
+      for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rbase + mi * 32 + 8 * (r >> 2) + (r & 3);
+          if (row < rows) {
+            const int64_t o = (int64_t)(m_start + row) * N + n0 + col;
+            const float gv = bf16_bits_to_f32(g.G[o]), u = bf16_bits_to_f32(g.U[o]);
+            const float sg = 1.f / (1.f + __expf(-gv));
+            const float dh = acc[mi][nj][r];
+            const float dgv = dh * u * (sg * (1.f + gv * (1.f - sg)));
+            const float du = dh * (gv * sg);
+            const int64_t o2 = (int64_t)(m_start + row) * (2 * N) + n0 + col;
+            dGU[o2] = f32_to_bf16_bits(dgv);
+            dGU[o2 + N] = f32_to_bf16_bits(du);
+          }
+        }
+    }
+  } else if constexpr (MODE == 3) {
+    float* C0 = static_cast<float*>(Cout);
+    float* C1 = static_cast<float*>(g.C1);
+    const int ms = g.msplit, M = g.M;
+#pragma unroll
+    for (int nj = 0; nj < TN; ++nj) {
+      const int col = wn * TN * 32 + nj * 32 + col_l;
+      if (col >= ncols) continue;
+#pragma unroll
+      for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rbase + mi * 32 + 8 * (r >> 2) + (r & 3);
+          if (row < rows) {
+            const int m = m_start + row;
+            float* dst = m < ms ? C0 + ((int64_t)e * ms + m) * N
+                                : C1 + ((int64_t)e * (M - ms) + (m - ms)) * N;
+            dst[n0 + col] = acc[mi][nj][r];
           }
         }
     }
@@ -461,28 +580,50 @@ __global__ __launch_bounds__(256) void ffn_f32_down_kernel(
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Modes 0-2: R = rows bound (grid upper bound).  Mode 3: a.M rows of C per
+// expert, every (expert, m-tile, n-tile) is a tile.
+template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS, int BAUX, bool BF8,
+          int MODE>
+hipError_t launch_gemm_args(const GemmArgs& a, int64_t R, hipStream_t stream) {
+  using Cfg = GemmCfg<MW, NW, TM, TN, GATEUP, BK, NS, BF8>;
+  auto kern = grouped_gemm_kernel<MW, NW, TM, TN, GATEUP, BK, NS, BAUX, BF8, MODE>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+      Cfg::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
+  const int64_t n_nt = (a.N + Cfg::BN - 1) / Cfg::BN;
+  int64_t tiles;
+  if (MODE == 3) {
+    tiles = (int64_t)a.E * ((a.M + Cfg::BM - 1) / Cfg::BM) * n_nt;
+  } else {
+    // upper bound on M-tiles: every expert may add one partial tile
+    const int64_t mt_max = (R + Cfg::BM - 1) / Cfg::BM + std::min<int64_t>(a.E, R);
+    tiles = mt_max * n_nt;
+  }
+  const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::LDS_BYTES, stream, a);
+  return hipGetLastError();
+}
+
 template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS, int BAUX, bool BF8 = false>
 hipError_t launch_gemm(const void* A, const void* B0, const void* B1, int N,
                        int K, int E, int64_t R, const int32_t* offsets,
                        const int32_t* mt_prefix, void* C, hipStream_t stream,
                        const float* scales = nullptr) {
-  using Cfg = GemmCfg<MW, NW, TM, TN, GATEUP, BK, NS, BF8>;
-  auto kern = grouped_gemm_kernel<MW, NW, TM, TN, GATEUP, BK, NS, BAUX, BF8>;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-      Cfg::LDS_BYTES);
-  if (attr != hipSuccess) return attr;
-  // upper bound on M-tiles: every expert may add one partial tile
-  const int64_t mt_max = (R + Cfg::BM - 1) / Cfg::BM + std::min<int64_t>(E, R);
-  const int64_t n_nt = (N + Cfg::BN - 1) / Cfg::BN;
-  const int64_t tiles = mt_max * n_nt;
-  const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
-  if (grid == 0) return hipSuccess;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::LDS_BYTES, stream,
-                     static_cast<const uint16_t*>(A), B0, B1, N, K, E, offsets, mt_prefix, C,
-                     scales);
-  return hipGetLastError();
+  GemmArgs a{};
+  a.A = static_cast<const uint16_t*>(A);
+  a.B0 = B0;
+  a.B1 = B1;
+  a.N = N;
+  a.K = K;
+  a.E = E;
+  a.offsets = offsets;
+  a.mt_prefix = mt_prefix;
+  a.C = C;
+  a.scales = scales;
+  return launch_gemm_args<MW, NW, TM, TN, GATEUP, BK, NS, BAUX, BF8, 0>(a, R, stream);
 }
 
 }  // namespace
@@ -570,6 +711,105 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
   err = launch_gemm<2, MOE_NW, 4, 4 / MOE_NW, true, MOE_BK, MOE_NS, 0>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
   if (err != hipSuccess) return err;
   return launch_gemm<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, 0>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
+}
+
+}  // namespace moe
+
+// ---- training forward and backward -----------------------------------------
+namespace moe {
+
+hipError_t launch_grouped_ffn_train(const void* X_perm, const int32_t* offsets,
+                                    const void* W_gate, const void* W_up, const void* W_down,
+                                    int64_t R, int d, int E, int d_ff, int rows_per_expert,
+                                    int32_t* mt_prefix, bool prefix_ready, void* H, void* G,
+                                    void* U, float* Y_perm, hipStream_t stream) {
+  const int bm = ffn_tile_rows(true, rows_per_expert, false);
+  if (R == 0) return hipSuccess;
+  hipError_t err;
+  if (!prefix_ready) {
+    ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, bm, mt_prefix);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  GemmArgs a{};
+  a.A = static_cast<const uint16_t*>(X_perm);
+  a.B0 = W_gate;
+  a.B1 = W_up;
+  a.N = d_ff;
+  a.K = d;
+  a.E = E;
+  a.offsets = offsets;
+  a.mt_prefix = mt_prefix;
+  a.C = H;
+  a.G = static_cast<uint16_t*>(G);
+  a.U = static_cast<uint16_t*>(U);
+  if (bm == 32) {
+    err = launch_gemm_args<1, MOE_SNW, 1, 1, true, MOE_SBK, MOE_SNS, MOE_SBAUX, false, 1>(a, R, stream);
+    if (err != hipSuccess) return err;
+    return launch_gemm<1, MOE_SNW, 1, 1, false, MOE_SBK, MOE_SNS, MOE_SBAUX>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
+  }
+  if (rows_per_expert <= MOE_BNT_ROWS) {
+    err = launch_gemm_args<2, MOE_NW, 4, 4 / MOE_NW, true, MOE_BK, MOE_NS, kNonTemporal, false, 1>(a, R, stream);
+    if (err != hipSuccess) return err;
+    return launch_gemm<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, kNonTemporal>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
+  }
+  err = launch_gemm_args<2, MOE_NW, 4, 4 / MOE_NW, true, MOE_BK, MOE_NS, 0, false, 1>(a, R, stream);
+  if (err != hipSuccess) return err;
+  return launch_gemm<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, 0>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
+}
+
+hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const void* WdT,
+                            const void* WguT, const void* G, const void* U, int64_t R, int d,
+                            int E, int d_ff, int rows_per_expert, int32_t* mt_prefix,
+                            void* dGU, float* dX_perm, hipStream_t stream) {
+  const int bm = ffn_tile_rows(true, rows_per_expert, false);
+  if (R == 0) return hipSuccess;
+  ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, bm, mt_prefix);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // dH = dY_perm Wd (B = Wd^T [E, d_ff, d]) -> SwiGLU backward -> dG | dU
+  GemmArgs a{};
+  a.A = static_cast<const uint16_t*>(dY_perm);
+  a.B0 = WdT;
+  a.N = d_ff;
+  a.K = d;
+  a.E = E;
+  a.offsets = offsets;
+  a.mt_prefix = mt_prefix;
+  a.C = dGU;
+  a.G = const_cast<uint16_t*>(static_cast<const uint16_t*>(G));
+  a.U = const_cast<uint16_t*>(static_cast<const uint16_t*>(U));
+  // dX_perm = dG Wg + dU Wu = [dG | dU] [Wg ; Wu] (B = [Wg^T | Wu^T] [E, d, 2 d_ff])
+  if (bm == 32) {
+    err = launch_gemm_args<1, MOE_SNW, 1, 1, false, MOE_SBK, MOE_SNS, MOE_SBAUX, false, 2>(a, R, stream);
+    if (err != hipSuccess) return err;
+    return launch_gemm<1, MOE_SNW, 1, 1, false, MOE_SBK, MOE_SNS, MOE_SBAUX>(dGU, WguT, nullptr, d, 2 * d_ff, E, R, offsets, mt_prefix, dX_perm, stream);
+  }
+  if (rows_per_expert <= MOE_BNT_ROWS) {
+    err = launch_gemm_args<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, kNonTemporal, false, 2>(a, R, stream);
+    if (err != hipSuccess) return err;
+    return launch_gemm<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, kNonTemporal>(dGU, WguT, nullptr, d, 2 * d_ff, E, R, offsets, mt_prefix, dX_perm, stream);
+  }
+  err = launch_gemm_args<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, 0, false, 2>(a, R, stream);
+  if (err != hipSuccess) return err;
+  return launch_gemm<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, 0>(dGU, WguT, nullptr, d, 2 * d_ff, E, R, offsets, mt_prefix, dX_perm, stream);
+}
+
+hipError_t launch_wgrad(const void* AT, int lda, int M, const void* BT, int ldb, int N,
+                        const int32_t* poff, int E, int msplit, float* C0, float* C1,
+                        hipStream_t stream) {
+  GemmArgs a{};
+  a.A = static_cast<const uint16_t*>(AT);
+  a.B0 = BT;
+  a.N = N;
+  a.E = E;
+  a.offsets = poff;
+  a.M = M;
+  a.lda = lda;
+  a.ldb = ldb;
+  a.msplit = msplit;
+  a.C = C0;
+  a.C1 = C1;
+  return launch_gemm_args<2, 4, 4, 2, false, 64, 2, 0, false, 3>(a, 0, stream);
 }
 
 }  // namespace moe

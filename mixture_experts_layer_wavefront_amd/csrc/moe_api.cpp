@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 
@@ -155,6 +156,74 @@ hipError_t enqueue_routed(const moe_problem_t* p, const void* X, const float* W_
   return moe::launch_grouped_ffn(x_perm, bf, offsets, W_gate, W_up, W_down, moe_rows_bound(p),
                                  p->d_model, p->E, p->d_ff, mean_rows_per_expert(p), y_perm,
                                  ws + L.ffn_scratch, mt_prefix != nullptr, stream, w_scales);
+}
+
+// ---- training ---------------------------------------------------------------
+// Transposed-row width of the weight-gradient operands: every expert's rows
+// padded to a multiple of 64, for any routing (at most R + 63 E).
+int64_t bwd_ld(const moe_problem_t* p) {
+  return (moe_rows_bound(p) + 63 * (int64_t)p->E + 63) / 64 * 64;
+}
+
+// Training supports bf16 layers; the weight-gradient tiles address 256 rows
+// of the transposed operands with one 32-bit buffer range.
+moe_status_t validate_train(const moe_problem_t* p) {
+  const moe_status_t st = validate(p);
+  if (st != MOE_OK) return st;
+  if (!is_bf16(p)) return MOE_ERR_UNSUPPORTED;
+  if (bwd_ld(p) >= (1 << 22)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// What moe_forward_train keeps for moe_backward.
+struct TrainState {
+  size_t topk_idx, topk_w, stats, dest_row, row_token, x_perm, g, u, h, y_perm, total;
+};
+
+TrainState train_state_layout(const moe_problem_t* p) {
+  const size_t Tk = (size_t)p->T * p->top_k;
+  const size_t R = (size_t)moe_rows_bound(p);
+  const size_t d = p->d_model, dff = p->d_ff;
+  TrainState S{};
+  size_t o = 0;
+  S.topk_idx = o; o += a256(Tk * 4);
+  S.topk_w = o; o += a256(Tk * 4);
+  S.stats = o; o += a256((size_t)(2 * p->E + 2) * 4);
+  S.dest_row = o; o += a256(Tk * 4);
+  S.row_token = o; o += a256(R * 4);
+  S.x_perm = o; o += a256(R * d * 2);
+  S.g = o; o += a256(R * dff * 2);
+  S.u = o; o += a256(R * dff * 2);
+  S.h = o; o += a256(R * dff * 2);
+  S.y_perm = o; o += a256(R * d * 4);
+  S.total = o;
+  return S;
+}
+
+struct BackwardLayout {
+  size_t wdT, wguT, dy, dgu, dxp, dl, poff, mtp, t1, t2, total;
+  int ld;
+};
+
+BackwardLayout backward_layout(const moe_problem_t* p) {
+  const size_t Tk = (size_t)p->T * p->top_k;
+  const size_t R = (size_t)moe_rows_bound(p);
+  const size_t d = p->d_model, dff = p->d_ff, E = p->E;
+  BackwardLayout B{};
+  B.ld = (int)bwd_ld(p);
+  size_t o = 0;
+  B.wdT = o; o += a256(E * dff * d * 2);
+  B.wguT = o; o += a256(E * d * 2 * dff * 2);
+  B.dy = o; o += a256(R * d * 2);
+  B.dgu = o; o += a256(R * 2 * dff * 2);
+  B.dxp = o; o += a256(R * d * 4);
+  B.dl = o; o += a256(Tk * 4);
+  B.poff = o; o += a256((E + 1) * 4);
+  B.mtp = o; o += a256((E + 1) * 4);
+  B.t1 = o; o += a256(std::max(d, 2 * dff) * (size_t)B.ld * 2);
+  B.t2 = o; o += a256(std::max(dff, d) * (size_t)B.ld * 2);
+  B.total = o;
+  return B;
 }
 
 }  // namespace
@@ -416,6 +485,132 @@ moe_status_t moe_forward_scaled(const moe_problem_t* p, const void* X, const flo
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_combine(r.y_perm, r.dest_row, r.topk_w, p->T, p->d_model, p->top_k,
                           nullptr, out_bf16(p), out, stream);
+  return hip_status(e);
+}
+
+size_t moe_train_state_bytes(const moe_problem_t* p) {
+  if (validate_train(p) != MOE_OK) return 0;
+  return train_state_layout(p).total;
+}
+
+moe_status_t moe_forward_train(const moe_problem_t* p, const void* X, const float* W_r,
+                               const float* bias, const void* W_gate, const void* W_up,
+                               const void* W_down, void* out, int32_t* stats, void* state,
+                               size_t state_bytes, void* workspace, size_t ws_bytes,
+                               hipStream_t stream) {
+  moe_status_t st = validate_train(p);
+  if (st != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;
+  if (!X || !W_r || !W_gate || !W_up || !W_down || !out) return MOE_ERR_INVALID_ARG;
+  const TrainState S = train_state_layout(p);
+  if (!state || state_bytes < S.total) return MOE_ERR_INVALID_ARG;
+  const ForwardLayout L = forward_layout(p);
+  if (!workspace || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  char* sb = static_cast<char*>(state);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* topk_idx = reinterpret_cast<int32_t*>(sb + S.topk_idx);
+  float* topk_w = reinterpret_cast<float*>(sb + S.topk_w);
+  int32_t* st_buf = reinterpret_cast<int32_t*>(sb + S.stats);
+  int32_t* dest_row = reinterpret_cast<int32_t*>(sb + S.dest_row);
+  int32_t* row_token = reinterpret_cast<int32_t*>(sb + S.row_token);
+  float* y_perm = reinterpret_cast<float*>(sb + S.y_perm);
+  const int rows = mean_rows_per_expert(p);
+  hipError_t e = moe::launch_route(X, true, W_r, bias, p->T, p->d_model, p->E, p->top_k,
+                                   (int)p->gating, topk_idx, topk_w, ws + L.route_scratch,
+                                   nullptr, stream);
+  const int bm = moe::ffn_tile_rows(true, rows, false);
+  int32_t* mt_prefix = reinterpret_cast<int32_t*>(ws + L.ffn_scratch);
+  if (e == hipSuccess)
+    e = moe::launch_permute(X, true, topk_idx, p->T, p->d_model, p->E, p->top_k,
+                            capacity_int(p), st_buf, st_buf + p->E, st_buf + 2 * p->E + 1,
+                            dest_row, row_token, sb + S.x_perm, ws + L.perm_scratch, mt_prefix,
+                            bm, stream);
+  if (e == hipSuccess)
+    e = moe::launch_grouped_ffn_train(sb + S.x_perm, st_buf + p->E, W_gate, W_up, W_down,
+                                      moe_rows_bound(p), p->d_model, p->E, p->d_ff, rows,
+                                      mt_prefix, true, sb + S.h, sb + S.g, sb + S.u, y_perm,
+                                      stream);
+  if (e == hipSuccess)
+    e = moe::launch_combine(y_perm, dest_row, topk_w, p->T, p->d_model, p->top_k, nullptr,
+                            out_bf16(p), out, stream);
+  if (e == hipSuccess && stats)
+    e = hipMemcpyAsync(stats, st_buf, (size_t)(2 * p->E + 2) * 4, hipMemcpyDeviceToDevice,
+                       stream);
+  return hip_status(e);
+}
+
+size_t moe_backward_workspace_bytes(const moe_problem_t* p) {
+  if (validate_train(p) != MOE_OK) return 0;
+  return backward_layout(p).total;
+}
+
+moe_status_t moe_backward(const moe_problem_t* p, const void* X, const float* W_r,
+                          const void* W_gate, const void* W_up, const void* W_down,
+                          const void* state, size_t state_bytes, const float* dout, float* dX,
+                          float* dW_r, float* dbias, float* dW_gate, float* dW_up,
+                          float* dW_down, void* workspace, size_t ws_bytes,
+                          hipStream_t stream) {
+  moe_status_t st = validate_train(p);
+  if (st != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;
+  if (!X || !W_r || !W_gate || !W_up || !W_down || !dout || !dX || !dW_r || !dW_gate ||
+      !dW_up || !dW_down)
+    return MOE_ERR_INVALID_ARG;
+  const TrainState S = train_state_layout(p);
+  if (!state || state_bytes < S.total) return MOE_ERR_INVALID_ARG;
+  const BackwardLayout B = backward_layout(p);
+  if (!workspace || ws_bytes < B.total) return MOE_ERR_WORKSPACE;
+  const char* sb = static_cast<const char*>(state);
+  char* ws = static_cast<char*>(workspace);
+  const int T = p->T, d = p->d_model, E = p->E, k = p->top_k, dff = p->d_ff;
+  const int64_t R = moe_rows_bound(p);
+  const int32_t* topk_idx = reinterpret_cast<const int32_t*>(sb + S.topk_idx);
+  const float* topk_w = reinterpret_cast<const float*>(sb + S.topk_w);
+  const int32_t* offsets = reinterpret_cast<const int32_t*>(sb + S.stats) + E;
+  const int32_t* dest_row = reinterpret_cast<const int32_t*>(sb + S.dest_row);
+  const float* y_perm = reinterpret_cast<const float*>(sb + S.y_perm);
+  float* dl = reinterpret_cast<float*>(ws + B.dl);
+  int32_t* poff = reinterpret_cast<int32_t*>(ws + B.poff);
+  int32_t* mtp = reinterpret_cast<int32_t*>(ws + B.mtp);
+  float* dxp = reinterpret_cast<float*>(ws + B.dxp);
+
+  // transposed weights: Wd^T [E, d_ff, d], [Wg^T | Wu^T] [E, d, 2 d_ff]
+  hipError_t e = moe::launch_transpose_weights(W_down, E, d, dff, ws + B.wdT, d, 0, stream);
+  if (e == hipSuccess)
+    e = moe::launch_transpose_weights(W_gate, E, dff, d, ws + B.wguT, 2 * dff, 0, stream);
+  if (e == hipSuccess)
+    e = moe::launch_transpose_weights(W_up, E, dff, d, ws + B.wguT, 2 * dff, dff, stream);
+  // combine and gate weights
+  if (e == hipSuccess)
+    e = moe::launch_bwd_combine(dout, y_perm, dest_row, topk_w, T, d, k, ws + B.dy, dl, stream);
+  // experts, data gradients
+  if (e == hipSuccess)
+    e = moe::launch_ffn_dgrad(ws + B.dy, offsets, ws + B.wdT, ws + B.wguT, sb + S.g, sb + S.u,
+                              R, d, E, dff, mean_rows_per_expert(p), mtp, ws + B.dgu, dxp,
+                              stream);
+  // permute and router
+  if (e == hipSuccess)
+    e = moe::launch_bwd_gather(dxp, dest_row, topk_idx, dl, W_r, T, d, k, dX, stream);
+  if (e == hipSuccess)
+    e = moe::launch_router_wgrad(X, topk_idx, dl, T, d, E, k, dW_r, dbias, stream);
+  // experts, weight gradients over each expert's (padded) rows
+  if (e == hipSuccess) e = moe::launch_pad_offsets(offsets, E, poff, stream);
+  if (e == hipSuccess)
+    e = moe::launch_transpose_segments(ws + B.dy, d, offsets, poff, E, ws + B.t1, B.ld, stream);
+  if (e == hipSuccess)
+    e = moe::launch_transpose_segments(sb + S.h, dff, offsets, poff, E, ws + B.t2, B.ld, stream);
+  if (e == hipSuccess)
+    e = moe::launch_wgrad(ws + B.t1, B.ld, d, ws + B.t2, B.ld, dff, poff, E, d, dW_down,
+                          nullptr, stream);
+  if (e == hipSuccess)
+    e = moe::launch_transpose_segments(ws + B.dgu, 2 * dff, offsets, poff, E, ws + B.t1, B.ld,
+                                       stream);
+  if (e == hipSuccess)
+    e = moe::launch_transpose_segments(sb + S.x_perm, d, offsets, poff, E, ws + B.t2, B.ld,
+                                       stream);
+  if (e == hipSuccess)
+    e = moe::launch_wgrad(ws + B.t1, B.ld, 2 * dff, ws + B.t2, B.ld, d, poff, E, dff, dW_gate,
+                          dW_up, stream);
   return hip_status(e);
 }
 

@@ -49,6 +49,7 @@ SOFTMAX_THEN_TOPK = 1
 # tensor ids of the per-tensor random streams
 _X, _WR, _WG, _WU, _WD, _PERM = 0, 1, 2, 3, 4, 5
 _SG, _SU, _SD = 6, 7, 8   # shared-expert projections
+_DOUT = 9                  # upstream gradient of the layer output (backward)
 
 
 @dataclass(frozen=True)
@@ -122,6 +123,13 @@ def _normal(rng, shape, std, bf16):
 def make_x(w: Workload, T=None):
     T = w.T if T is None else T
     return _normal(_rng(w.seed, _X), (T, w.d_model), 1.0, w.dtype == BF16)
+
+
+def make_dout(w: Workload, T=None):
+    """Upstream gradient dL/d(out) for the backward pass: [T, d] fp32,
+    N(0, 1) entries."""
+    T = w.T if T is None else T
+    return _normal(_rng(w.seed, _DOUT), (T, w.d_model), 1.0, False)
 
 
 def make_router(w: Workload):

@@ -195,3 +195,51 @@ def test_binding_rejects_host_tensors():
     X = torch.zeros((8, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         B.moe_route(p, X, torch.zeros((4, 64)), topk_idx=X, topk_w=X)
+
+
+def test_training_entry_points_checked_on_the_host():
+    lib = B.load()
+    fake = ctypes.c_void_p(0x1000)
+    big = 1 << 40
+    p = B.problem(64, 128, 8, 2, 256)
+    S = lib.moe_train_state_bytes(ctypes.byref(p))
+    W = lib.moe_backward_workspace_bytes(ctypes.byref(p))
+    fw = lib.moe_workspace_bytes(ctypes.byref(p))
+    R = lib.moe_rows_bound(ctypes.byref(p))
+    # the state holds X_perm, G, U, H (bf16) and Y_perm (fp32) at least
+    assert S >= R * (128 * 2 + 3 * 256 * 2 + 128 * 4)
+    # the workspace holds the transposed expert weights at least
+    assert W >= 8 * 3 * 128 * 256 * 2
+
+    def fwd(prob, state=fake, state_bytes=big, ws=fake, ws_bytes=big, X=fake):
+        return lib.moe_forward_train(ctypes.byref(prob), X, fake, None, fake, fake,
+                                     fake, fake, None, state, state_bytes, ws,
+                                     ws_bytes, None)
+
+    def bwd(prob, state=fake, state_bytes=big, ws=fake, ws_bytes=big, dout=fake,
+            dbias=fake):
+        return lib.moe_backward(ctypes.byref(prob), fake, fake, fake, fake, fake,
+                                state, state_bytes, dout, fake, fake, dbias, fake,
+                                fake, fake, ws, ws_bytes, None)
+
+    # fp32 layers are not supported for training
+    q = B.problem(64, 128, 8, 2, 256, dtype="f32")
+    assert lib.moe_train_state_bytes(ctypes.byref(q)) == 0
+    assert fwd(q) == B.MOE_ERR_UNSUPPORTED and bwd(q) == B.MOE_ERR_UNSUPPORTED
+    # a state that is missing or too small, a workspace that is too small
+    assert fwd(p, state=None) == B.MOE_ERR_INVALID_ARG
+    assert fwd(p, state_bytes=S - 1) == B.MOE_ERR_INVALID_ARG
+    assert fwd(p, ws_bytes=fw - 1) == B.MOE_ERR_WORKSPACE
+    assert fwd(p, X=None) == B.MOE_ERR_INVALID_ARG
+    assert bwd(p, state_bytes=S - 1) == B.MOE_ERR_INVALID_ARG
+    assert bwd(p, ws_bytes=W - 1) == B.MOE_ERR_WORKSPACE
+    assert bwd(p, ws=None) == B.MOE_ERR_WORKSPACE
+    assert bwd(p, dout=None) == B.MOE_ERR_INVALID_ARG
+    # an empty batch does nothing
+    e = B.problem(0, 128, 8, 2, 256)
+    assert fwd(e, state=None, ws=None) == B.MOE_OK
+    assert bwd(e, state=None, ws=None, dout=None) == B.MOE_OK
+    # the transposed row segments must fit one 32-bit buffer range
+    h = B.problem(1 << 20, 128, 8, 4, 256)
+    assert lib.moe_train_state_bytes(ctypes.byref(h)) == 0
+    assert bwd(h) == B.MOE_ERR_UNSUPPORTED
