@@ -43,6 +43,9 @@ def _parse():
     ap.add_argument("--shared-dff", type=int, default=0,
                     help="add a shared expert of this hidden size (the "
                          "DeepSeek-V3 layer form; moe_forward_shared)")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the training step (moe_forward_train + "
+                         "moe_backward) and report the backward's GEMM rate")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -333,6 +336,39 @@ def main():
         line["shared_expert"] = {
             "ms_per_step_side_stream": ms, "ms_per_step_one_stream": t_serial,
             "ms_routed_layer_alone": t_routed, "shared_ffn_flops": sh_flops}
+    if args.backward:
+        if args.fp8 or wl.dtype != W.BF16:
+            sys.exit("--backward needs a bf16 layer without --fp8")
+        state = torch.empty(M.train_state_bytes(p), dtype=torch.uint8, device="cuda")
+        ws_b = torch.empty(M.backward_workspace_bytes(p), dtype=torch.uint8,
+                           device="cuda")
+        dout = torch.from_numpy(W.make_dout(wl)).to("cuda")
+        grads = None
+
+        def fwd_train():
+            M.moe_forward_train(p, *a, out=out, stats=stats, state=state, workspace=ws)
+
+        def bwd():
+            nonlocal grads
+            grads = M.moe_backward(p, dev["X"], dev["W_r"], dev["W_gate"], dev["W_up"],
+                                   dev["W_down"], state, dout, grads=grads,
+                                   with_dbias=dev["bias"] is not None, workspace=ws_b)
+
+        for _ in range(2):
+            fwd_train()
+            bwd()
+        t_ft = _time_loop(fwd_train, n, stream)
+        fwd_train()
+        t_bwd = _time_loop(bwd, n, stream)
+        t_train = _time_loop(lambda: (fwd_train(), bwd()), n, stream)
+        bwd_flops = 12.0 * N * d * dff   # dH, dX_perm (x2), dW_down, dW_gate + dW_up (x2)
+        line["training"] = {
+            "ms_forward_train": t_ft, "ms_backward": t_bwd,
+            "ms_training_step": t_train,
+            "tokens_per_s_training": T / (t_train * 1e-3),
+            "backward_gemm_flops": bwd_flops,
+            "backward_tflops": bwd_flops / (t_bwd * 1e-3) / 1e12,
+            "backward_frac_of_bf16_peak": bwd_flops / (t_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = _cpu_baseline(
             wl, dev, args.cpu_sample_tokens,

@@ -13,10 +13,13 @@
 //   permute   dX[t] = sum over kept copies of dX_perm[dest[t,j]]
 //   router    dX[t] += sum_j dl[t,j] W_r[idx[t,j]],  dW_r = dl^T X,
 //             dbias = sum_t dl[t]
-// The expert GEMMs (dgrad and wgrad) run on the grouped GEMM kernel; their
-// transposed operands are written here.  Every sum runs in a fixed order,
-// so the same inputs give the same bits.
+// The expert GEMMs (dgrad and wgrad) run on the grouped GEMM kernel, which
+// reads the weights and the saved activations as stored.  Every sum runs in
+// a fixed order, so the same inputs give the same bits.
 #include "common.h"
+
+#include <algorithm>
+
 #include "launch.h"
 
 namespace moe {
@@ -106,28 +109,32 @@ __global__ __launch_bounds__(256) void bwd_gather_kernel(
 }
 
 // dW_r[e, c] = sum_t dl[t, e] X[t, c] and dbias[e] = sum_t dl[t, e], with dl
-// the sparse logit gradient (dl_sel at the selected ids).  Block: 256
-// columns x ET experts; each thread one column and ET accumulators.  Tokens
-// go 32 at a time: the block scatters their selections into a dense
-// [32 x ET] LDS tile, then every thread runs the tile in token order.
+// the sparse logit gradient (dl_sel at the selected ids), in two passes.
+// Pass 1: block (column slice of 256, ET experts, token chunk s) sums its
+// chunk's tokens in order into part[s] ([E, d], and [E] for the bias): each
+// thread one column and ET accumulators; tokens go 32 at a time, their
+// selections scattered into a dense [32 x ET] LDS tile first.  Pass 2 adds
+// the chunks' partial sums in chunk order.
 template <int ET>
-__global__ __launch_bounds__(256) void router_wgrad_kernel(
+__global__ __launch_bounds__(256) void router_wgrad_part_kernel(
     const uint16_t* __restrict__ X, const int32_t* __restrict__ idx,
-    const float* __restrict__ dl_sel, int T, int d, int E, int k,
-    float* __restrict__ dW_r, float* __restrict__ dbias) {
+    const float* __restrict__ dl_sel, int T, int d, int E, int k, int chunk,
+    float* __restrict__ part, float* __restrict__ part_b) {
   constexpr int TT = 32;
   __shared__ float s_dl[TT][ET];
   const int tid = threadIdx.x;
   const int c = blockIdx.x * 256 + tid;
   const int e0 = blockIdx.y * ET;
+  const int s = blockIdx.z;
+  const int t_beg = s * chunk, t_end = min(T, t_beg + chunk);
   float acc[ET];
 #pragma unroll
   for (int i = 0; i < ET; ++i) acc[i] = 0.f;
   float bacc = 0.f;
-  for (int t0 = 0; t0 < T; t0 += TT) {
+  for (int t0 = t_beg; t0 < t_end; t0 += TT) {
     for (int i = tid; i < TT * ET; i += 256) (&s_dl[0][0])[i] = 0.f;
     __syncthreads();
-    const int nt = min(TT, T - t0);
+    const int nt = min(TT, t_end - t0);
     for (int p = tid; p < nt * k; p += 256) {
       const int64_t q = (int64_t)t0 * k + p;
       const int e = idx[q] - e0;
@@ -145,100 +152,30 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(
       for (int tl = 0; tl < nt; ++tl) bacc += s_dl[tl][tid];
     __syncthreads();
   }
+  float* ps = part + (int64_t)s * E * d;
   if (c < d) {
 #pragma unroll
     for (int i = 0; i < ET; ++i)
-      if (e0 + i < E) dW_r[(int64_t)(e0 + i) * d + c] = acc[i];
+      if (e0 + i < E) ps[(int64_t)(e0 + i) * d + c] = acc[i];
   }
-  if (dbias != nullptr && blockIdx.x == 0 && tid < ET && e0 + tid < E) dbias[e0 + tid] = bacc;
+  if (blockIdx.x == 0 && tid < ET && e0 + tid < E) part_b[(int64_t)s * E + e0 + tid] = bacc;
 }
 
-// 64 x 64 tile transpose through LDS (bf16).  Source: rows i < 64 at
-// src_rows + i * C (rows i >= nrows read as zero), columns [c0, c0 + 64) of
-// C.  Destination: dst[(c0 + c) * ldo + i] for i < nout and c0 + c < C.
-// C, ldo and the destination's column offset are multiples of 8, so every
-// access is one 16-byte chunk.
-__device__ __forceinline__ void transpose_tile(const uint16_t* __restrict__ src_rows,
-                                               int nrows, int C, int c0,
-                                               uint16_t* __restrict__ dst, int64_t ldo,
-                                               int nout) {
-  __shared__ uint16_t s[64][66];
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int p = tid + 256 * h;
-    const int row = p / 8, cc = (p % 8) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row < nrows && c0 + cc < C)
-      v = *reinterpret_cast<const uint4*>(src_rows + (int64_t)row * C + c0 + cc);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[row][cc + 2 * i] = (uint16_t)(w[i] & 0xFFFF);
-      s[row][cc + 2 * i + 1] = (uint16_t)(w[i] >> 16);
-    }
+__global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(
+    const float* __restrict__ part, const float* __restrict__ part_b, int S, int E, int d,
+    float* __restrict__ dW_r, float* __restrict__ dbias) {
+  const int64_t n = (int64_t)E * d;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) {
+    float v = 0.f;
+    for (int s = 0; s < S; ++s) v += part[(int64_t)s * n + i];
+    dW_r[i] = v;
   }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int p = tid + 256 * h;
-    const int oc = p / 8, rc = (p % 8) * 8;
-    if (c0 + oc >= C || rc >= nout) continue;
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = (uint32_t)s[rc + 2 * i][oc] | ((uint32_t)s[rc + 2 * i + 1][oc] << 16);
-    *reinterpret_cast<uint4*>(dst + (int64_t)(c0 + oc) * ldo + rc) =
-        make_uint4(w[0], w[1], w[2], w[3]);
+  if (dbias != nullptr && blockIdx.x == 0 && threadIdx.x < E) {
+    float v = 0.f;
+    for (int s = 0; s < S; ++s) v += part_b[(int64_t)s * E + threadIdx.x];
+    dbias[threadIdx.x] = v;
   }
-}
-
-// Batched weight transpose: src [B, R, C] -> dst[b] [C, ldo] at column
-// offset co (dst[b][c][co + r] = src[b][r][c]).  Grid (C/64, R/64, B).
-__global__ __launch_bounds__(256) void transpose_weights_kernel(
-    const uint16_t* __restrict__ src, int R, int C, uint16_t* __restrict__ dst,
-    int ldo, int co) {
-  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
-  const int64_t b = blockIdx.z;
-  transpose_tile(src + (b * R + r0) * (int64_t)C, min(64, R - r0), C, c0,
-                 dst + b * (int64_t)C * ldo + co + r0, ldo, min(64, R - r0));
-}
-
-// Padded expert offsets: poff[e + 1] = poff[e] + roundup(rows of e, 64).
-__global__ __launch_bounds__(256) void pad_offsets_kernel(const int32_t* __restrict__ offsets,
-                                                          int E, int32_t* __restrict__ poff) {
-  __shared__ int32_t s[256];
-  const int e = threadIdx.x;
-  s[e] = e < E ? (offsets[e + 1] - offsets[e] + 63) / 64 * 64 : 0;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    const int v = e >= o ? s[e - o] : 0;
-    __syncthreads();
-    s[e] += v;
-    __syncthreads();
-  }
-  if (e == 0) poff[0] = 0;
-  if (e < E) poff[e + 1] = s[e];
-}
-
-// Rows grouped by expert -> transposed, padded segments: dst[c][p] for p in
-// [poff[e], poff[e + 1]) is src[offsets[e] + p - poff[e]][c], zero past the
-// expert's rows.  Grid (ld / 64, C / 64); a 64-column block of dst lies in
-// one expert's segment (segments are multiples of 64 wide).
-__global__ __launch_bounds__(256) void transpose_segments_kernel(
-    const uint16_t* __restrict__ src, int C, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ poff, int E, uint16_t* __restrict__ dst, int ld) {
-  const int p0 = blockIdx.x * 64;
-  if (p0 >= poff[E]) return;
-  int lo = 0, hi = E;  // poff[lo] <= p0 < poff[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (poff[mid] <= p0) lo = mid; else hi = mid;
-  }
-  const int e = lo;
-  const int r0 = offsets[e] + (p0 - poff[e]);
-  const int nrows = max(0, min(64, offsets[e + 1] - r0));
-  transpose_tile(src + (int64_t)r0 * C, nrows, C, blockIdx.y * 64, dst + p0, ld, 64);
 }
 
 }  // namespace
@@ -261,42 +198,42 @@ hipError_t launch_bwd_gather(const float* dX_perm, const int32_t* dest, const in
   return hipGetLastError();
 }
 
+int router_wgrad_chunks(int T, int d, int E) {
+  const int et = E <= 8 ? 8 : (E <= 32 ? 32 : 64);
+  const int blocks = ((d + 255) / 256) * ((E + et - 1) / et);
+  const int max_chunks = (T + 31) / 32;
+  return std::max(1, std::min(max_chunks, (1024 + blocks - 1) / blocks));
+}
+
+size_t router_wgrad_scratch_bytes(int T, int d, int E) {
+  const size_t S = (size_t)router_wgrad_chunks(T, d, E);
+  return S * E * d * 4 + ((S * E * 4 + 255) & ~size_t(255));
+}
+
 hipError_t launch_router_wgrad(const void* X, const int32_t* idx, const float* dl_sel, int T,
-                               int d, int E, int k, float* dW_r, float* dbias,
+                               int d, int E, int k, float* dW_r, float* dbias, void* scratch,
                                hipStream_t stream) {
   const uint16_t* x = static_cast<const uint16_t*>(X);
+  const int S = router_wgrad_chunks(T, d, E);
+  const int chunk = ((T + S - 1) / S + 31) / 32 * 32;
+  float* part_b = static_cast<float*>(scratch);
+  float* part = part_b + ((size_t)S * E + 63) / 64 * 64;
   const unsigned gx = (d + 255) / 256;
   if (E <= 8) {
-    router_wgrad_kernel<8><<<dim3(gx, 1), 256, 0, stream>>>(x, idx, dl_sel, T, d, E, k, dW_r, dbias);
+    router_wgrad_part_kernel<8><<<dim3(gx, 1, S), 256, 0, stream>>>(x, idx, dl_sel, T, d, E, k,
+                                                                   chunk, part, part_b);
   } else if (E <= 32) {
-    router_wgrad_kernel<32><<<dim3(gx, 1), 256, 0, stream>>>(x, idx, dl_sel, T, d, E, k, dW_r, dbias);
+    router_wgrad_part_kernel<32><<<dim3(gx, 1, S), 256, 0, stream>>>(x, idx, dl_sel, T, d, E, k,
+                                                                    chunk, part, part_b);
   } else {
-    router_wgrad_kernel<64><<<dim3(gx, (E + 63) / 64), 256, 0, stream>>>(x, idx, dl_sel, T, d, E,
-                                                                         k, dW_r, dbias);
+    router_wgrad_part_kernel<64><<<dim3(gx, (E + 63) / 64, S), 256, 0, stream>>>(
+        x, idx, dl_sel, T, d, E, k, chunk, part, part_b);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_weights(const void* src, int B, int R, int C, void* dst, int ldo,
-                                    int co, hipStream_t stream) {
-  const dim3 grid((C + 63) / 64, (R + 63) / 64, B);
-  transpose_weights_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint16_t*>(src), R, C,
-                                                    static_cast<uint16_t*>(dst), ldo, co);
-  return hipGetLastError();
-}
-
-hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t stream) {
-  pad_offsets_kernel<<<1, 256, 0, stream>>>(offsets, E, poff);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_segments(const void* src, int C, const int32_t* offsets,
-                                     const int32_t* poff, int E, void* dst, int ld,
-                                     hipStream_t stream) {
-  const dim3 grid(ld / 64, (C + 63) / 64);
-  transpose_segments_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint16_t*>(src), C,
-                                                     offsets, poff, E,
-                                                     static_cast<uint16_t*>(dst), ld);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t n = (int64_t)E * d;
+  router_wgrad_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(part, part_b, S, E,
+                                                                             d, dW_r, dbias);
   return hipGetLastError();
 }
 

@@ -153,7 +153,14 @@ __global__ __launch_bounds__(256) void ffn_schedule_kernel(
   if (e == E - 1) mt_prefix[E] = s[e];
 }
 
-template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS, bool BF8>
+// Operand layouts.  "NT" (row-major along K): A [M][K], B [N][K]; a stage
+// holds BM rows of A and BROWS rows of B, each BK elements of K, and the
+// fragments are read with ds_read_b128.  "T" (row-major along M or N, i.e.
+// K-major: A [K][M], B [K][N]): a stage holds BK rows (one per k) of BM or
+// BN elements, and the fragments are read with the gfx950 LDS transpose
+// read ds_read_b64_tr_b16 (see lds_frag_tr).  AT / BT select the T layout.
+template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS, bool BF8,
+          bool AT = false, bool BT = false>
 struct GemmCfg {
   static constexpr int NWAVES = MW * NW;
   static constexpr int NT = NWAVES * kWave;
@@ -161,33 +168,74 @@ struct GemmCfg {
   static constexpr int BN = NW * TN * 32;            // output columns per tile
   static constexpr int NB = GATEUP ? 2 * TN : TN;    // B sub-tiles per wave
   static constexpr int BROWS = GATEUP ? 2 * BN : BN;  // B rows staged per K step
-  // LDS stage: BM rows of A (bf16, RBA bytes each), then BROWS rows of B
-  // (bf16, or FP8 codes when BF8: RBB bytes each)
-  static constexpr int RBA = BK * 2;
-  static constexpr int RBB = BF8 ? BK : BK * 2;
+  // LDS stage: the A region (ROWSA rows of RBA bytes), then the B region
+  // (ROWSB rows of RBB bytes; FP8 codes when BF8)
+  static constexpr int RBA = AT ? BM * 2 : BK * 2;
+  static constexpr int RBB = BT ? BROWS * 2 : (BF8 ? BK : BK * 2);
+  static constexpr int ROWSA = AT ? BK : BM;
+  static constexpr int ROWSB = BT ? BK : BROWS;
   static constexpr int CPRA = RBA / 16, CPRB = RBB / 16;  // 16-byte chunks per row
   static constexpr int RPIA = 1024 / RBA, RPIB = 1024 / RBB;  // rows per wave-level load
-  static constexpr int NIA = BM / RPIA, NIB = BROWS / RPIB;
-  static constexpr int AREG = BM * RBA;
-  static constexpr int STAGE = AREG + BROWS * RBB;
+  static constexpr int NIA = ROWSA / RPIA, NIB = ROWSB / RPIB;
+  static constexpr int AREG = ROWSA * RBA;
+  static constexpr int STAGE = AREG + ROWSB * RBB;
   static constexpr int NINSTR = NIA + NIB;
   // the first LW waves issue the global -> LDS loads (LW <= NWAVES)
   static constexpr int LW = (MOE_LW < NWAVES) ? MOE_LW : NWAVES;
   static constexpr int IPW = NINSTR / LW;
   static_assert(NINSTR % LW == 0, "loads must split evenly over waves");
-  static_assert(BM % RPIA == 0 && BN % RPIB == 0, "a load must not straddle operands");
+  static_assert(RBA <= 1024 && RBB <= 1024, "a row must fit one wave-level load");
+  static_assert(ROWSA % RPIA == 0 && ROWSB % RPIB == 0 && (BT || BN % RPIB == 0),
+                "a load must not straddle operands");
+  static_assert((!AT || CPRA >= 16) && (!BT || CPRB >= 16), "T rows: at least 256 bytes");
+  static_assert(!(GATEUP && BT) && !(BF8 && BT), "T layout: one bf16 B");
   static constexpr int KSUB = BK / 16;               // MFMA k-steps per stage
   static constexpr int LDS_BYTES = NS * STAGE + 1040;  // + the tile prefix
 };
 
-// Kernel arguments.  Modes 0-2 (rows grouped by expert):
-//   A [R, K] bf16 rows; B0/B1 [E, N, K] bf16 (or FP8 codes); offsets = the
-//   experts' row offsets [E + 1]; mt_prefix = tile schedule [E + 1].
-// Mode 3 (weight gradient, C_e = A_e B_e^T with K = the expert's rows):
-//   A [M, lda] and B0 [N, ldb] bf16 hold the transposed rows of all experts,
-//   expert e in columns [offsets[e], offsets[e + 1]) (a multiple of 64 wide,
-//   zero-padded); C rows m < msplit go to C [E, msplit, N], the others to
-//   C1 [E, M - msplit, N] (fp32).
+// Chunk swizzle of T-layout row R (k index): the four rows a transpose read
+// touches at once (R & 3 = 0..3) put their 64 bytes on distinct banks.
+__device__ __forceinline__ uint32_t swz_t(uint32_t R) { return (R & 3u) << 2; }
+
+// One 32x32x16 MFMA fragment (8 bf16 of consecutive k for one row m or
+// column n per lane) from a T-layout region: LDS row k holds the m (or n)
+// values of that k.  ds_read_b64_tr_b16 hands lane l of each 16-lane group
+// the element (l % 4) of the 4 elements that lane 4 j + l / 4 addressed, as
+// its element j; so lane i of a group addresses row k0 + i / 4 at column
+// c0 + 4 (i % 4) and receives k0..k0+3 of column c0 + (its lane) -- the
+// second read (rows + 4) completes the 8 values.  p: this lane's address for
+// k0 = 0; rb: row bytes.
+__device__ __forceinline__ bf16x8 lds_frag_tr(const char* p, uint32_t rb) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 4 * rb));
+  const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+  const i32x4 w = {(int)a.x, (int)a.y, (int)b.x, (int)b.y};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// This lane's transpose-read address (bytes, k0 = 0) for the 32-wide sub-tile
+// starting at column col0 of a T region with rows of rb bytes: lanes 32-63
+// take k + 8, lanes 16-31 of each half columns + 16.
+__device__ __forceinline__ uint32_t tr_lane_off(int lane, uint32_t col0, uint32_t rb) {
+  const uint32_t i = lane & 15;
+  const uint32_t row = 8 * (lane >> 5) + (i >> 2);
+  const uint32_t col = col0 + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
+  return row * rb + (((col >> 3) ^ swz_t(row)) << 4) + (col & 7) * 2;
+}
+
+// Kernel arguments.
+//   Modes 0-2, 4 (rows grouped by expert): A holds the experts' rows
+//   ([R, K] bf16; mode 4: [R, lda]); offsets = row offsets [E + 1];
+//   mt_prefix = tile schedule [E + 1].  Modes 0, 1: B0/B1 [E, N, K] bf16 (or
+//   FP8 codes).  Mode 2: B0 [E, K, N] (the down projection as stored, read
+//   along its rows).  Mode 4: B0, B1 [E, K, N] (gate and up as stored; the
+//   two halves of A's K = 2 K).
+//   Mode 3 (weight gradient): for expert e, C_e = A_e^T B_e over its rows
+//   r in [offsets[e], offsets[e + 1]): A [R, lda] (M = g.M columns used),
+//   B0 [R, ldb] (N columns); C rows m < msplit go to C [E, msplit, N], the
+//   others to C1 [E, M - msplit, N] (fp32).
 struct GemmArgs {
   const uint16_t* A;
   const void* B0;
@@ -199,7 +247,7 @@ struct GemmArgs {
   const float* scales;  // FP8 weights: [E, 3]
   uint16_t* G;          // mode 1: G out; mode 2: G in ([R, N] bf16)
   uint16_t* U;          // mode 1: U out; mode 2: U in
-  int M, lda, ldb, msplit;  // mode 3
+  int M, lda, ldb, msplit;  // mode 3 (lda also mode 4)
   void* C1;                 // mode 3
 };
 
@@ -211,13 +259,16 @@ struct GemmArgs {
 // bits of the weight loads (kNonTemporal when each weight tile is read by
 // about one workgroup: the loads then stream past the caches).
 // MODE 0: the forward FFN.  MODE 1 (GATEUP, training forward): also stores
-// G = A B0^T and U = A B1^T in bf16.  MODE 2 (not GATEUP, backward of the
-// down projection): the accumulator is dH; the epilogue applies the SwiGLU
-// backward with the saved G and U and stores dG | dU as bf16 [R, 2N].
-// MODE 3: weight gradient (see GemmArgs).
+// G = A B0^T and U = A B1^T in bf16.  MODE 2 (backward of the down
+// projection): dH = A Wd with Wd read along its rows (T layout); the epilogue
+// applies the SwiGLU backward with the saved G and U and stores dG | dU as
+// bf16 [R, 2N].  MODE 3: weight gradient, both operands in T layout.
+// MODE 4: dX_perm = dG Wg + dU Wu, two K passes, B in T layout, fp32 out.
 template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS, int BAUX, bool BF8,
           int MODE>
 __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const GemmArgs g) {
+  constexpr bool AT = MODE == 3;
+  constexpr bool BT = MODE >= 2;
   const uint16_t* __restrict__ A = g.A;
   const void* __restrict__ B0 = g.B0;
   const void* __restrict__ B1 = g.B1;
@@ -227,8 +278,8 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   void* __restrict__ Cout = g.C;
   const float* __restrict__ scales = g.scales;
   static_assert(MODE != 1 || GATEUP, "mode 1 is a gate/up mode");
-  static_assert((MODE != 2 && MODE != 3) || (!GATEUP && !BF8), "modes 2, 3: one bf16 B");
-  using Cfg = GemmCfg<MW, NW, TM, TN, GATEUP, BK, NS, BF8>;
+  static_assert(MODE < 2 || (!GATEUP && !BF8), "modes 2-4: one bf16 B");
+  using Cfg = GemmCfg<MW, NW, TM, TN, GATEUP, BK, NS, BF8, AT, BT>;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, NB = Cfg::NB, IPW = Cfg::IPW;
   constexpr int NWAVES = Cfg::NWAVES, STAGE = Cfg::STAGE, LW = Cfg::LW;
   constexpr int RBA = Cfg::RBA, RBB = Cfg::RBB, CPRA = Cfg::CPRA, CPRB = Cfg::CPRB;
@@ -242,9 +293,9 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
   // ---- which tile is mine --------------------------------------------------
-  // e, the tile's first row (m_start: of X_perm / H; mode 3: of A) and
-  // column, its row and column counts, K of the tile, and the element
-  // offsets of its first A and B elements.
+  // e, the tile's first row (m_start: of X_perm / H; mode 3: first column
+  // of A) and column n0, its row and column counts, K of the tile (per pass),
+  // the element offsets of its first A and B elements, and the row strides.
   int e, m_start, rows, n0, ncols, K;
   int64_t a_off, b_off;
   uint32_t kbytes, kbytesB;  // A and B row strides in bytes
@@ -265,10 +316,10 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
     rows = min(BM, g.M - m_start);
     n0 = n_t * BN;
     ncols = min(BN, N - n0);
-    const int k0 = offsets[e];
-    K = offsets[e + 1] - k0;
-    a_off = (int64_t)m_start * g.lda + k0;
-    b_off = (int64_t)n0 * g.ldb + k0;
+    const int r0 = offsets[e];
+    K = offsets[e + 1] - r0;
+    a_off = (int64_t)r0 * g.lda + m_start;
+    b_off = (int64_t)r0 * g.ldb + n0;
     kbytes = (uint32_t)g.lda * 2u;
     kbytesB = (uint32_t)g.ldb * 2u;
   } else {
@@ -295,22 +346,45 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
     n0 = n_t * BN;
     ncols = min(BN, N - n0);
     K = g.K;
-    a_off = (int64_t)m_start * K;
-    b_off = ((int64_t)e * N + n0) * K;
-    kbytes = (uint32_t)K * 2u;
-    kbytesB = (uint32_t)K * (BF8 ? 1u : 2u);
+    if constexpr (MODE == 4) {
+      a_off = (int64_t)m_start * g.lda;
+      kbytes = (uint32_t)g.lda * 2u;
+    } else {
+      a_off = (int64_t)m_start * K;
+      kbytes = (uint32_t)K * 2u;
+    }
+    if constexpr (BT) {
+      b_off = (int64_t)e * K * N + n0;
+      kbytesB = (uint32_t)N * 2u;
+    } else {
+      b_off = ((int64_t)e * N + n0) * K;
+      kbytesB = (uint32_t)K * (BF8 ? 1u : 2u);
+    }
   }
 
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(A + a_off, (uint32_t)rows * kbytes);
+  // Buffer ranges: NT operands span the tile's rows (rows past them read
+  // zero).  T operands span K rows of the full row stride, the last one only
+  // up to the tile's valid width, so k >= K and the last row's columns past
+  // M or N read zero (nothing past the matrix is touched); in earlier rows
+  // the columns past M or N read the next row, which only reaches output
+  // rows or columns that the epilogue drops.  Widths are multiples of 8
+  // elements: no 16-byte chunk straddles a range end.
+  const uint32_t a_bytes =
+      AT ? (K > 0 ? (uint32_t)(K - 1) * kbytes + (uint32_t)rows * 2u : 0u)
+         : (uint32_t)rows * kbytes;
+  const uint32_t b_bytes =
+      BT ? (K > 0 ? (uint32_t)(K - 1) * kbytesB + (uint32_t)ncols * 2u : 0u)
+         : (uint32_t)ncols * kbytesB;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(A + a_off, a_bytes);
   const int64_t boff = b_off * (BF8 ? 1 : 2);  // bytes
-  const __amdgpu_buffer_rsrc_t rB0 =
-      make_rsrc(static_cast<const char*>(B0) + boff, (uint32_t)ncols * kbytesB);
+  const __amdgpu_buffer_rsrc_t rB0 = make_rsrc(static_cast<const char*>(B0) + boff, b_bytes);
   const __amdgpu_buffer_rsrc_t rB1 =
-      GATEUP ? make_rsrc(static_cast<const char*>(B1) + boff, (uint32_t)ncols * kbytesB) : rB0;
+      (GATEUP || MODE == 4) ? make_rsrc(static_cast<const char*>(B1) + boff, b_bytes) : rB0;
 
   // ---- per-lane load offsets (one 16-byte chunk per wave-level load) -------
-  // Loads 0..NIA-1 fill the A rows, the rest the B rows (B-local row index
-  // for the swizzle); kcol = first K element of the lane's chunk.
+  // Loads 0..NIA-1 fill the A region, the rest the B region.  NT: R is the
+  // region-local row (B-local for the swizzle), kcol the first K element of
+  // the lane's chunk.  T: R is the k row within the stage.
   uint32_t voff[IPW];
   int kcol[IPW];
   {
@@ -319,31 +393,58 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
       const int qi = wave + LW * i;
       if (qi < NIA) {
         const uint32_t R = qi * RPIA + lane / CPRA;
-        const uint32_t c = (lane % CPRA) ^ swz<CPRA>(R);
-        voff[i] = R * kbytes + c * 16;
-        kcol[i] = c * 8;
+        if constexpr (AT) {
+          const uint32_t c = (lane % CPRA) ^ swz_t(R);
+          voff[i] = R * kbytes + c * 16;
+          kcol[i] = 0;
+        } else {
+          const uint32_t c = (lane % CPRA) ^ swz<CPRA>(R);
+          voff[i] = R * kbytes + c * 16;
+          kcol[i] = c * 8;
+        }
       } else {
         const uint32_t R = (qi - NIA) * RPIB + lane / CPRB;
-        const uint32_t c = (lane % CPRB) ^ swz<CPRB>(R);
-        const uint32_t row = (GATEUP && R >= (uint32_t)BN) ? R - BN : R;
-        voff[i] = row * kbytesB + c * 16;
-        kcol[i] = c * (BF8 ? 16 : 8);
+        if constexpr (BT) {
+          const uint32_t c = (lane % CPRB) ^ swz_t(R);
+          voff[i] = R * kbytesB + c * 16;
+          kcol[i] = 0;
+        } else {
+          const uint32_t c = (lane % CPRB) ^ swz<CPRB>(R);
+          const uint32_t row = (GATEUP && R >= (uint32_t)BN) ? R - BN : R;
+          voff[i] = row * kbytesB + c * 16;
+          kcol[i] = c * (BF8 ? 16 : 8);
+        }
       }
     }
   }
-  const int nk = (K + BK - 1) / BK;
+  // MODE 4 runs K twice: stages [0, nk1) take dG (A columns 0..K) against
+  // the gate projection, stages [nk1, 2 nk1) dU (A columns K..2K) against
+  // the up projection, in one pipeline
+  const int nk1 = (K + BK - 1) / BK;
+  const int nk = MODE == 4 ? 2 * nk1 : nk1;
   const bool ktail = (K % BK) != 0;
+  // bytes a stage advances along K
+  const uint32_t stepA = AT ? (uint32_t)BK * kbytes : (uint32_t)RBA;
+  const uint32_t stepB = BT ? (uint32_t)BK * kbytesB : (uint32_t)RBB;
 
   auto issue = [&](int stage, int kt) {
     if (LW < NWAVES && wave >= LW) return;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int qi = wave + LW * i;
-      uint32_t vo = voff[i] + (uint32_t)kt * (qi < NIA ? RBA : RBB);
-      if (ktail && kt * BK + kcol[i] >= K) vo = kOob;
+      const bool is_a = qi < NIA;
+      const bool second = MODE == 4 && kt >= nk1;
+      const int ktl = second ? kt - nk1 : kt;
+      uint32_t vo = voff[i] + (uint32_t)ktl * (is_a ? stepA : stepB);
+      if (second && is_a) vo += (uint32_t)K * 2u;
+      const bool t_layout = is_a ? AT : BT;
+      if (!t_layout && ktail && ktl * BK + kcol[i] >= K) vo = kOob;
       char* dst = smem + stage * STAGE + qi * 1024;
-      if (qi < NIA)
+      if (is_a)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, MOE_LDS_PTR(dst), 16, vo, 0, 0, 0);
+      else if (MODE == 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? rB1 : rB0, MOE_LDS_PTR(dst), 16, vo, 0, 0,
+                                                 BAUX);
       else if (!GATEUP || (qi - NIA) * RPIB < BN)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rB0, MOE_LDS_PTR(dst), 16, vo, 0, 0, BAUX);
       else
@@ -363,25 +464,40 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   // row sub-tiles of this wave that hold any of the tile's rows
   int tm_active = (rows - wm * TM * 32 + 31) / 32;
   tm_active = tm_active < 0 ? 0 : (tm_active > TM ? TM : tm_active);
-  uint32_t offA[TM][KSUB], offB[NB][KSUB];
+  // NT: per (sub-tile, k-step) offsets.  T: per sub-tile offsets at k = 0
+  // (k-step ks adds ks * 16 rows).
+  uint32_t offA[TM][AT ? 1 : KSUB], offB[NB][BT ? 1 : KSUB];
+  if constexpr (AT) {
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi) offA[mi][0] = tr_lane_off(lane, wm * TM * 32 + mi * 32, RBA);
+  }
+  if constexpr (BT) {
+#pragma unroll
+    for (int nj = 0; nj < NB; ++nj)
+      offB[nj][0] = AREG + tr_lane_off(lane, wn * TN * 32 + nj * 32, RBB);
+  }
 #pragma unroll
   for (int ks = 0; ks < KSUB; ++ks) {
     const uint32_t c = 2 * ks + (lane >> 5);
+    if constexpr (!AT) {
 #pragma unroll
-    for (int mi = 0; mi < TM; ++mi) {
-      const uint32_t R = wm * TM * 32 + mi * 32 + (lane & 31);
-      offA[mi][ks] = R * RBA + ((c ^ swz<CPRA>(R)) * 16);
+      for (int mi = 0; mi < TM; ++mi) {
+        const uint32_t R = wm * TM * 32 + mi * 32 + (lane & 31);
+        offA[mi][ks] = R * RBA + ((c ^ swz<CPRA>(R)) * 16);
+      }
     }
+    if constexpr (!BT) {
 #pragma unroll
-    for (int nj = 0; nj < NB; ++nj) {
-      uint32_t brow;
-      if (GATEUP) brow = (nj < TN) ? wn * TN * 32 + nj * 32 : BN + wn * TN * 32 + (nj - TN) * 32;
-      else brow = wn * TN * 32 + nj * 32;
-      const uint32_t R = brow + (lane & 31);  // B-local row
-      if constexpr (BF8)  // 8 codes: half (lane >> 5) of 16-byte chunk ks
-        offB[nj][ks] = AREG + R * RBB + ((ks ^ swz<CPRB>(R)) * 16) + (lane >> 5) * 8;
-      else
-        offB[nj][ks] = AREG + R * RBB + ((c ^ swz<CPRB>(R)) * 16);
+      for (int nj = 0; nj < NB; ++nj) {
+        uint32_t brow;
+        if (GATEUP) brow = (nj < TN) ? wn * TN * 32 + nj * 32 : BN + wn * TN * 32 + (nj - TN) * 32;
+        else brow = wn * TN * 32 + nj * 32;
+        const uint32_t R = brow + (lane & 31);  // B-local row
+        if constexpr (BF8)  // 8 codes: half (lane >> 5) of 16-byte chunk ks
+          offB[nj][ks] = AREG + R * RBB + ((ks ^ swz<CPRB>(R)) * 16) + (lane >> 5) * 8;
+        else
+          offB[nj][ks] = AREG + R * RBB + ((c ^ swz<CPRB>(R)) * 16);
+      }
     }
   }
 
@@ -411,10 +527,14 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
         bf16x8 a[TM], b[NB];
 #pragma unroll
         for (int mi = 0; mi < TM; ++mi)
-          if (!RAGGED || mi < tm_active) a[mi] = *reinterpret_cast<const bf16x8*>(st + offA[mi][ks]);
+          if (!RAGGED || mi < tm_active) {
+            if constexpr (AT) a[mi] = lds_frag_tr(st + offA[mi][0] + ks * 16 * RBA, RBA);
+            else a[mi] = *reinterpret_cast<const bf16x8*>(st + offA[mi][ks]);
+          }
 #pragma unroll
         for (int nj = 0; nj < NB; ++nj) {
-          if constexpr (BF8) b[nj] = fp8x8_to_bf16x8(*reinterpret_cast<const uint2*>(st + offB[nj][ks]));
+          if constexpr (BT) b[nj] = lds_frag_tr(st + offB[nj][0] + ks * 16 * RBB, RBB);
+          else if constexpr (BF8) b[nj] = fp8x8_to_bf16x8(*reinterpret_cast<const uint2*>(st + offB[nj][ks]));
           else b[nj] = *reinterpret_cast<const bf16x8*>(st + offB[nj][ks]);
         }
 #pragma unroll
@@ -757,19 +877,19 @@ hipError_t launch_grouped_ffn_train(const void* X_perm, const int32_t* offsets,
   return launch_gemm<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, 0>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
 }
 
-hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const void* WdT,
-                            const void* WguT, const void* G, const void* U, int64_t R, int d,
-                            int E, int d_ff, int rows_per_expert, int32_t* mt_prefix,
-                            void* dGU, float* dX_perm, hipStream_t stream) {
+hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const void* W_gate,
+                            const void* W_up, const void* W_down, const void* G, const void* U,
+                            int64_t R, int d, int E, int d_ff, int rows_per_expert,
+                            int32_t* mt_prefix, void* dGU, float* dX_perm, hipStream_t stream) {
   const int bm = ffn_tile_rows(true, rows_per_expert, false);
   if (R == 0) return hipSuccess;
   ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, bm, mt_prefix);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // dH = dY_perm Wd (B = Wd^T [E, d_ff, d]) -> SwiGLU backward -> dG | dU
+  // dH = dY_perm Wd (Wd [E, d, d_ff] read along its rows) -> SwiGLU backward
   GemmArgs a{};
   a.A = static_cast<const uint16_t*>(dY_perm);
-  a.B0 = WdT;
+  a.B0 = W_down;
   a.N = d_ff;
   a.K = d;
   a.E = E;
@@ -778,31 +898,42 @@ hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const v
   a.C = dGU;
   a.G = const_cast<uint16_t*>(static_cast<const uint16_t*>(G));
   a.U = const_cast<uint16_t*>(static_cast<const uint16_t*>(U));
-  // dX_perm = dG Wg + dU Wu = [dG | dU] [Wg ; Wu] (B = [Wg^T | Wu^T] [E, d, 2 d_ff])
+  // dX_perm = dG Wg + dU Wu (Wg, Wu [E, d_ff, d] read along their rows)
+  GemmArgs x{};
+  x.A = static_cast<const uint16_t*>(dGU);
+  x.B0 = W_gate;
+  x.B1 = W_up;
+  x.N = d;
+  x.K = d_ff;
+  x.E = E;
+  x.offsets = offsets;
+  x.mt_prefix = mt_prefix;
+  x.C = dX_perm;
+  x.lda = 2 * d_ff;
   if (bm == 32) {
     err = launch_gemm_args<1, MOE_SNW, 1, 1, false, MOE_SBK, MOE_SNS, MOE_SBAUX, false, 2>(a, R, stream);
     if (err != hipSuccess) return err;
-    return launch_gemm<1, MOE_SNW, 1, 1, false, MOE_SBK, MOE_SNS, MOE_SBAUX>(dGU, WguT, nullptr, d, 2 * d_ff, E, R, offsets, mt_prefix, dX_perm, stream);
+    return launch_gemm_args<1, MOE_SNW, 1, 1, false, MOE_SBK, MOE_SNS, MOE_SBAUX, false, 4>(x, R, stream);
   }
   if (rows_per_expert <= MOE_BNT_ROWS) {
     err = launch_gemm_args<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, kNonTemporal, false, 2>(a, R, stream);
     if (err != hipSuccess) return err;
-    return launch_gemm<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, kNonTemporal>(dGU, WguT, nullptr, d, 2 * d_ff, E, R, offsets, mt_prefix, dX_perm, stream);
+    return launch_gemm_args<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, kNonTemporal, false, 4>(x, R, stream);
   }
   err = launch_gemm_args<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, 0, false, 2>(a, R, stream);
   if (err != hipSuccess) return err;
-  return launch_gemm<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, 0>(dGU, WguT, nullptr, d, 2 * d_ff, E, R, offsets, mt_prefix, dX_perm, stream);
+  return launch_gemm_args<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, 0, false, 4>(x, R, stream);
 }
 
-hipError_t launch_wgrad(const void* AT, int lda, int M, const void* BT, int ldb, int N,
-                        const int32_t* poff, int E, int msplit, float* C0, float* C1,
+hipError_t launch_wgrad(const void* A, int lda, int M, const void* B, int ldb, int N,
+                        const int32_t* offsets, int E, int msplit, float* C0, float* C1,
                         hipStream_t stream) {
   GemmArgs a{};
-  a.A = static_cast<const uint16_t*>(AT);
-  a.B0 = BT;
+  a.A = static_cast<const uint16_t*>(A);
+  a.B0 = B;
   a.N = N;
   a.E = E;
-  a.offsets = poff;
+  a.offsets = offsets;
   a.M = M;
   a.lda = lda;
   a.ldb = ldb;

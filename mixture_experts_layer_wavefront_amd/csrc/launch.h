@@ -56,19 +56,19 @@ hipError_t launch_grouped_ffn_train(const void* X_perm, const int32_t* offsets,
                                     void* U, float* Y_perm, hipStream_t stream);
 
 // Backward, data gradients of the experts: dGU [R, 2 d_ff] bf16 = (dG | dU)
-// from dH = dY_perm Wd and the saved G, U; dX_perm [R, d] fp32 = dGU [Wg ; Wu].
-// WdT [E, d_ff, d] and WguT [E, d, 2 d_ff] are the transposed weights.
-hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const void* WdT,
-                            const void* WguT, const void* G, const void* U, int64_t R, int d,
-                            int E, int d_ff, int rows_per_expert, int32_t* mt_prefix,
-                            void* dGU, float* dX_perm, hipStream_t stream);
+// from dH = dY_perm Wd and the saved G, U; dX_perm [R, d] fp32 = dG Wg + dU Wu.
+// The weights are read as stored ([E, out, in]), along their rows.
+hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const void* W_gate,
+                            const void* W_up, const void* W_down, const void* G, const void* U,
+                            int64_t R, int d, int E, int d_ff, int rows_per_expert,
+                            int32_t* mt_prefix, void* dGU, float* dX_perm, hipStream_t stream);
 
-// Weight gradients: for every expert e, C_e = AT_e BT_e^T over the expert's
-// padded row segment [poff[e], poff[e + 1]) (AT [M, lda], BT [N, ldb] bf16,
-// transposed rows, zero-padded to multiples of 64); rows m < msplit of C_e
-// go to C0 [E, msplit, N], the others to C1 [E, M - msplit, N] (fp32).
-hipError_t launch_wgrad(const void* AT, int lda, int M, const void* BT, int ldb, int N,
-                        const int32_t* poff, int E, int msplit, float* C0, float* C1,
+// Weight gradients: for every expert e, C_e = A_e^T B_e over the expert's
+// rows [offsets[e], offsets[e + 1]) of A [R, lda] (M columns used) and
+// B [R, ldb] (N columns), bf16; rows m < msplit of C_e go to
+// C0 [E, msplit, N], the others to C1 [E, M - msplit, N] (fp32).
+hipError_t launch_wgrad(const void* A, int lda, int M, const void* B, int ldb, int N,
+                        const int32_t* offsets, int E, int msplit, float* C0, float* C1,
                         hipStream_t stream);
 
 // Backward kernels that are not GEMMs (bf16 layers).
@@ -78,15 +78,10 @@ hipError_t launch_bwd_combine(const float* dout, const float* Y_perm, const int3
 hipError_t launch_bwd_gather(const float* dX_perm, const int32_t* dest, const int32_t* idx,
                              const float* dl_sel, const float* W_r, int T, int d, int k,
                              float* dX, hipStream_t stream);
+size_t router_wgrad_scratch_bytes(int T, int d, int E);
 hipError_t launch_router_wgrad(const void* X, const int32_t* idx, const float* dl_sel, int T,
-                               int d, int E, int k, float* dW_r, float* dbias,
+                               int d, int E, int k, float* dW_r, float* dbias, void* scratch,
                                hipStream_t stream);
-hipError_t launch_transpose_weights(const void* src, int B, int R, int C, void* dst, int ldo,
-                                    int co, hipStream_t stream);
-hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t stream);
-hipError_t launch_transpose_segments(const void* src, int C, const int32_t* offsets,
-                                     const int32_t* poff, int E, void* dst, int ld,
-                                     hipStream_t stream);
 
 // Expert offsets {0, T} of a dense FFN over all T rows (one "expert").
 hipError_t launch_dense_offsets(int32_t* offsets, int T, hipStream_t stream);

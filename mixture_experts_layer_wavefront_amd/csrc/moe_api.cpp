@@ -159,19 +159,17 @@ hipError_t enqueue_routed(const moe_problem_t* p, const void* X, const float* W_
 }
 
 // ---- training ---------------------------------------------------------------
-// Transposed-row width of the weight-gradient operands: every expert's rows
-// padded to a multiple of 64, for any routing (at most R + 63 E).
-int64_t bwd_ld(const moe_problem_t* p) {
-  return (moe_rows_bound(p) + 63 * (int64_t)p->E + 63) / 64 * 64;
-}
-
-// Training supports bf16 layers; the weight-gradient tiles address 256 rows
-// of the transposed operands with one 32-bit buffer range.
+// Training supports bf16 layers.  The backward GEMMs address a weight
+// matrix, or an expert's rows of a saved activation, with one 32-bit buffer
+// range.
 moe_status_t validate_train(const moe_problem_t* p) {
   const moe_status_t st = validate(p);
   if (st != MOE_OK) return st;
   if (!is_bf16(p)) return MOE_ERR_UNSUPPORTED;
-  if (bwd_ld(p) >= (1 << 22)) return MOE_ERR_UNSUPPORTED;
+  const int64_t w_bytes = (int64_t)p->d_model * p->d_ff * 2;
+  const int64_t row_bytes = (int64_t)std::max(p->d_model, 2 * p->d_ff) * 2;
+  if (w_bytes >= (int64_t(1) << 31) || moe_rows_bound(p) * row_bytes >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -201,8 +199,7 @@ TrainState train_state_layout(const moe_problem_t* p) {
 }
 
 struct BackwardLayout {
-  size_t wdT, wguT, dy, dgu, dxp, dl, poff, mtp, t1, t2, total;
-  int ld;
+  size_t dy, dgu, dxp, dl, mtp, rw, total;
 };
 
 BackwardLayout backward_layout(const moe_problem_t* p) {
@@ -210,18 +207,13 @@ BackwardLayout backward_layout(const moe_problem_t* p) {
   const size_t R = (size_t)moe_rows_bound(p);
   const size_t d = p->d_model, dff = p->d_ff, E = p->E;
   BackwardLayout B{};
-  B.ld = (int)bwd_ld(p);
   size_t o = 0;
-  B.wdT = o; o += a256(E * dff * d * 2);
-  B.wguT = o; o += a256(E * d * 2 * dff * 2);
   B.dy = o; o += a256(R * d * 2);
   B.dgu = o; o += a256(R * 2 * dff * 2);
   B.dxp = o; o += a256(R * d * 4);
   B.dl = o; o += a256(Tk * 4);
-  B.poff = o; o += a256((E + 1) * 4);
   B.mtp = o; o += a256((E + 1) * 4);
-  B.t1 = o; o += a256(std::max(d, 2 * dff) * (size_t)B.ld * 2);
-  B.t2 = o; o += a256(std::max(dff, d) * (size_t)B.ld * 2);
+  B.rw = o; o += a256(moe::router_wgrad_scratch_bytes(p->T, p->d_model, p->E));
   B.total = o;
   return B;
 }
@@ -570,47 +562,29 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* X, const float* W_
   const int32_t* dest_row = reinterpret_cast<const int32_t*>(sb + S.dest_row);
   const float* y_perm = reinterpret_cast<const float*>(sb + S.y_perm);
   float* dl = reinterpret_cast<float*>(ws + B.dl);
-  int32_t* poff = reinterpret_cast<int32_t*>(ws + B.poff);
   int32_t* mtp = reinterpret_cast<int32_t*>(ws + B.mtp);
   float* dxp = reinterpret_cast<float*>(ws + B.dxp);
 
-  // transposed weights: Wd^T [E, d_ff, d], [Wg^T | Wu^T] [E, d, 2 d_ff]
-  hipError_t e = moe::launch_transpose_weights(W_down, E, d, dff, ws + B.wdT, d, 0, stream);
-  if (e == hipSuccess)
-    e = moe::launch_transpose_weights(W_gate, E, dff, d, ws + B.wguT, 2 * dff, 0, stream);
-  if (e == hipSuccess)
-    e = moe::launch_transpose_weights(W_up, E, dff, d, ws + B.wguT, 2 * dff, dff, stream);
   // combine and gate weights
+  hipError_t e =
+      moe::launch_bwd_combine(dout, y_perm, dest_row, topk_w, T, d, k, ws + B.dy, dl, stream);
+  // experts, data gradients (SwiGLU backward in the dH epilogue)
   if (e == hipSuccess)
-    e = moe::launch_bwd_combine(dout, y_perm, dest_row, topk_w, T, d, k, ws + B.dy, dl, stream);
-  // experts, data gradients
-  if (e == hipSuccess)
-    e = moe::launch_ffn_dgrad(ws + B.dy, offsets, ws + B.wdT, ws + B.wguT, sb + S.g, sb + S.u,
-                              R, d, E, dff, mean_rows_per_expert(p), mtp, ws + B.dgu, dxp,
-                              stream);
+    e = moe::launch_ffn_dgrad(ws + B.dy, offsets, W_gate, W_up, W_down, sb + S.g, sb + S.u, R,
+                              d, E, dff, mean_rows_per_expert(p), mtp, ws + B.dgu, dxp, stream);
   // permute and router
   if (e == hipSuccess)
     e = moe::launch_bwd_gather(dxp, dest_row, topk_idx, dl, W_r, T, d, k, dX, stream);
   if (e == hipSuccess)
-    e = moe::launch_router_wgrad(X, topk_idx, dl, T, d, E, k, dW_r, dbias, stream);
-  // experts, weight gradients over each expert's (padded) rows
-  if (e == hipSuccess) e = moe::launch_pad_offsets(offsets, E, poff, stream);
+    e = moe::launch_router_wgrad(X, topk_idx, dl, T, d, E, k, dW_r, dbias, ws + B.rw, stream);
+  // experts, weight gradients over each expert's rows:
+  // dW_down = dY^T H, [dW_gate ; dW_up] = [dG | dU]^T X_perm
   if (e == hipSuccess)
-    e = moe::launch_transpose_segments(ws + B.dy, d, offsets, poff, E, ws + B.t1, B.ld, stream);
+    e = moe::launch_wgrad(ws + B.dy, d, d, sb + S.h, dff, dff, offsets, E, d, dW_down, nullptr,
+                          stream);
   if (e == hipSuccess)
-    e = moe::launch_transpose_segments(sb + S.h, dff, offsets, poff, E, ws + B.t2, B.ld, stream);
-  if (e == hipSuccess)
-    e = moe::launch_wgrad(ws + B.t1, B.ld, d, ws + B.t2, B.ld, dff, poff, E, d, dW_down,
-                          nullptr, stream);
-  if (e == hipSuccess)
-    e = moe::launch_transpose_segments(ws + B.dgu, 2 * dff, offsets, poff, E, ws + B.t1, B.ld,
-                                       stream);
-  if (e == hipSuccess)
-    e = moe::launch_transpose_segments(sb + S.x_perm, d, offsets, poff, E, ws + B.t2, B.ld,
-                                       stream);
-  if (e == hipSuccess)
-    e = moe::launch_wgrad(ws + B.t1, B.ld, 2 * dff, ws + B.t2, B.ld, d, poff, E, dff, dW_gate,
-                          dW_up, stream);
+    e = moe::launch_wgrad(ws + B.dgu, 2 * dff, 2 * dff, sb + S.x_perm, d, d, offsets, E, dff,
+                          dW_gate, dW_up, stream);
   return hip_status(e);
 }
 

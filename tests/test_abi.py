@@ -208,8 +208,8 @@ def test_training_entry_points_checked_on_the_host():
     R = lib.moe_rows_bound(ctypes.byref(p))
     # the state holds X_perm, G, U, H (bf16) and Y_perm (fp32) at least
     assert S >= R * (128 * 2 + 3 * 256 * 2 + 128 * 4)
-    # the workspace holds the transposed expert weights at least
-    assert W >= 8 * 3 * 128 * 256 * 2
+    # the workspace holds dY, dG | dU (bf16) and dX_perm (fp32) at least
+    assert W >= R * (128 * 2 + 2 * 256 * 2 + 128 * 4)
 
     def fwd(prob, state=fake, state_bytes=big, ws=fake, ws_bytes=big, X=fake):
         return lib.moe_forward_train(ctypes.byref(prob), X, fake, None, fake, fake,
@@ -239,7 +239,7 @@ def test_training_entry_points_checked_on_the_host():
     e = B.problem(0, 128, 8, 2, 256)
     assert fwd(e, state=None, ws=None) == B.MOE_OK
     assert bwd(e, state=None, ws=None, dout=None) == B.MOE_OK
-    # the transposed row segments must fit one 32-bit buffer range
+    # an expert's rows of a saved activation must fit one 32-bit buffer range
     h = B.problem(1 << 20, 128, 8, 4, 256)
     assert lib.moe_train_state_bytes(ctypes.byref(h)) == 0
     assert bwd(h) == B.MOE_ERR_UNSUPPORTED
