@@ -592,27 +592,65 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
     }
   } else if constexpr (MODE == 2) {
     // SwiGLU backward: dG = dH U silu'(G), dU = dH silu(G) with
-    // silu'(z) = s (1 + z (1 - s)), s = 1 / (1 + e^-z)
+    // silu'(z) = s (1 + z (1 - s)), s = 1 / (1 + e^-z).  The saved G and U
+    // of each 32x32 sub-tile are staged in LDS with 16-byte loads (a row
+    // of 32 values = 4 lanes), then read back in the accumulator layout (4
+    // consecutive rows of one column per lane) with the transpose load: lane
+    // x of a 16-lane group addresses row x / 4, columns 4 (x % 4)..+3 of its
+    // 4x16 block and receives the 4 rows of column (its lane).  Each wave
+    // uses its own LDS region (TM sub-tiles x 2 matrices x 2 KB), one column
+    // sub-tile at a time.
+    static_assert(NWAVES * TM * 4096 <= NS * STAGE, "epilogue staging fits the stages");
     uint16_t* dGU = static_cast<uint16_t*>(Cout);
+    __syncthreads();  // every wave is done with the last stage
+    char* wreg = smem + wave * (TM * 4096);
+    const uint32_t gbytes = (uint32_t)rows * (uint32_t)N * 2u;
+    const __amdgpu_buffer_rsrc_t rG = make_rsrc(g.G + (int64_t)m_start * N, gbytes);
+    const __amdgpu_buffer_rsrc_t rU = make_rsrc(g.U + (int64_t)m_start * N, gbytes);
+    const uint32_t i16 = lane & 15;
+    // transpose-read address within a 2 KB sub-tile region (k = 8 q added)
+    const uint32_t tr_off = (4 * (lane >> 5) + (i16 >> 2)) * 64 + ((lane >> 4) & 1) * 32 +
+                            (i16 & 3) * 8;
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
 #pragma unroll
     for (int nj = 0; nj < TN; ++nj) {
-      const int col = wn * TN * 32 + nj * 32 + col_l;
-      if (col >= ncols) continue;
+      const int cb = wn * TN * 32 + nj * 32;  // tile-local first column of the sub-tile
+      if (nj > 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
       for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rbase + mi * 32 + 8 * (r >> 2) + (r & 3);
-          if (row < rows) {
-            const int64_t o = (int64_t)(m_start + row) * N + n0 + col;
-            const float gv = bf16_bits_to_f32(g.G[o]), u = bf16_bits_to_f32(g.U[o]);
-            const float sg = 1.f / (1.f + __expf(-gv));
-            const float dh = acc[mi][nj][r];
-            const float dgv = dh * u * (sg * (1.f + gv * (1.f - sg)));
-            const float du = dh * (gv * sg);
-            const int64_t o2 = (int64_t)(m_start + row) * (2 * N) + n0 + col;
-            dGU[o2] = f32_to_bf16_bits(dgv);
-            dGU[o2 + N] = f32_to_bf16_bits(du);
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t row = wm * TM * 32 + mi * 32 + h * 16 + (lane >> 2);
+          const uint32_t vo = row * (uint32_t)N * 2u + (uint32_t)(n0 + cb + 8 * (lane & 3)) * 2u;
+          char* dg = wreg + mi * 4096 + h * 1024;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rG, MOE_LDS_PTR(dg), 16, vo, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rU, MOE_LDS_PTR(dg + 2048), 16, vo, 0, 0, 0);
+        }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      const int col = cb + col_l;
+#pragma unroll
+      for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const char* pg = wreg + mi * 4096 + q * 512 + tr_off;
+          const v4s gq = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(pg));
+          const v4s uq = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(pg + 2048));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = 4 * q + j;
+            const int row = rbase + mi * 32 + 8 * q + j;
+            if (row < rows && col < ncols) {
+              const float gv = bf16_bits_to_f32((uint16_t)gq[j]);
+              const float u = bf16_bits_to_f32((uint16_t)uq[j]);
+              const float sg = 1.f / (1.f + __expf(-gv));
+              const float dh = acc[mi][nj][r];
+              const float dgv = dh * u * (sg * (1.f + gv * (1.f - sg)));
+              const float du = dh * (gv * sg);
+              const int64_t o2 = (int64_t)(m_start + row) * (2 * N) + n0 + col;
+              dGU[o2] = f32_to_bf16_bits(dgv);
+              dGU[o2 + N] = f32_to_bf16_bits(du);
+            }
           }
         }
     }
