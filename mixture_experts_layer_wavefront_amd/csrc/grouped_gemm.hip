@@ -77,6 +77,9 @@
 #ifndef MOE_SBAUX
 #define MOE_SBAUX kNonTemporal  // 32-row tiles: weight loads stream (nt)
 #endif
+#ifndef MOE_WG_GM
+#define MOE_WG_GM 4  // weight-gradient tiles: M-tiles per group
+#endif
 #ifndef MOE_F8SBK
 #define MOE_F8SBK 128  // 32-row tiles with FP8 weights: K per stage (128-byte weight rows)
 #endif
@@ -311,7 +314,14 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
     if (logical >= total) return;
     e = logical / per_e;
     const int local = logical - e * per_e;
-    const int n_t = local / n_mt, m_t = local - n_t * n_mt;
+    // groups of 4 M-tiles walk the N-tiles together: the 32 tiles an XCD
+    // runs at once cover about 4 x 8 (M, N) tiles and share their operands
+    constexpr int kGroupM = MOE_WG_GM;
+    const int grp = local / (kGroupM * n_nt);
+    const int first_m = grp * kGroupM;
+    const int gsize = min(kGroupM, n_mt - first_m);
+    const int in_grp = local - grp * kGroupM * n_nt;
+    const int m_t = first_m + in_grp % gsize, n_t = in_grp / gsize;
     m_start = m_t * BM;
     rows = min(BM, g.M - m_start);
     n0 = n_t * BN;
