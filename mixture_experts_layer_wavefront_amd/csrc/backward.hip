@@ -72,11 +72,13 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(
   if (lane < k) dl_sel[(int64_t)t * k + lane] = my_w * (my_dw - sw);
 }
 
-// dX[t, c] = sum over kept slots j of dX_perm[dest[t,j], c], then
-// + sum over slots j of dl[t,j] W_r[idx[t,j], c] (both in slot order).  One
-// wavefront per (token, 512-column slice); each lane 8 columns.
+// dX[t, c] = sum over kept slots j of (P0 + P1)[dest[t,j], c], then
+// + sum over slots j of dl[t,j] W_r[idx[t,j], c] (both in slot order), with
+// P0 = dX_perm and P1 = dX_perm + R d the two K halves of the experts' data
+// gradient.  One wavefront per (token, 512-column slice); each lane 8
+// columns.
 __global__ __launch_bounds__(256) void bwd_gather_kernel(
-    const float* __restrict__ dX_perm, const int32_t* __restrict__ dest,
+    const float* __restrict__ dX_perm, int64_t R, const int32_t* __restrict__ dest,
     const int32_t* __restrict__ idx, const float* __restrict__ dl_sel,
     const float* __restrict__ W_r, int T, int d, int k, float* __restrict__ dX) {
   const int lane = threadIdx.x % kWave;
@@ -89,9 +91,10 @@ __global__ __launch_bounds__(256) void bwd_gather_kernel(
     const int r = dest[(int64_t)t * k + j];
     if (r < 0) continue;
     const float4* p = reinterpret_cast<const float4*>(dX_perm + (int64_t)r * d + c0);
-    const float4 u = p[0], v = p[1];
-    a0.x += u.x; a0.y += u.y; a0.z += u.z; a0.w += u.w;
-    a1.x += v.x; a1.y += v.y; a1.z += v.z; a1.w += v.w;
+    const float4* p2 = reinterpret_cast<const float4*>(dX_perm + (R + r) * d + c0);
+    const float4 u = p[0], v = p[1], u2 = p2[0], v2 = p2[1];
+    a0.x += u.x + u2.x; a0.y += u.y + u2.y; a0.z += u.z + u2.z; a0.w += u.w + u2.w;
+    a1.x += v.x + v2.x; a1.y += v.y + v2.y; a1.z += v.z + v2.z; a1.w += v.w + v2.w;
   }
   for (int j = 0; j < k; ++j) {
     const float l = dl_sel[(int64_t)t * k + j];
@@ -189,12 +192,12 @@ hipError_t launch_bwd_combine(const float* dout, const float* Y_perm, const int3
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_gather(const float* dX_perm, const int32_t* dest, const int32_t* idx,
-                             const float* dl_sel, const float* W_r, int T, int d, int k,
-                             float* dX, hipStream_t stream) {
+hipError_t launch_bwd_gather(const float* dX_perm, int64_t R, const int32_t* dest,
+                             const int32_t* idx, const float* dl_sel, const float* W_r, int T,
+                             int d, int k, float* dX, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const dim3 grid((T + kTokPerBlock - 1) / kTokPerBlock, (d + 511) / 512);
-  bwd_gather_kernel<<<grid, 256, 0, stream>>>(dX_perm, dest, idx, dl_sel, W_r, T, d, k, dX);
+  bwd_gather_kernel<<<grid, 256, 0, stream>>>(dX_perm, R, dest, idx, dl_sel, W_r, T, d, k, dX);
   return hipGetLastError();
 }
 

@@ -234,7 +234,8 @@ __device__ __forceinline__ uint32_t tr_lane_off(int lane, uint32_t col0, uint32_
 //   mt_prefix = tile schedule [E + 1].  Modes 0, 1: B0/B1 [E, N, K] bf16 (or
 //   FP8 codes).  Mode 2: B0 [E, K, N] (the down projection as stored, read
 //   along its rows).  Mode 4: B0, B1 [E, K, N] (gate and up as stored; the
-//   two halves of A's K = 2 K).
+//   two halves of A's K = 2 K), g.M = R: the second half's partial sums go
+//   to C + R N.
 //   Mode 3 (weight gradient): for expert e, C_e = A_e^T B_e over its rows
 //   r in [offsets[e], offsets[e + 1]): A [R, lda] (M = g.M columns used),
 //   B0 [R, ldb] (N columns); C rows m < msplit go to C [E, msplit, N], the
@@ -266,7 +267,8 @@ struct GemmArgs {
 // projection): dH = A Wd with Wd read along its rows (T layout); the epilogue
 // applies the SwiGLU backward with the saved G and U and stores dG | dU as
 // bf16 [R, 2N].  MODE 3: weight gradient, both operands in T layout.
-// MODE 4: dX_perm = dG Wg + dU Wu, two K passes, B in T layout, fp32 out.
+// MODE 4: the two halves of dX_perm = dG Wg + dU Wu as separate tiles (B in
+// T layout, fp32 out): half 0 writes dG Wg to C, half 1 dU Wu to C + R N.
 template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS, int BAUX, bool BF8,
           int MODE>
 __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const GemmArgs g) {
@@ -300,6 +302,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   // of A) and column n0, its row and column counts, K of the tile (per pass),
   // the element offsets of its first A and B elements, and the row strides.
   int e, m_start, rows, n0, ncols, K;
+  int half = 0;  // MODE 4: 0 = dG against the gate projection, 1 = dU against up
   int64_t a_off, b_off;
   uint32_t kbytes, kbytesB;  // A and B row strides in bytes
   const int n_nt = (N + BN - 1) / BN;
@@ -335,7 +338,9 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   } else {
     for (int i = tid; i <= E; i += Cfg::NT) s_pref[i] = mt_prefix[i];
     __syncthreads();
-    const int total = s_pref[E] * n_nt;
+    // MODE 4: each (expert, n, m) tile twice, once per K half (NH = 2)
+    constexpr int NH = MODE == 4 ? 2 : 1;
+    const int total = s_pref[E] * n_nt * NH;
     const int q = (total + kXcds - 1) / kXcds;
     const int slot = blockIdx.x / kXcds;
     if (slot >= q) return;
@@ -344,11 +349,13 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
     int lo = 0, hi = E;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (s_pref[mid] * n_nt <= logical) lo = mid; else hi = mid;
+      if (s_pref[mid] * n_nt * NH <= logical) lo = mid; else hi = mid;
     }
     e = lo;
     const int mt_e = s_pref[e + 1] - s_pref[e];
-    const int local = logical - s_pref[e] * n_nt;
+    int local = logical - s_pref[e] * n_nt * NH;
+    half = local / (mt_e * n_nt);
+    local -= half * mt_e * n_nt;
     const int n_t = local / mt_e, m_t = local % mt_e;
     const int row_end = offsets[e + 1];
     m_start = offsets[e] + m_t * BM;
@@ -357,8 +364,10 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
     ncols = min(BN, N - n0);
     K = g.K;
     if constexpr (MODE == 4) {
-      a_off = (int64_t)m_start * g.lda;
+      a_off = (int64_t)m_start * g.lda + (int64_t)half * K;
       kbytes = (uint32_t)g.lda * 2u;
+      if (half) B0 = B1;
+      Cout = static_cast<float*>(Cout) + (int64_t)half * g.M * N;
     } else {
       a_off = (int64_t)m_start * K;
       kbytes = (uint32_t)K * 2u;
@@ -381,7 +390,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   // elements: no 16-byte chunk straddles a range end.
   const uint32_t a_bytes =
       AT ? (K > 0 ? (uint32_t)(K - 1) * kbytes + (uint32_t)rows * 2u : 0u)
-         : (uint32_t)rows * kbytes;
+         : (uint32_t)rows * kbytes - (uint32_t)half * (uint32_t)K * 2u;
   const uint32_t b_bytes =
       BT ? (K > 0 ? (uint32_t)(K - 1) * kbytesB + (uint32_t)ncols * 2u : 0u)
          : (uint32_t)ncols * kbytesB;
@@ -389,7 +398,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   const int64_t boff = b_off * (BF8 ? 1 : 2);  // bytes
   const __amdgpu_buffer_rsrc_t rB0 = make_rsrc(static_cast<const char*>(B0) + boff, b_bytes);
   const __amdgpu_buffer_rsrc_t rB1 =
-      (GATEUP || MODE == 4) ? make_rsrc(static_cast<const char*>(B1) + boff, b_bytes) : rB0;
+      GATEUP ? make_rsrc(static_cast<const char*>(B1) + boff, b_bytes) : rB0;
 
   // ---- per-lane load offsets (one 16-byte chunk per wave-level load) -------
   // Loads 0..NIA-1 fill the A region, the rest the B region.  NT: R is the
@@ -427,11 +436,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
       }
     }
   }
-  // MODE 4 runs K twice: stages [0, nk1) take dG (A columns 0..K) against
-  // the gate projection, stages [nk1, 2 nk1) dU (A columns K..2K) against
-  // the up projection, in one pipeline
-  const int nk1 = (K + BK - 1) / BK;
-  const int nk = MODE == 4 ? 2 * nk1 : nk1;
+  const int nk = (K + BK - 1) / BK;
   const bool ktail = (K % BK) != 0;
   // bytes a stage advances along K
   const uint32_t stepA = AT ? (uint32_t)BK * kbytes : (uint32_t)RBA;
@@ -443,18 +448,12 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
     for (int i = 0; i < IPW; ++i) {
       const int qi = wave + LW * i;
       const bool is_a = qi < NIA;
-      const bool second = MODE == 4 && kt >= nk1;
-      const int ktl = second ? kt - nk1 : kt;
-      uint32_t vo = voff[i] + (uint32_t)ktl * (is_a ? stepA : stepB);
-      if (second && is_a) vo += (uint32_t)K * 2u;
+      uint32_t vo = voff[i] + (uint32_t)kt * (is_a ? stepA : stepB);
       const bool t_layout = is_a ? AT : BT;
-      if (!t_layout && ktail && ktl * BK + kcol[i] >= K) vo = kOob;
+      if (!t_layout && ktail && kt * BK + kcol[i] >= K) vo = kOob;
       char* dst = smem + stage * STAGE + qi * 1024;
       if (is_a)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, MOE_LDS_PTR(dst), 16, vo, 0, 0, 0);
-      else if (MODE == 4)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? rB1 : rB0, MOE_LDS_PTR(dst), 16, vo, 0, 0,
-                                                 BAUX);
       else if (!GATEUP || (qi - NIA) * RPIB < BN)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rB0, MOE_LDS_PTR(dst), 16, vo, 0, 0, BAUX);
       else
@@ -766,7 +765,7 @@ hipError_t launch_gemm_args(const GemmArgs& a, int64_t R, hipStream_t stream) {
   } else {
     // upper bound on M-tiles: every expert may add one partial tile
     const int64_t mt_max = (R + Cfg::BM - 1) / Cfg::BM + std::min<int64_t>(a.E, R);
-    tiles = mt_max * n_nt;
+    tiles = mt_max * n_nt * (MODE == 4 ? 2 : 1);
   }
   const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
   if (grid == 0) return hipSuccess;
@@ -958,6 +957,7 @@ hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const v
   x.mt_prefix = mt_prefix;
   x.C = dX_perm;
   x.lda = 2 * d_ff;
+  x.M = (int)R;  // the second K half's partial sums start R rows further
   if (bm == 32) {
     err = launch_gemm_args<1, MOE_SNW, 1, 1, false, MOE_SBK, MOE_SNS, MOE_SBAUX, false, 2>(a, R, stream);
     if (err != hipSuccess) return err;

@@ -56,7 +56,8 @@ hipError_t launch_grouped_ffn_train(const void* X_perm, const int32_t* offsets,
                                     void* U, float* Y_perm, hipStream_t stream);
 
 // Backward, data gradients of the experts: dGU [R, 2 d_ff] bf16 = (dG | dU)
-// from dH = dY_perm Wd and the saved G, U; dX_perm [R, d] fp32 = dG Wg + dU Wu.
+// from dH = dY_perm Wd and the saved G, U; dX_perm [2, R, d] fp32 holds the
+// two partial sums dG Wg and dU Wu (their sum is the rows' gradient).
 // The weights are read as stored ([E, out, in]), along their rows.
 hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const void* W_gate,
                             const void* W_up, const void* W_down, const void* G, const void* U,
@@ -75,9 +76,9 @@ hipError_t launch_wgrad(const void* A, int lda, int M, const void* B, int ldb, i
 hipError_t launch_bwd_combine(const float* dout, const float* Y_perm, const int32_t* dest,
                               const float* topk_w, int T, int d, int k, void* dY_perm,
                               float* dl_sel, hipStream_t stream);
-hipError_t launch_bwd_gather(const float* dX_perm, const int32_t* dest, const int32_t* idx,
-                             const float* dl_sel, const float* W_r, int T, int d, int k,
-                             float* dX, hipStream_t stream);
+hipError_t launch_bwd_gather(const float* dX_perm, int64_t R, const int32_t* dest,
+                             const int32_t* idx, const float* dl_sel, const float* W_r, int T,
+                             int d, int k, float* dX, hipStream_t stream);
 size_t router_wgrad_scratch_bytes(int T, int d, int E);
 hipError_t launch_router_wgrad(const void* X, const int32_t* idx, const float* dl_sel, int T,
                                int d, int E, int k, float* dW_r, float* dbias, void* scratch,

@@ -210,7 +210,7 @@ BackwardLayout backward_layout(const moe_problem_t* p) {
   size_t o = 0;
   B.dy = o; o += a256(R * d * 2);
   B.dgu = o; o += a256(R * 2 * dff * 2);
-  B.dxp = o; o += a256(R * d * 4);
+  B.dxp = o; o += a256(2 * R * d * 4);
   B.dl = o; o += a256(Tk * 4);
   B.mtp = o; o += a256((E + 1) * 4);
   B.rw = o; o += a256(moe::router_wgrad_scratch_bytes(p->T, p->d_model, p->E));
@@ -574,7 +574,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* X, const float* W_
                               d, E, dff, mean_rows_per_expert(p), mtp, ws + B.dgu, dxp, stream);
   // permute and router
   if (e == hipSuccess)
-    e = moe::launch_bwd_gather(dxp, dest_row, topk_idx, dl, W_r, T, d, k, dX, stream);
+    e = moe::launch_bwd_gather(dxp, R, dest_row, topk_idx, dl, W_r, T, d, k, dX, stream);
   if (e == hipSuccess)
     e = moe::launch_router_wgrad(X, topk_idx, dl, T, d, E, k, dW_r, dbias, ws + B.rw, stream);
   // experts, weight gradients over each expert's rows:

@@ -208,8 +208,8 @@ def test_training_entry_points_checked_on_the_host():
     R = lib.moe_rows_bound(ctypes.byref(p))
     # the state holds X_perm, G, U, H (bf16) and Y_perm (fp32) at least
     assert S >= R * (128 * 2 + 3 * 256 * 2 + 128 * 4)
-    # the workspace holds dY, dG | dU (bf16) and dX_perm (fp32) at least
-    assert W >= R * (128 * 2 + 2 * 256 * 2 + 128 * 4)
+    # the workspace holds dY, dG | dU (bf16) and dX_perm's two halves (fp32)
+    assert W >= R * (128 * 2 + 2 * 256 * 2 + 2 * 128 * 4)
 
     def fwd(prob, state=fake, state_bytes=big, ws=fake, ws_bytes=big, X=fake):
         return lib.moe_forward_train(ctypes.byref(prob), X, fake, None, fake, fake,
