@@ -10,7 +10,9 @@
 // A gather-reduce rather than a scatter-add: each slice of an output row is
 // owned by one wavefront that reads its k source rows and adds them in slot
 // order, so the sum order is fixed and no atomics are needed.  fp32
-// accumulation, one rounding at the store.
+// accumulation, one rounding at the store.  When the down projection ran as
+// two K halves, Y2 holds the second half's partial sums and each source row
+// is Y[r] + Y2[r] (the same fp32 add the grouped FFN's own sum performs).
 #include "common.h"
 #include "launch.h"
 
@@ -26,9 +28,9 @@ constexpr int kColsPerWave = 8 * kWave;  // 8 columns per lane
 // slot order).
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kTokPerBlock * kWave) void combine_kernel(
-    const float* __restrict__ Y, const int32_t* __restrict__ dest_row,
-    const float* __restrict__ topk_w, int T, int d, int k,
-    const float* __restrict__ add_rows, void* __restrict__ out) {
+    const float* __restrict__ Y, const float* __restrict__ Y2,
+    const int32_t* __restrict__ dest_row, const float* __restrict__ topk_w, int T, int d,
+    int k, const float* __restrict__ add_rows, void* __restrict__ out) {
   __shared__ int32_t s_dest[kTokPerBlock][32];
   __shared__ float s_w[kTokPerBlock][32];
   const int lane = threadIdx.x % kWave;
@@ -70,6 +72,19 @@ __global__ __launch_bounds__(kTokPerBlock * kWave) void combine_kernel(
         b[u] = src[1];
       }
     }
+    if (Y2 != nullptr) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (r[u] < 0) continue;
+        const f32x4* src = reinterpret_cast<const f32x4*>(Y2 + (int64_t)r[u] * d) + 2 * c;
+        const f32x4 a2 = src[0], b2 = src[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a[u][i] = a[u][i] + a2[i];
+          b[u][i] = b[u][i] + b2[i];
+        }
+      }
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (r[u] < 0) continue;
@@ -100,13 +115,13 @@ __global__ __launch_bounds__(kTokPerBlock * kWave) void combine_kernel(
 hipError_t launch_combine(const float* Y_perm, const int32_t* dest_row,
                           const float* topk_w, int T, int d, int k,
                           const float* add_rows, bool out_bf16, void* out,
-                          hipStream_t stream) {
+                          hipStream_t stream, const float* Y_half) {
   if (T == 0) return hipSuccess;
   const dim3 grid((T + kTokPerBlock - 1) / kTokPerBlock, (d + kColsPerWave - 1) / kColsPerWave);
   if (out_bf16)
-    combine_kernel<true><<<grid, kTokPerBlock * kWave, 0, stream>>>(Y_perm, dest_row, topk_w, T, d, k, add_rows, out);
+    combine_kernel<true><<<grid, kTokPerBlock * kWave, 0, stream>>>(Y_perm, Y_half, dest_row, topk_w, T, d, k, add_rows, out);
   else
-    combine_kernel<false><<<grid, kTokPerBlock * kWave, 0, stream>>>(Y_perm, dest_row, topk_w, T, d, k, add_rows, out);
+    combine_kernel<false><<<grid, kTokPerBlock * kWave, 0, stream>>>(Y_perm, Y_half, dest_row, topk_w, T, d, k, add_rows, out);
   return hipGetLastError();
 }
 

@@ -77,6 +77,9 @@
 #ifndef MOE_SBAUX
 #define MOE_SBAUX kNonTemporal  // 32-row tiles: weight loads stream (nt)
 #endif
+#ifndef MOE_SPLIT_DOWN
+#define MOE_SPLIT_DOWN 1  // split the down projection's K when its tiles fill the chip few times
+#endif
 #ifndef MOE_WG_GM
 #define MOE_WG_GM 4  // weight-gradient tiles: M-tiles per group
 #endif
@@ -234,8 +237,9 @@ __device__ __forceinline__ uint32_t tr_lane_off(int lane, uint32_t col0, uint32_
 //   mt_prefix = tile schedule [E + 1].  Modes 0, 1: B0/B1 [E, N, K] bf16 (or
 //   FP8 codes).  Mode 2: B0 [E, K, N] (the down projection as stored, read
 //   along its rows).  Mode 4: B0, B1 [E, K, N] (gate and up as stored; the
-//   two halves of A's K = 2 K), g.M = R: the second half's partial sums go
-//   to C + R N.
+//   two halves of A's K = 2 K), the second half's partial sums go to C1.
+//   Mode 5: B0 [E, N, ldb], K = half of A's row (lda = ldb = 2 K), partial
+//   sums of the two halves to C and C1.
 //   Mode 3 (weight gradient): for expert e, C_e = A_e^T B_e over its rows
 //   r in [offsets[e], offsets[e + 1]): A [R, lda] (M = g.M columns used),
 //   B0 [R, ldb] (N columns); C rows m < msplit go to C [E, msplit, N], the
@@ -251,8 +255,8 @@ struct GemmArgs {
   const float* scales;  // FP8 weights: [E, 3]
   uint16_t* G;          // mode 1: G out; mode 2: G in ([R, N] bf16)
   uint16_t* U;          // mode 1: U out; mode 2: U in
-  int M, lda, ldb, msplit;  // mode 3 (lda also mode 4)
-  void* C1;                 // mode 3
+  int M, lda, ldb, msplit;  // mode 3 (lda also modes 4, 5; ldb mode 5)
+  void* C1;                 // modes 3-5
 };
 
 // A [R, K] bf16 rows; B0/B1 [E, N, K] bf16, or FP8 E4M3 codes when BF8
@@ -268,12 +272,14 @@ struct GemmArgs {
 // applies the SwiGLU backward with the saved G and U and stores dG | dU as
 // bf16 [R, 2N].  MODE 3: weight gradient, both operands in T layout.
 // MODE 4: the two halves of dX_perm = dG Wg + dU Wu as separate tiles (B in
-// T layout, fp32 out): half 0 writes dG Wg to C, half 1 dU Wu to C + R N.
+// T layout, fp32 out): half 0 writes dG Wg to C, half 1 dU Wu to C1.
+// MODE 5: the down projection split in two K halves the same way (A [R, lda],
+// B [E, N, ldb] with K = lda / 2 per half): partial sums to C and C1.
 template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS, int BAUX, bool BF8,
           int MODE>
 __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const GemmArgs g) {
   constexpr bool AT = MODE == 3;
-  constexpr bool BT = MODE >= 2;
+  constexpr bool BT = MODE >= 2 && MODE <= 4;
   const uint16_t* __restrict__ A = g.A;
   const void* __restrict__ B0 = g.B0;
   const void* __restrict__ B1 = g.B1;
@@ -283,7 +289,8 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   void* __restrict__ Cout = g.C;
   const float* __restrict__ scales = g.scales;
   static_assert(MODE != 1 || GATEUP, "mode 1 is a gate/up mode");
-  static_assert(MODE < 2 || (!GATEUP && !BF8), "modes 2-4: one bf16 B");
+  static_assert(MODE < 2 || MODE == 5 || (!GATEUP && !BF8), "modes 2-4: one bf16 B");
+  static_assert(MODE != 5 || !GATEUP, "mode 5 is a down-projection mode");
   using Cfg = GemmCfg<MW, NW, TM, TN, GATEUP, BK, NS, BF8, AT, BT>;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, NB = Cfg::NB, IPW = Cfg::IPW;
   constexpr int NWAVES = Cfg::NWAVES, STAGE = Cfg::STAGE, LW = Cfg::LW;
@@ -338,8 +345,8 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   } else {
     for (int i = tid; i <= E; i += Cfg::NT) s_pref[i] = mt_prefix[i];
     __syncthreads();
-    // MODE 4: each (expert, n, m) tile twice, once per K half (NH = 2)
-    constexpr int NH = MODE == 4 ? 2 : 1;
+    // MODES 4, 5: each (expert, n, m) tile twice, once per K half (NH = 2)
+    constexpr int NH = (MODE == 4 || MODE == 5) ? 2 : 1;
     const int total = s_pref[E] * n_nt * NH;
     const int q = (total + kXcds - 1) / kXcds;
     const int slot = blockIdx.x / kXcds;
@@ -363,11 +370,11 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
     n0 = n_t * BN;
     ncols = min(BN, N - n0);
     K = g.K;
-    if constexpr (MODE == 4) {
+    if constexpr (MODE == 4 || MODE == 5) {
       a_off = (int64_t)m_start * g.lda + (int64_t)half * K;
       kbytes = (uint32_t)g.lda * 2u;
-      if (half) B0 = B1;
-      Cout = static_cast<float*>(Cout) + (int64_t)half * g.M * N;
+      if (MODE == 4 && half) B0 = B1;
+      if (half) Cout = g.C1;
     } else {
       a_off = (int64_t)m_start * K;
       kbytes = (uint32_t)K * 2u;
@@ -375,6 +382,9 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
     if constexpr (BT) {
       b_off = (int64_t)e * K * N + n0;
       kbytesB = (uint32_t)N * 2u;
+    } else if constexpr (MODE == 5) {
+      b_off = ((int64_t)e * N + n0) * g.ldb + (int64_t)half * K;
+      kbytesB = (uint32_t)g.ldb * (BF8 ? 1u : 2u);
     } else {
       b_off = ((int64_t)e * N + n0) * K;
       kbytesB = (uint32_t)K * (BF8 ? 1u : 2u);
@@ -393,7 +403,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
          : (uint32_t)rows * kbytes - (uint32_t)half * (uint32_t)K * 2u;
   const uint32_t b_bytes =
       BT ? (K > 0 ? (uint32_t)(K - 1) * kbytesB + (uint32_t)ncols * 2u : 0u)
-         : (uint32_t)ncols * kbytesB;
+         : (uint32_t)ncols * kbytesB - (uint32_t)half * (uint32_t)K * (BF8 ? 1u : 2u);
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(A + a_off, a_bytes);
   const int64_t boff = b_off * (BF8 ? 1 : 2);  // bytes
   const __amdgpu_buffer_rsrc_t rB0 = make_rsrc(static_cast<const char*>(B0) + boff, b_bytes);
@@ -765,7 +775,7 @@ hipError_t launch_gemm_args(const GemmArgs& a, int64_t R, hipStream_t stream) {
   } else {
     // upper bound on M-tiles: every expert may add one partial tile
     const int64_t mt_max = (R + Cfg::BM - 1) / Cfg::BM + std::min<int64_t>(a.E, R);
-    tiles = mt_max * n_nt * (MODE == 4 ? 2 : 1);
+    tiles = mt_max * n_nt * ((MODE == 4 || MODE == 5) ? 2 : 1);
   }
   const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
   if (grid == 0) return hipSuccess;
@@ -793,7 +803,64 @@ hipError_t launch_gemm(const void* A, const void* B0, const void* B1, int N,
   return launch_gemm_args<MW, NW, TM, TN, GATEUP, BK, NS, BAUX, BF8, 0>(a, R, stream);
 }
 
+// Y[r] += Y2[r] for the kept rows r < offsets[E] (the two K halves of the
+// down projection), 4 values per thread.
+__global__ __launch_bounds__(256) void ffn_add_halves_kernel(float* __restrict__ Y,
+                                                             const float* __restrict__ Y2,
+                                                             const int32_t* __restrict__ offsets,
+                                                             int E, int d) {
+  const int64_t n4 = (int64_t)offsets[E] * d / 4;
+  f32x4* y = reinterpret_cast<f32x4*>(Y);
+  const f32x4* y2 = reinterpret_cast<const f32x4*>(Y2);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * 256) {
+    const f32x4 a = y[i], b = y2[i];
+    y[i] = f32x4{a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]};
+  }
+}
+
+// The down projection Y = H Wd^T.  Y_half != nullptr: the two K halves run as
+// separate tiles (twice as many, so the last round of tiles is fuller), the
+// second half's partial sums go to Y_half and are then added into Y.
+template <int MW, int NW, int TM, int TN, int BK, int NS, int BAUX, bool BF8>
+hipError_t launch_down(const void* H, const void* W_down, int d, int d_ff, int E, int64_t R,
+                       const int32_t* offsets, const int32_t* mt_prefix, float* Y_perm,
+                       float* Y_half, hipStream_t stream, const float* scales,
+                       bool defer = false) {
+  if (Y_half == nullptr)
+    return launch_gemm<MW, NW, TM, TN, false, BK, NS, BAUX, BF8>(
+        H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream, scales);
+  GemmArgs a{};
+  a.A = static_cast<const uint16_t*>(H);
+  a.B0 = W_down;
+  a.N = d;
+  a.K = d_ff / 2;
+  a.E = E;
+  a.offsets = offsets;
+  a.mt_prefix = mt_prefix;
+  a.C = Y_perm;
+  a.C1 = Y_half;
+  a.scales = scales;
+  a.lda = d_ff;
+  a.ldb = d_ff;
+  hipError_t err = launch_gemm_args<MW, NW, TM, TN, false, BK, NS, BAUX, BF8, 5>(a, R, stream);
+  if (err != hipSuccess || defer) return err;  // defer: the caller adds the halves
+  const int64_t n4 = R * d / 4;
+  const unsigned grid = (unsigned)std::min<int64_t>((n4 + 255) / 256, 4096);
+  ffn_add_halves_kernel<<<grid, 256, 0, stream>>>(Y_perm, Y_half, offsets, E, d);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool ffn_split_down(bool bf16, int E, int rows_per_expert, int d, int d_ff) {
+  if (!MOE_SPLIT_DOWN || !bf16 || rows_per_expert <= 64) return false;
+  if (d_ff < 2048 || d_ff % 32 != 0) return false;
+  // 256 x 256 tiles of the unsplit GEMM: split when they fill the 256 CUs
+  // fewer than four times
+  const int64_t tiles = (int64_t)E * ((rows_per_expert + 255) / 256) * ((d + 255) / 256);
+  return tiles < 4 * 256;
+}
 
 int ffn_tile_rows(bool bf16, int rows_per_expert, bool fp8) {
   if (!bf16) return 0;
@@ -801,8 +868,16 @@ int ffn_tile_rows(bool bf16, int rows_per_expert, bool fp8) {
   return (fp8 && rows_per_expert <= 512) ? 128 : 256;
 }
 
-size_t ffn_scratch_bytes(int64_t R, int E, int d_ff, bool bf16) {
-  return align256((size_t)(E + 1) * 4) + align256((size_t)R * d_ff * (bf16 ? 2 : 4));
+float* ffn_half_sums(void* scratch, int64_t R, int E, int d, int d_ff, bool bf16,
+                     int rows_per_expert) {
+  if (!ffn_split_down(bf16, E, rows_per_expert, d, d_ff)) return nullptr;
+  return reinterpret_cast<float*>(static_cast<char*>(scratch) + align256((size_t)(E + 1) * 4) +
+                                  align256((size_t)R * d_ff * 2));
+}
+
+size_t ffn_scratch_bytes(int64_t R, int E, int d, int d_ff, bool bf16, int rows_per_expert) {
+  return align256((size_t)(E + 1) * 4) + align256((size_t)R * d_ff * (bf16 ? 2 : 4)) +
+         (ffn_split_down(bf16, E, rows_per_expert, d, d_ff) ? align256((size_t)R * d * 4) : 0);
 }
 
 hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
@@ -810,13 +885,14 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
                               const void* W_up, const void* W_down, int64_t R,
                               int d, int E, int d_ff, int rows_per_expert,
                               float* Y_perm, void* scratch, bool prefix_ready,
-                              hipStream_t stream, const float* w_scales) {
+                              hipStream_t stream, const float* w_scales, bool defer) {
   const bool fp8 = w_scales != nullptr;
   const int bm = ffn_tile_rows(bf16, rows_per_expert, fp8);
   const bool small_m = bm == 32;
   if (R == 0) return hipSuccess;
   int32_t* mt_prefix = static_cast<int32_t*>(scratch);
   void* H = static_cast<char*>(scratch) + align256((size_t)(E + 1) * 4);
+  float* Y_half = ffn_half_sums(scratch, R, E, d, d_ff, bf16, rows_per_expert);
   if (!bf16) {
     const dim3 g1((d_ff + 255) / 256, (unsigned)R), g2((d + 255) / 256, (unsigned)R);
     ffn_f32_gateup_kernel<<<g1, 256, 0, stream>>>(
@@ -856,28 +932,28 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
     if (rows_per_expert <= 128) {
       err = launch_gemm<2, 4, 2, 1, true, 128, 2, kNonTemporal, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales);
       if (err != hipSuccess) return err;
-      return launch_gemm<2, 4, 2, 2, false, 128, 2, kNonTemporal, true>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream, w_scales);
+      return launch_down<2, 4, 2, 2, 128, 2, kNonTemporal, true>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, w_scales, defer);
     }
     err = launch_gemm<2, 4, 2, 1, true, 128, 2, 0, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales);
     if (err != hipSuccess) return err;
-    return launch_gemm<2, 4, 2, 2, false, 128, 2, 0, true>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream, w_scales);
+    return launch_down<2, 4, 2, 2, 128, 2, 0, true>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, w_scales, defer);
   }
   if (fp8) {
     // FP8 weights, many rows per expert: the 256-row tiles of the bf16 path
     // (the weight tiles are shared by several M-tiles through L2)
     err = launch_gemm<2, MOE_NW, 4, 4 / MOE_NW, true, MOE_BK, MOE_NS, 0, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales);
     if (err != hipSuccess) return err;
-    return launch_gemm<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, 0, true>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream, w_scales);
+    return launch_down<2, MOE_NW, 4, MOE_DTN / MOE_NW, MOE_BK, MOE_NS, 0, true>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, w_scales, defer);
   }
   if (rows_per_expert <= MOE_BNT_ROWS) {
     // about one M-tile per expert: every weight tile is read once
     err = launch_gemm<2, MOE_NW, 4, 4 / MOE_NW, true, MOE_BK, MOE_NS, kNonTemporal>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
     if (err != hipSuccess) return err;
-    return launch_gemm<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, kNonTemporal>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
+    return launch_down<2, MOE_NW, 4, MOE_DTN / MOE_NW, MOE_BK, MOE_NS, kNonTemporal, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr, defer);
   }
   err = launch_gemm<2, MOE_NW, 4, 4 / MOE_NW, true, MOE_BK, MOE_NS, 0>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
   if (err != hipSuccess) return err;
-  return launch_gemm<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, 0>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
+  return launch_down<2, MOE_NW, 4, MOE_DTN / MOE_NW, MOE_BK, MOE_NS, 0, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr, defer);
 }
 
 }  // namespace moe
@@ -914,14 +990,17 @@ hipError_t launch_grouped_ffn_train(const void* X_perm, const int32_t* offsets,
     if (err != hipSuccess) return err;
     return launch_gemm<1, MOE_SNW, 1, 1, false, MOE_SBK, MOE_SNS, MOE_SBAUX>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
   }
+  // the down projection as in launch_grouped_ffn (same split, same scratch
+  // place for the second K half), so the output equals moe_forward's
+  float* Y_half = ffn_half_sums(mt_prefix, R, E, d, d_ff, true, rows_per_expert);
   if (rows_per_expert <= MOE_BNT_ROWS) {
     err = launch_gemm_args<2, MOE_NW, 4, 4 / MOE_NW, true, MOE_BK, MOE_NS, kNonTemporal, false, 1>(a, R, stream);
     if (err != hipSuccess) return err;
-    return launch_gemm<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, kNonTemporal>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
+    return launch_down<2, MOE_NW, 4, MOE_DTN / MOE_NW, MOE_BK, MOE_NS, kNonTemporal, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr);
   }
   err = launch_gemm_args<2, MOE_NW, 4, 4 / MOE_NW, true, MOE_BK, MOE_NS, 0, false, 1>(a, R, stream);
   if (err != hipSuccess) return err;
-  return launch_gemm<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, 0>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
+  return launch_down<2, MOE_NW, 4, MOE_DTN / MOE_NW, MOE_BK, MOE_NS, 0, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr);
 }
 
 hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const void* W_gate,
@@ -956,8 +1035,8 @@ hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const v
   x.offsets = offsets;
   x.mt_prefix = mt_prefix;
   x.C = dX_perm;
+  x.C1 = dX_perm + R * d;  // the second K half's partial sums
   x.lda = 2 * d_ff;
-  x.M = (int)R;  // the second K half's partial sums start R rows further
   if (bm == 32) {
     err = launch_gemm_args<1, MOE_SNW, 1, 1, false, MOE_SBK, MOE_SNS, MOE_SBAUX, false, 2>(a, R, stream);
     if (err != hipSuccess) return err;

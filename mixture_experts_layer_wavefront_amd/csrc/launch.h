@@ -37,14 +37,24 @@ hipError_t launch_permute(const void* X, bool x_bf16, const int32_t* topk_idx,
 // experts of their tile counts, E + 1 ints) lives at the start of `scratch`;
 // with prefix_ready the caller has already written it there.  w_scales !=
 // nullptr: the weights are FP8 E4M3 codes with scales [E, 3] (bf16 layers).
+// The down projection runs as two K halves (their sums added afterwards) for
+// shapes whose 256 x 256 tiles fill the chip only a few times; the second
+// half's partial sums need R d fp32 more scratch.
 int ffn_tile_rows(bool bf16, int rows_per_expert, bool fp8 = false);
-size_t ffn_scratch_bytes(int64_t R, int E, int d_ff, bool bf16);
+bool ffn_split_down(bool bf16, int E, int rows_per_expert, int d, int d_ff);
+size_t ffn_scratch_bytes(int64_t R, int E, int d, int d_ff, bool bf16, int rows_per_expert);
 hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
                               const int32_t* offsets, const void* W_gate,
                               const void* W_up, const void* W_down,
                               int64_t R, int d, int E, int d_ff, int rows_per_expert,
                               float* Y_perm, void* scratch, bool prefix_ready,
-                              hipStream_t stream, const float* w_scales = nullptr);
+                              hipStream_t stream, const float* w_scales = nullptr,
+                              bool defer_half_sum = false);
+
+// Where a split down projection leaves its second K half (inside `scratch`),
+// or nullptr when it is not split.
+float* ffn_half_sums(void* scratch, int64_t R, int E, int d, int d_ff, bool bf16,
+                     int rows_per_expert);
 
 // Training forward (bf16 layers): the grouped FFN that also keeps
 // G = X Wg^T and U = X Wu^T (bf16 [R, d_ff]) and H (bf16 [R, d_ff]) for the
@@ -88,10 +98,11 @@ hipError_t launch_router_wgrad(const void* X, const int32_t* idx, const float* d
 hipError_t launch_dense_offsets(int32_t* offsets, int T, hipStream_t stream);
 
 // Gate-weighted gather-combine back to token order.  add_rows ([T, d] fp32 or
-// nullptr) is the first term of every output row's sum.
+// nullptr) is the first term of every output row's sum; Y_half ([R, d] or
+// nullptr): second partial sums of the expert rows, added to Y_perm's.
 hipError_t launch_combine(const float* Y_perm, const int32_t* dest_row,
                           const float* topk_w, int T, int d, int k,
                           const float* add_rows, bool out_bf16, void* out,
-                          hipStream_t stream);
+                          hipStream_t stream, const float* Y_half = nullptr);
 
 }  // namespace moe

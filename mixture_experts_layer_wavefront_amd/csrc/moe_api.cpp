@@ -87,7 +87,9 @@ ForwardLayout forward_layout(const moe_problem_t* p, bool router_stats = false) 
   L.dest_row = o; o += a256(Tk * 4);
   L.row_token = o; o += a256(R * 4);
   L.x_perm = o; o += a256(R * p->d_model * act_bytes(p));
-  L.ffn_scratch = o; o += a256(moe::ffn_scratch_bytes((int64_t)R, p->E, p->d_ff, is_bf16(p)));
+  L.ffn_scratch = o;
+  o += a256(moe::ffn_scratch_bytes((int64_t)R, p->E, p->d_model, p->d_ff, is_bf16(p),
+                                   mean_rows_per_expert(p)));
   L.y_perm = o; o += a256(R * p->d_model * 4);
   L.total = o;
   return L;
@@ -104,7 +106,8 @@ SharedLayout shared_layout(const moe_problem_t* p, int sdff, size_t base) {
   SharedLayout S{};
   size_t o = base;
   S.offsets = o; o += 256;
-  S.ffn_scratch = o; o += a256(moe::ffn_scratch_bytes(p->T, 1, sdff, is_bf16(p)));
+  S.ffn_scratch = o;
+  o += a256(moe::ffn_scratch_bytes(p->T, 1, p->d_model, sdff, is_bf16(p), p->T));
   S.y_shared = o; o += a256((size_t)p->T * p->d_model * 4);
   S.total = o;
   return S;
@@ -122,6 +125,7 @@ struct RoutedOut {
   int32_t* dest_row;
   float* topk_w;
   float* y_perm;
+  float* y_half;  // second K half of a split down projection (the combine adds it), or null
 };
 
 hipError_t enqueue_routed(const moe_problem_t* p, const void* X, const float* W_r,
@@ -140,7 +144,9 @@ hipError_t enqueue_routed(const moe_problem_t* p, const void* X, const float* W_
   void* x_perm = ws + L.x_perm;
   float* y_perm = reinterpret_cast<float*>(ws + L.y_perm);
   const bool bf = is_bf16(p);
-  *r = RoutedOut{dest_row, topk_w, y_perm};
+  *r = RoutedOut{dest_row, topk_w, y_perm,
+                 moe::ffn_half_sums(ws + L.ffn_scratch, moe_rows_bound(p), p->E, p->d_model,
+                                    p->d_ff, bf, mean_rows_per_expert(p))};
 
   hipError_t e = moe::launch_route(X, bf, W_r, bias, p->T, p->d_model, p->E, p->top_k,
                                    (int)p->gating, topk_idx, topk_w, ws + L.route_scratch,
@@ -155,7 +161,8 @@ hipError_t enqueue_routed(const moe_problem_t* p, const void* X, const float* W_
   if (e != hipSuccess) return e;
   return moe::launch_grouped_ffn(x_perm, bf, offsets, W_gate, W_up, W_down, moe_rows_bound(p),
                                  p->d_model, p->E, p->d_ff, mean_rows_per_expert(p), y_perm,
-                                 ws + L.ffn_scratch, mt_prefix != nullptr, stream, w_scales);
+                                 ws + L.ffn_scratch, mt_prefix != nullptr, stream, w_scales,
+                                 /*defer_half_sum=*/true);
 }
 
 // ---- training ---------------------------------------------------------------
@@ -250,7 +257,8 @@ size_t moe_permute_workspace_bytes(const moe_problem_t* p) {
 
 size_t moe_grouped_ffn_workspace_bytes(const moe_problem_t* p) {
   if (validate(p, true) != MOE_OK) return 0;
-  return a256(moe::ffn_scratch_bytes(moe_rows_bound(p), p->E, p->d_ff, is_bf16(p)));
+  return a256(moe::ffn_scratch_bytes(moe_rows_bound(p), p->E, p->d_model, p->d_ff, is_bf16(p),
+                                     mean_rows_per_expert(p)));
 }
 
 size_t moe_workspace_bytes(const moe_problem_t* p) {
@@ -353,7 +361,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* X, const float* W_r
                                 stream, &r);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_combine(r.y_perm, r.dest_row, r.topk_w, p->T, p->d_model, p->top_k,
-                          nullptr, out_bf16(p), out, stream);
+                          nullptr, out_bf16(p), out, stream, r.y_half);
   return hip_status(e);
 }
 
@@ -380,7 +388,7 @@ moe_status_t moe_forward_stats(const moe_problem_t* p, const void* X, const floa
                                 L, stream, &r);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_combine(r.y_perm, r.dest_row, r.topk_w, p->T, p->d_model, p->top_k,
-                          nullptr, out_bf16(p), out, stream);
+                          nullptr, out_bf16(p), out, stream, r.y_half);
   return hip_status(e);
 }
 
@@ -432,7 +440,7 @@ moe_status_t moe_forward_shared(const moe_problem_t* p, int32_t shared_d_ff,
   if (e == hipSuccess && side_stream != nullptr) e = hipStreamWaitEvent(stream, join, 0);
   if (e == hipSuccess)
     e = moe::launch_combine(r.y_perm, r.dest_row, r.topk_w, p->T, p->d_model, p->top_k,
-                            y_shared, out_bf16(p), out, stream);
+                            y_shared, out_bf16(p), out, stream, r.y_half);
   if (fork) (void)hipEventDestroy(fork);
   if (join) (void)hipEventDestroy(join);
   return hip_status(e);
@@ -476,7 +484,7 @@ moe_status_t moe_forward_scaled(const moe_problem_t* p, const void* X, const flo
                                 stream, &r, w_scales);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_combine(r.y_perm, r.dest_row, r.topk_w, p->T, p->d_model, p->top_k,
-                          nullptr, out_bf16(p), out, stream);
+                          nullptr, out_bf16(p), out, stream, r.y_half);
   return hip_status(e);
 }
 

@@ -48,6 +48,8 @@ CASES = {
     "top1_bwd": WL("top1_bwd", 256, 128, 4, 1, 192, W.BF16, TK, 0.0, 0.0, 66),
     # d_model and d_ff not multiples of 64 (K and N tails everywhere)
     "ragged_bwd": WL("ragged_bwd", 200, 264, 8, 2, 328, W.BF16, ST, 0.0, 0.8, 67),
+    # the training forward's down projection split in two K halves
+    "split_bwd": WL("split_bwd", 600, 520, 4, 2, 2080, W.BF16, TK, 0.0, 0.0, 68),
 }
 
 

@@ -34,6 +34,9 @@ CASES = {
     "rows300_f8": WL("rows300_f8", 1200, 256, 4, 1, 128, W.BF16, TK, 0.0, 0.0, 96),
     # ~600 rows per expert: 256-row tiles
     "rows600_f8": WL("rows600_f8", 2400, 256, 4, 1, 128, W.BF16, TK, 0.0, 0.0, 97),
+    # the down projection split in two K halves (256-row and 128-row tiles)
+    "split_f8": WL("split_f8", 2400, 528, 4, 1, 2080, W.BF16, TK, 0.0, 0.0, 98),
+    "split128_f8": WL("split128_f8", 800, 528, 4, 1, 2080, W.BF16, TK, 0.0, 0.0, 99),
 }
 
 

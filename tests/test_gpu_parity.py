@@ -36,6 +36,9 @@ SMALL = {
     "decode_s": WL("decode_s", 24, 512, 64, 8, 320, W.BF16, TK, 0.0, 0.0, 16),
     # the widest routing the ABI takes
     "wide_k": WL("wide_k", 300, 64, 256, 32, 64, W.BF16, ST, 0.0, 0.0, 17),
+    # d_ff >= 2048 with few tiles: the down projection runs as two K halves
+    # (d_ff / 2 = 1040 leaves a K tail in each half; N tail 520 = 2 x 256 + 8)
+    "split_down": WL("split_down", 600, 520, 4, 2, 2080, W.BF16, TK, 0.0, 0.8, 18),
 }
 
 
