@@ -46,6 +46,15 @@ def _parse():
     ap.add_argument("--backward", action="store_true",
                     help="also time the training step (moe_forward_train + "
                          "moe_backward) and report the backward's GEMM rate")
+    ap.add_argument("--library-loop", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the vendor-library form of the same FFN on "
+                         "the same permuted rows: one hipBLASLt GEMM per expert "
+                         "and projection (torch.nn.functional.linear) plus the "
+                         "SwiGLU in torch; context for the grouped FFN only")
+    ap.add_argument("--sample-power", action=argparse.BooleanOptionalAction, default=True,
+                    help="also run the grouped FFN back to back for a few "
+                         "seconds while amd-smi samples socket power and the "
+                         "graphics clock; reports the MFMA peak at that clock")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -101,6 +110,115 @@ def _time_loop(fn, steps, stream):
     e.record(stream)
     e.synchronize()
     return s.elapsed_time(e) / steps  # ms per call
+
+
+def _smi_sample():
+    """One amd-smi reading: (socket power in W, mean graphics clock over the
+    XCDs in MHz), or None where amd-smi is missing or prints no such field."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"],
+                           capture_output=True, text=True, timeout=10)
+        js = json.loads(r.stdout)
+    except Exception:
+        return None
+    gpu = js[0] if isinstance(js, list) else js.get("gpu_data", [js])[0]
+    try:
+        watts = float(gpu["power"]["socket_power"]["value"])
+        clk = [float(v["clk"]["value"]) for k, v in gpu["clock"].items()
+               if k.startswith("gfx_") and isinstance(v, dict)
+               and isinstance(v.get("clk"), dict) and v["clk"].get("value") not in (None, "N/A")]
+    except (KeyError, TypeError, ValueError):
+        return None
+    return watts, (sum(clk) / len(clk) if clk else None)
+
+
+def _sample_power(fn, flops, stream, secs=4.0):
+    """Runs fn back to back for about `secs` seconds while a thread samples
+    amd-smi every 0.2 s; reports the medians (the first two samples, taken
+    while the clock ramps, are dropped), the event-timed rate and the bf16
+    MFMA peak scaled to the sampled clock (the 2.5 PFLOP/s figure is quoted
+    at 2400 MHz)."""
+    import threading
+    import torch
+    samples, done = [], threading.Event()
+
+    def sampler():
+        while not done.is_set():
+            v = _smi_sample()
+            if v is not None:
+                samples.append(v)
+            done.wait(0.2)
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    t0, n = time.perf_counter(), 0
+    s.record(stream)
+    while time.perf_counter() - t0 < secs:
+        for _ in range(10):
+            fn()
+        n += 10
+        torch.cuda.synchronize()
+    e.record(stream)
+    e.synchronize()
+    done.set()
+    th.join()
+    ms = s.elapsed_time(e) / n
+    tflops = flops / (ms * 1e-3) / 1e12
+    kept = samples[2:] or samples
+    if not kept:
+        return {"ms_per_call": ms, "tflops": tflops, "samples": 0}
+    med = lambda xs: sorted(xs)[len(xs) // 2]  # noqa: E731
+    watts = med([w for w, _ in kept])
+    clks = [c for _, c in kept if c is not None]
+    clk = med(clks) if clks else None
+    out = {"ms_per_call": ms, "tflops": tflops, "samples": len(kept),
+           "socket_power_w": watts, "gfx_clock_mhz": clk}
+    if clk:
+        peak = PEAK_BF16_TFLOPS * clk / 2400.0
+        out.update(mfma_peak_at_clock_tflops=peak, frac_at_clock=tflops / peak)
+    return out
+
+
+def _library_loop(wl, dev, perm, n, stream, flops, fns_only=False):
+    """The grouped FFN's work done the plain way on the same permuted rows:
+    per expert, one hipBLASLt GEMM for gate|up (the two weights stacked), the
+    SwiGLU in torch, one GEMM for the down projection (bf16 out).  Expert
+    boundaries are read to the host before timing.  Also the two GEMMs alone
+    (down projection on a fixed H), the library's best case."""
+    import torch
+    import torch.nn.functional as F
+    o = perm["offsets"].cpu().tolist()
+    Xp, Wd, dff = perm["X_perm"], dev["W_down"], wl.d_ff
+    Wgu = torch.cat([dev["W_gate"], dev["W_up"]], dim=1).contiguous()
+    Hf = torch.empty((o[-1], dff), dtype=torch.bfloat16, device="cuda").normal_(0.0, 0.05)
+    live = [e for e in range(wl.E) if o[e + 1] > o[e]]
+
+    def ffn_loop():
+        for e in live:
+            gu = F.linear(Xp[o[e]:o[e + 1]], Wgu[e])
+            F.linear(F.silu(gu[:, :dff]) * gu[:, dff:], Wd[e])
+
+    def gemms_only():
+        for e in live:
+            F.linear(Xp[o[e]:o[e + 1]], Wgu[e])
+            F.linear(Hf[o[e]:o[e + 1]], Wd[e])
+    if fns_only:
+        return gemms_only
+    for _ in range(2):
+        ffn_loop()
+        gemms_only()
+    t_loop = _time_loop(ffn_loop, n, stream)
+    t_gemm = _time_loop(gemms_only, n, stream)
+    del Wgu, Hf
+    return {"what": "per-expert hipBLASLt GEMMs (torch.nn.functional.linear) on "
+                    "the same permuted rows",
+            "ms_ffn_loop": t_loop, "ms_gemms_only": t_gemm,
+            "gemms_only_tflops": flops / (t_gemm * 1e-3) / 1e12}
 
 
 def _cpu_baseline(wl, dev, ntok, min_s=10.0, max_s=30.0, shared=None, fp8_scales=None):
@@ -369,6 +487,13 @@ def main():
             "backward_gemm_flops": bwd_flops,
             "backward_tflops": bwd_flops / (t_bwd * 1e-3) / 1e12,
             "backward_frac_of_bf16_peak": bwd_flops / (t_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    if args.sample_power:
+        line["power"] = _sample_power(lambda: ffn(Y, ffn_ws), ffn_flops, stream)
+        if args.library_loop and not args.fp8 and wl.dtype == W.BF16:
+            lib = _library_loop(wl, dev, perm, 1, stream, ffn_flops, fns_only=True)
+            line["power_library_gemms"] = _sample_power(lib, ffn_flops, stream)
+    if args.library_loop and not args.fp8 and wl.dtype == W.BF16:
+        line["library_loop"] = _library_loop(wl, dev, perm, n, stream, ffn_flops)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = _cpu_baseline(
             wl, dev, args.cpu_sample_tokens,
