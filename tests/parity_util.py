@@ -26,6 +26,38 @@ BF16_TOL = 2e-2
 GATE_W_TOL = 1e-4
 
 
+U_BF16 = 2.0 ** -8   # bf16 unit roundoff
+
+
+def h_rounding_bound(X_perm, offsets, W_gate, W_up, W_down):
+    """Per kept row r and output column i, u * sum_j |H_rj| |W_down[e]_ij|
+    (u = 2^-8): the largest change of Y_perm that rounding the hidden
+    activation H (stored in the activation dtype, bf16) can cause, since each
+    H element moves by at most u |H|.  From fp64 values of the oracle's own
+    H; rows in expert order as in X_perm."""
+    X_perm = np.asarray(X_perm, np.float64)
+    out = np.zeros((X_perm.shape[0], np.shape(W_down)[1]))
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        A = X_perm[lo:hi]
+        G = A @ np.asarray(W_gate[e], np.float64).T
+        U = A @ np.asarray(W_up[e], np.float64).T
+        H = O.silu(G) * U
+        out[lo:hi] = U_BF16 * (np.abs(H) @ np.abs(np.asarray(W_down[e], np.float64)).T)
+    return out
+
+
+def bounded_err(g, o, B):
+    """max |g - o| / (BF16_TOL rms(o) + B), elementwise allowance B."""
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    if o.size == 0:
+        return 0.0
+    return float(np.max(np.abs(g - o) / (BF16_TOL * rms(o) + B + 1e-300)))
+
+
 def rms(o):
     return float(np.sqrt(np.mean(np.square(o)))) if o.size else 0.0
 

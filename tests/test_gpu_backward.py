@@ -13,7 +13,9 @@ errors of independent terms add in quadrature); every element of every
 gradient must satisfy |g - o| <= 6 sigma + 1e-5 rms(o) (the second term
 covers fp32 accumulation).  The same model applied to a CPU simulation of
 the rounding points gives at most 3.7 sigma on the shapes below.  Over each
-tensor, rms(g - o) / rms(o) <= 1e-2 as well.  Exact checks: zero
+tensor, rms(g - o) / rms(o) <= 1e-2 as well, or, where the exact values
+cancel (a router-bias gradient of three experts sums terms of both signs),
+rms(g - o) <= 2 rms(sigma).  Exact checks: zero
 gradients of unused experts and of fully dropped tokens, zero router
 gradient at top-1 with the softmax of the selected logit, the training
 forward's output equal to moe_forward's bit for bit, two backward runs
@@ -153,11 +155,12 @@ def _error_sigma(host, dout, k, cf, gating, idx):
 
 def check_gradients(name, wl, g, o, sigma):
     """Every gradient element within Z_MAX sigma of the oracle (plus the fp32
-    floor), rms error <= BWD_RMS_TOL, unused experts exactly zero, and no
-    router gradient at top-1 with the softmax of the selected logit."""
+    floor), rms error <= BWD_RMS_TOL or at most twice the rms of sigma,
+    unused experts exactly zero, and no router gradient at top-1 with the
+    softmax of the selected logit."""
     kept = np.diff(o["offsets"]) > 0
     exact_router = wl.top_k == 1 and wl.gating == TK
-    ratio, rms_errs = {}, {}
+    ratio, rms_errs, rms_sig = {}, {}, {}
     for key in ("dX", "dW_r", "dbias", "dW_gate", "dW_up", "dW_down"):
         if g.get(key) is None:
             continue
@@ -170,6 +173,8 @@ def check_gradients(name, wl, g, o, sigma):
         floor = FP32_FLOOR * np.sqrt(np.mean(o[key] ** 2))
         ratio[key] = float(np.max(np.abs(got - o[key]) / (sigma[key] + floor + 1e-300)))
         rms_errs[key] = _rms_err(got, o[key])
+        rms_sig[key] = float(np.sqrt(np.mean(np.square(got - o[key]))) /
+                             max(np.sqrt(np.mean(np.square(sigma[key] + floor))), 1e-300))
         del got
     print(f"[backward] {name}: max |g - o| / sigma " +
           ", ".join(f"{k} {v:.2f}" for k, v in ratio.items()), flush=True)
@@ -178,7 +183,8 @@ def check_gradients(name, wl, g, o, sigma):
           f"; unused experts {int((~kept).sum())}", flush=True)
     for key in ratio:
         assert ratio[key] <= Z_MAX, f"{key}: error {ratio[key]:.2f} sigma"
-        assert rms_errs[key] <= BWD_RMS_TOL, f"{key}: rms {rms_errs[key]:.3e}"
+        assert rms_errs[key] <= BWD_RMS_TOL or rms_sig[key] <= 2.0, \
+            f"{key}: rms {rms_errs[key]:.3e} ({rms_sig[key]:.2f} rms sigma)"
 
 
 @pytest.mark.parametrize("name", list(CASES))
