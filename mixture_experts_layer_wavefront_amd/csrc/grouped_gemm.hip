@@ -114,19 +114,18 @@ __device__ __forceinline__ uint32_t swz(uint32_t R) {
 }
 
 // Eight FP8 E4M3 codes (little-endian bytes) -> eight bf16 values.  Every
-// E4M3 value is exactly representable in bf16: decode to fp32 with the
-// hardware conversion, keep the upper 16 bits.
+// E4M3 value is exactly representable in bf16: gfx950's scaled conversion
+// (v_cvt_scalef32_pk_bf16_fp8, scale 1, so exact) turns two codes into a
+// packed bf16 pair in one instruction; the expert's scale is applied to the
+// fp32 accumulators instead.
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint2 q) {
-  typedef __attribute__((ext_vector_type(2))) float f32x2;
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, true);
-  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, false);
-  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, true);
-  auto pk = [](float lo, float hi) {
-    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
-  };
-  const i32x4 w = {(int)pk(a[0], a[1]), (int)pk(b[0], b[1]), (int)pk(c[0], c[1]),
-                   (int)pk(d[0], d[1])};
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)q.x, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)q.x, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)q.y, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)q.y, 1.0f, true);
+  const i32x4 w = {__builtin_bit_cast(int, a), __builtin_bit_cast(int, b),
+                   __builtin_bit_cast(int, c), __builtin_bit_cast(int, d)};
   return __builtin_bit_cast(bf16x8, w);
 }
 
