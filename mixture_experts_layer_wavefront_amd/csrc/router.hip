@@ -429,7 +429,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
 // Few tokens (bf16): K-split FMA partial logits (no W_r split) + select.
 constexpr int kSmallT = 64;
 #ifndef MOE_RKS
-#define MOE_RKS 128
+#define MOE_RKS 64
 #endif
 constexpr int kSmallKS = MOE_RKS;  // K per workgroup
 
@@ -607,7 +607,9 @@ RoutePlan route_plan(int T, int E, int d, bool x_bf16, bool stats) {
   if (T <= kSmallT || !x_bf16) {
     P.small = true;
     P.EP = E <= 8 ? 8 : E <= 16 ? 16 : E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256;
-    P.S = (d + kSmallKS - 1) / kSmallKS;
+    // fp32 X (statistics requested): one partial over all of K, so the
+    // logits equal the fused kernel's bit for bit
+    P.S = x_bf16 ? (d + kSmallKS - 1) / kSmallKS : 1;
     P.split_bytes = 0;
     P.partial_bytes = a256r((size_t)P.S * T * P.EP * 4);
     return P;
@@ -650,7 +652,7 @@ hipError_t launch_partial(const XT* X, const float* W_r, int T, int d, int E,
   constexpr int TT = (kRouterThreads / TX) * RT;
   const dim3 grid((T + TT - 1) / TT, S);
   router_topk_kernel<TX, RE, RT, XT, true><<<grid, kRouterThreads, 0, stream>>>(
-      X, W_r, nullptr, T, d, E, 0, 0, nullptr, nullptr, kSmallKS, partial);
+      X, W_r, nullptr, T, d, E, 0, 0, nullptr, nullptr, S == 1 ? d : kSmallKS, partial);
   return hipGetLastError();
 }
 
