@@ -37,6 +37,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
 constexpr uint32_t kOob = 0x80000000u;
 
 // Wave-wide reductions (64 lanes) via cross-lane shuffles.
+// M-tiles of an expert with `rows` rows under a tile code: tiles of
+// (code & 0xFFFF) rows, and a remainder of at most (code >> 16) rows joins
+// the last full tile instead of taking a tile of its own.
+constexpr int kTallTileCode = 256 | (64 << 16);
+__host__ __device__ __forceinline__ int m_tiles(int rows, int code) {
+  const int step = code & 0xFFFF, extra = code >> 16;
+  const int full = rows / step, rem = rows - full * step;
+  return (rem == 0 || (full > 0 && rem <= extra)) ? full : full + 1;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);

@@ -141,11 +141,11 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 __global__ __launch_bounds__(256) void ffn_schedule_kernel(
-    const int32_t* __restrict__ offsets, int E, int BM,
+    const int32_t* __restrict__ offsets, int E, int tile_code,
     int32_t* __restrict__ mt_prefix) {
   __shared__ int32_t s[256];
   const int e = threadIdx.x;
-  const int mt = (e < E) ? (offsets[e + 1] - offsets[e] + BM - 1) / BM : 0;
+  const int mt = (e < E) ? m_tiles(offsets[e + 1] - offsets[e], tile_code) : 0;
   s[e] = mt;
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {
@@ -296,6 +296,13 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   constexpr int RBA = Cfg::RBA, RBB = Cfg::RBB, CPRA = Cfg::CPRA, CPRB = Cfg::CPRB;
   constexpr int RPIA = Cfg::RPIA, RPIB = Cfg::RPIB, NIA = Cfg::NIA, AREG = Cfg::AREG;
   constexpr int KSUB = Cfg::KSUB;
+  // Tall tiles (TM = 5): M-tiles step by 256 rows, and an expert's last tile
+  // also takes a remainder of up to 64 rows (the schedule merges it instead
+  // of giving it a tile of its own that would stream the whole weight tile
+  // for a few rows).
+  constexpr bool TALL = TM == 5;
+  static_assert(!TALL || (MW == 2 && NS == 2 && !AT), "tall tiles: 2 wave rows, 2 stages, NT A");
+  constexpr int MSTEP = TALL ? 256 : BM;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   int32_t* s_pref = reinterpret_cast<int32_t*>(smem + NS * STAGE);
 
@@ -364,8 +371,8 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
     local -= half * mt_e * n_nt;
     const int n_t = local / mt_e, m_t = local % mt_e;
     const int row_end = offsets[e + 1];
-    m_start = offsets[e] + m_t * BM;
-    rows = min(BM, row_end - m_start);
+    m_start = offsets[e] + m_t * MSTEP;
+    rows = (m_t == mt_e - 1) ? row_end - m_start : MSTEP;
     n0 = n_t * BN;
     ncols = min(BN, N - n0);
     K = g.K;
@@ -412,54 +419,60 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   // ---- per-lane load offsets (one 16-byte chunk per wave-level load) -------
   // Loads 0..NIA-1 fill the A region, the rest the B region.  NT: R is the
   // region-local row (B-local for the swizzle), kcol the first K element of
-  // the lane's chunk.  T: R is the k row within the stage.
-  uint32_t voff[IPW];
-  int kcol[IPW];
-  {
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int qi = wave + LW * i;
-      if (qi < NIA) {
-        const uint32_t R = qi * RPIA + lane / CPRA;
-        if constexpr (AT) {
-          const uint32_t c = (lane % CPRA) ^ swz_t(R);
-          voff[i] = R * kbytes + c * 16;
-          kcol[i] = 0;
-        } else {
-          const uint32_t c = (lane % CPRA) ^ swz<CPRA>(R);
-          voff[i] = R * kbytes + c * 16;
-          kcol[i] = c * 8;
-        }
+  // the lane's chunk.  T: R is the k row within the stage.  Computed when
+  // the load is issued (a few integer operations) rather than held in
+  // registers across the K loop.
+  auto load_off = [&](int i) __attribute__((always_inline)) -> uint2 {
+    const int qi = wave + LW * i;
+    uint32_t voff;
+    int kcol;
+    if (qi < NIA) {
+      const uint32_t R = qi * RPIA + lane / CPRA;
+      if constexpr (AT) {
+        const uint32_t c = (lane % CPRA) ^ swz_t(R);
+        voff = R * kbytes + c * 16;
+        kcol = 0;
       } else {
-        const uint32_t R = (qi - NIA) * RPIB + lane / CPRB;
-        if constexpr (BT) {
-          const uint32_t c = (lane % CPRB) ^ swz_t(R);
-          voff[i] = R * kbytesB + c * 16;
-          kcol[i] = 0;
-        } else {
-          const uint32_t c = (lane % CPRB) ^ swz<CPRB>(R);
-          const uint32_t row = (GATEUP && R >= (uint32_t)BN) ? R - BN : R;
-          voff[i] = row * kbytesB + c * 16;
-          kcol[i] = c * (BF8 ? 16 : 8);
-        }
+        const uint32_t c = (lane % CPRA) ^ swz<CPRA>(R);
+        voff = R * kbytes + c * 16;
+        kcol = c * 8;
+      }
+    } else {
+      const uint32_t R = (qi - NIA) * RPIB + lane / CPRB;
+      if constexpr (BT) {
+        const uint32_t c = (lane % CPRB) ^ swz_t(R);
+        voff = R * kbytesB + c * 16;
+        kcol = 0;
+      } else {
+        const uint32_t c = (lane % CPRB) ^ swz<CPRB>(R);
+        const uint32_t row = (GATEUP && R >= (uint32_t)BN) ? R - BN : R;
+        voff = row * kbytesB + c * 16;
+        kcol = c * (BF8 ? 16 : 8);
       }
     }
-  }
+    return uint2{voff, (uint32_t)kcol};
+  };
   const int nk = (K + BK - 1) / BK;
   const bool ktail = (K % BK) != 0;
   // bytes a stage advances along K
   const uint32_t stepA = AT ? (uint32_t)BK * kbytes : (uint32_t)RBA;
   const uint32_t stepB = BT ? (uint32_t)BK * kbytesB : (uint32_t)RBB;
 
-  auto issue = [&](int stage, int kt) {
+  auto issue = [&](int stage, int kt) __attribute__((always_inline)) {
     if (LW < NWAVES && wave >= LW) return;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int qi = wave + LW * i;
       const bool is_a = qi < NIA;
-      uint32_t vo = voff[i] + (uint32_t)kt * (is_a ? stepA : stepB);
+      // a tall kernel's 256-row tile: the rows of the 64-row extension are
+      // not loaded (their sub-tiles issue no MFMA; with two stages every
+      // wait is for all of a wave's loads, so the count may vary)
+      if (TALL && is_a && qi * RPIA >= 256 && rows <= 256) continue;
+      const uint2 lo = load_off(i);
+      const int kc = (int)lo.y;
+      uint32_t vo = lo.x + (uint32_t)kt * (is_a ? stepA : stepB);
       const bool t_layout = is_a ? AT : BT;
-      if (!t_layout && ktail && kt * BK + kcol[i] >= K) vo = kOob;
+      if (!t_layout && ktail && kt * BK + kc >= K) vo = kOob;
       char* dst = smem + stage * STAGE + qi * 1024;
       if (is_a)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, MOE_LDS_PTR(dst), 16, vo, 0, 0, 0);
@@ -479,15 +492,33 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
 #else
   const int wm = wave % MW, wn = wave / MW;
 #endif
-  // row sub-tiles of this wave that hold any of the tile's rows
-  int tm_active = (rows - wm * TM * 32 + 31) / 32;
-  tm_active = tm_active < 0 ? 0 : (tm_active > TM ? TM : tm_active);
+  // Rows of the wave's sub-tiles: wave row wm covers rows wm * TM * 32 +
+  // 32 mi; a tall kernel's tiles of at most 256 rows use 4 sub-tiles per
+  // wave row (wm * 128 + 32 mi) so the two wave rows stay balanced, and the
+  // fifth is placed past every tile row (never read, never stored).
+  const int wrows = (TALL && rows <= 256) ? 128 : TM * 32;
+  auto sub_row0 = [&](int mi) { return mi * 32 < wrows ? wm * wrows + mi * 32 : 1 << 16; };
+  // row sub-tiles of this wave that hold any of the tile's rows (a prefix
+  // of 0..TM-1)
+  int tm_active = (rows - wm * wrows + 31) / 32;
+  tm_active = tm_active < 0 ? 0 : (tm_active > wrows / 32 ? wrows / 32 : tm_active);
   // NT: per (sub-tile, k-step) offsets.  T: per sub-tile offsets at k = 0
-  // (k-step ks adds ks * 16 rows).
-  uint32_t offA[TM][AT ? 1 : KSUB], offB[NB][BT ? 1 : KSUB];
+  // (k-step ks adds ks * 16 rows).  NT A with 128-byte rows (ACOMPACT):
+  // sub-tile mi's rows are 32 mi past sub-tile 0's, which moves its chunk
+  // swizzle by 4 when mi is odd, i.e. turns k-step ks into ks ^ 2; so
+  // offA(mi, ks) = abase[ks ^ 2 (mi & 1)] + 4096 mi and only abase is held.
+  // The same holds for the B sub-tiles (BCOMPACT): sub-tile nj sits bj(nj)
+  // 32-row blocks past the wave's first B row.
+  constexpr bool ACOMPACT = !AT && CPRA == 8;
+  constexpr bool BCOMPACT = !BT && !BF8 && CPRB == 8;
+  uint32_t offA[ACOMPACT ? 1 : TM][AT ? 1 : KSUB], offB[BCOMPACT ? 1 : NB][BT ? 1 : KSUB];
+  uint32_t abase[KSUB], bbase[KSUB];
+  // B sub-tile nj: 32-row blocks past B-local row wn * TN * 32 (gate/up: the
+  // up rows start BN rows on)
+  auto bj = [](int nj) { return (GATEUP && nj >= TN) ? nj + (NW - 1) * TN : nj; };
   if constexpr (AT) {
 #pragma unroll
-    for (int mi = 0; mi < TM; ++mi) offA[mi][0] = tr_lane_off(lane, wm * TM * 32 + mi * 32, RBA);
+    for (int mi = 0; mi < TM; ++mi) offA[mi][0] = tr_lane_off(lane, sub_row0(mi), RBA);
   }
   if constexpr (BT) {
 #pragma unroll
@@ -497,14 +528,20 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
 #pragma unroll
   for (int ks = 0; ks < KSUB; ++ks) {
     const uint32_t c = 2 * ks + (lane >> 5);
-    if constexpr (!AT) {
+    if constexpr (ACOMPACT) {
+      const uint32_t R = sub_row0(0) + (lane & 31);
+      abase[ks] = R * RBA + ((c ^ swz<CPRA>(R)) * 16);
+    } else if constexpr (!AT) {
 #pragma unroll
       for (int mi = 0; mi < TM; ++mi) {
-        const uint32_t R = wm * TM * 32 + mi * 32 + (lane & 31);
+        const uint32_t R = sub_row0(mi) + (lane & 31);
         offA[mi][ks] = R * RBA + ((c ^ swz<CPRA>(R)) * 16);
       }
     }
-    if constexpr (!BT) {
+    if constexpr (BCOMPACT) {
+      const uint32_t R = wn * TN * 32 + (lane & 31);
+      bbase[ks] = AREG + R * RBB + ((c ^ swz<CPRB>(R)) * 16);
+    } else if constexpr (!BT) {
 #pragma unroll
       for (int nj = 0; nj < NB; ++nj) {
         uint32_t brow;
@@ -528,10 +565,13 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
       for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.f;
 
   // NS-stage pipeline: stage kt+NS-1 is requested while stage kt is consumed.
-  // RAGGED: only the row sub-tiles of this wave that hold rows issue MFMAs
-  // (and read their A fragments); full tiles take the branch-free loop.
-  auto kloop = [&](auto ragged) {
-    constexpr bool RAGGED = decltype(ragged)::value;
+  // NA = the number of row sub-tiles that hold rows, when known at compile
+  // time (full tiles; a tall kernel's 256-row tiles): branch-free loops over
+  // them.  NA < 0 (ragged tiles): only the tm_active sub-tiles that hold rows
+  // issue MFMAs and read their A fragments.
+  auto kloop = [&](auto na) {
+    constexpr int NA = decltype(na)::value;
+    auto active = [&](int mi) { return NA < 0 ? mi < tm_active : mi < NA; };
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
       if (s < nk) issue(s, s);
@@ -544,29 +584,41 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
       for (int ks = 0; ks < KSUB; ++ks) {
         bf16x8 a[TM], b[NB];
 #pragma unroll
-        for (int mi = 0; mi < TM; ++mi)
-          if (!RAGGED || mi < tm_active) {
-            if constexpr (AT) a[mi] = lds_frag_tr(st + offA[mi][0] + ks * 16 * RBA, RBA);
-            else a[mi] = *reinterpret_cast<const bf16x8*>(st + offA[mi][ks]);
-          }
-#pragma unroll
         for (int nj = 0; nj < NB; ++nj) {
           if constexpr (BT) b[nj] = lds_frag_tr(st + offB[nj][0] + ks * 16 * RBB, RBB);
           else if constexpr (BF8) b[nj] = fp8x8_to_bf16x8(*reinterpret_cast<const uint2*>(st + offB[nj][ks]));
+          else if constexpr (BCOMPACT)
+            b[nj] = *reinterpret_cast<const bf16x8*>(st + bbase[ks ^ (2 * (bj(nj) & 1))] + 4096 * bj(nj));
           else b[nj] = *reinterpret_cast<const bf16x8*>(st + offB[nj][ks]);
         }
 #pragma unroll
         for (int mi = 0; mi < TM; ++mi)
-          if (!RAGGED || mi < tm_active) {
+          if (active(mi)) {
+            if constexpr (AT) a[mi] = lds_frag_tr(st + offA[mi][0] + ks * 16 * RBA, RBA);
+            else if constexpr (ACOMPACT)
+              a[mi] = *reinterpret_cast<const bf16x8*>(st + abase[ks ^ (2 * (mi & 1))] + 4096 * mi);
+            else a[mi] = *reinterpret_cast<const bf16x8*>(st + offA[mi][ks]);
+          }
+#pragma unroll
+        for (int mi = 0; mi < TM; ++mi)
+          if (active(mi)) {
 #pragma unroll
             for (int nj = 0; nj < NB; ++nj)
               acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[nj], acc[mi][nj], 0, 0, 0);
           }
+        // tall kernels (256 VGPRs): all of the k-step's LDS reads, then its
+        // MFMAs; left to itself the scheduler waits on each fragment just
+        // before its first MFMA (measured: Mixtral layer 2.91 -> 2.78 ms)
+        if constexpr (TALL && NA > 0) {
+          __builtin_amdgcn_sched_group_barrier(0x100, NA + NB, 0);  // DS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, NA * NB, 0);  // MFMAs
+        }
       }
     }
   };
-  if (!MOE_SKIP || tm_active == TM) kloop(std::false_type{});
-  else kloop(std::true_type{});
+  if (!MOE_SKIP || tm_active == TM) kloop(std::integral_constant<int, TM>{});
+  else if (TALL && tm_active == 4) kloop(std::integral_constant<int, 4>{});
+  else kloop(std::integral_constant<int, -1>{});
 
   // FP8 weights: the expert's scales multiply the accumulators
   if constexpr (BF8) {
@@ -584,7 +636,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   // acc[mi][nj][r] is element (row, col) of the tile with
   //   row = wm*TM*32 + mi*32 + 8*(r/4) + 4*(lane/32) + r%4,  col = lane%32 (+ sub-tile base)
   const int col_l = lane & 31;
-  const int rbase = wm * TM * 32 + 4 * (lane >> 5);
+  const int rlane = 4 * (lane >> 5);
   if constexpr (GATEUP) {
     uint16_t* H = static_cast<uint16_t*>(Cout);
 #pragma unroll
@@ -595,7 +647,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
       for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = rbase + mi * 32 + 8 * (r >> 2) + (r & 3);
+          const int row = sub_row0(mi) + rlane + 8 * (r >> 2) + (r & 3);
           if (row < rows) {
             const float gv = acc[mi][nj][r], u = acc[mi][nj + TN][r];
             const float h = gv / (1.f + __expf(-gv)) * u;
@@ -639,7 +691,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
       for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const uint32_t row = wm * TM * 32 + mi * 32 + h * 16 + (lane >> 2);
+          const uint32_t row = sub_row0(mi) + h * 16 + (lane >> 2);
           const uint32_t vo = row * (uint32_t)N * 2u + (uint32_t)(n0 + cb + 8 * (lane & 3)) * 2u;
           char* dg = wreg + mi * 4096 + h * 1024;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rG, MOE_LDS_PTR(dg), 16, vo, 0, 0, 0);
@@ -657,7 +709,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int r = 4 * q + j;
-            const int row = rbase + mi * 32 + 8 * q + j;
+            const int row = sub_row0(mi) + rlane + 8 * q + j;
             if (row < rows && col < ncols) {
               const float gv = bf16_bits_to_f32((uint16_t)gq[j]);
               const float u = bf16_bits_to_f32((uint16_t)uq[j]);
@@ -684,7 +736,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
       for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = rbase + mi * 32 + 8 * (r >> 2) + (r & 3);
+          const int row = sub_row0(mi) + rlane + 8 * (r >> 2) + (r & 3);
           if (row < rows) {
             const int m = m_start + row;
             float* dst = m < ms ? C0 + ((int64_t)e * ms + m) * N
@@ -703,7 +755,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
       for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = rbase + mi * 32 + 8 * (r >> 2) + (r & 3);
+          const int row = sub_row0(mi) + rlane + 8 * (r >> 2) + (r & 3);
           if (row < rows) Y[(int64_t)(m_start + row) * N + n0 + col] = acc[mi][nj][r];
         }
     }
@@ -773,7 +825,8 @@ hipError_t launch_gemm_args(const GemmArgs& a, int64_t R, hipStream_t stream) {
     tiles = (int64_t)a.E * ((a.M + Cfg::BM - 1) / Cfg::BM) * n_nt;
   } else {
     // upper bound on M-tiles: every expert may add one partial tile
-    const int64_t mt_max = (R + Cfg::BM - 1) / Cfg::BM + std::min<int64_t>(a.E, R);
+    constexpr int MSTEP = TM == 5 ? 256 : Cfg::BM;  // tall tiles step by 256 rows
+    const int64_t mt_max = (R + MSTEP - 1) / MSTEP + std::min<int64_t>(a.E, R);
     tiles = mt_max * n_nt * ((MODE == 4 || MODE == 5) ? 2 : 1);
   }
   const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
@@ -861,6 +914,11 @@ bool ffn_split_down(bool bf16, int E, int rows_per_expert, int d, int d_ff) {
   return tiles < 4 * 256;
 }
 
+int ffn_tile_code(bool bf16, int rows_per_expert, bool fp8) {
+  const int bm = ffn_tile_rows(bf16, rows_per_expert, fp8);
+  return (bm == 256 && !fp8 && rows_per_expert > MOE_BNT_ROWS) ? kTallTileCode : bm;
+}
+
 int ffn_tile_rows(bool bf16, int rows_per_expert, bool fp8) {
   if (!bf16) return 0;
   if (rows_per_expert <= 64) return 32;
@@ -920,8 +978,9 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
     if (err != hipSuccess) return err;
     return launch_gemm<1, MOE_SNW, 1, 1, false, MOE_SBK, MOE_SNS, MOE_SBAUX>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
   }
+  const int code = ffn_tile_code(bf16, rows_per_expert, fp8);
   if (!prefix_ready) {
-    ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, bm, mt_prefix);
+    ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, code, mt_prefix);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (fp8 && bm == 128) {
@@ -950,9 +1009,11 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
     if (err != hipSuccess) return err;
     return launch_down<2, MOE_NW, 4, MOE_DTN / MOE_NW, MOE_BK, MOE_NS, kNonTemporal, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr, defer);
   }
-  err = launch_gemm<2, MOE_NW, 4, 4 / MOE_NW, true, MOE_BK, MOE_NS, 0>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
+  // several M-tiles per expert: tall tiles (the schedule merges remainders
+  // of up to 64 rows into the expert's last tile)
+  err = launch_gemm<2, MOE_NW, 5, 4 / MOE_NW, true, MOE_BK, 2, 0>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
   if (err != hipSuccess) return err;
-  return launch_down<2, MOE_NW, 4, MOE_DTN / MOE_NW, MOE_BK, MOE_NS, 0, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr, defer);
+  return launch_down<2, MOE_NW, 5, MOE_DTN / MOE_NW, MOE_BK, 2, 0, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr, defer);
 }
 
 }  // namespace moe

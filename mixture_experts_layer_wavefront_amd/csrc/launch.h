@@ -22,13 +22,13 @@ hipError_t launch_route(const void* X, bool x_bf16, const float* W_r,
 // Permute, three kernels: per-block counts and in-block ranks; one-block
 // scan with capacity; destination rows and the row copy (one kernel for few
 // copies).  With mt_prefix != nullptr it also writes the grouped FFN's tile
-// schedule for tiles of bm rows (see launch_grouped_ffn).
+// schedule: M-tiles per expert under tile_code (m_tiles; see launch_grouped_ffn).
 size_t permute_scratch_bytes(int T, int k, int E);
 hipError_t launch_permute(const void* X, bool x_bf16, const int32_t* topk_idx,
                           int T, int d, int E, int k, int C,
                           int32_t* counts, int32_t* offsets, int32_t* dropped,
                           int32_t* dest_row, int32_t* row_token, void* X_perm,
-                          void* scratch, int32_t* mt_prefix, int bm,
+                          void* scratch, int32_t* mt_prefix, int tile_code,
                           hipStream_t stream);
 
 // Grouped SwiGLU FFN.  `rows_per_expert` (the mean, known on the host from
@@ -41,6 +41,10 @@ hipError_t launch_permute(const void* X, bool x_bf16, const int32_t* topk_idx,
 // shapes whose 256 x 256 tiles fill the chip only a few times; the second
 // half's partial sums need R d fp32 more scratch.
 int ffn_tile_rows(bool bf16, int rows_per_expert, bool fp8 = false);
+// The M-tile code of moe_forward's grouped FFN (m_tiles): ffn_tile_rows, or
+// 256-row tiles that take remainders of up to 64 rows (bf16, more than 256
+// rows per expert).
+int ffn_tile_code(bool bf16, int rows_per_expert, bool fp8 = false);
 bool ffn_split_down(bool bf16, int E, int rows_per_expert, int d, int d_ff);
 size_t ffn_scratch_bytes(int64_t R, int E, int d, int d_ff, bool bf16, int rows_per_expert);
 hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,

@@ -153,7 +153,7 @@ hipError_t enqueue_routed(const moe_problem_t* p, const void* X, const float* W_
                                    router_stats, stream);
   if (e != hipSuccess) return e;
   // the permute also writes the FFN's tile schedule (start of its scratch)
-  const int bm = moe::ffn_tile_rows(bf, mean_rows_per_expert(p), w_scales != nullptr);
+  const int bm = moe::ffn_tile_code(bf, mean_rows_per_expert(p), w_scales != nullptr);
   int32_t* mt_prefix = bm > 0 ? reinterpret_cast<int32_t*>(ws + L.ffn_scratch) : nullptr;
   e = moe::launch_permute(X, bf, topk_idx, p->T, p->d_model, p->E, p->top_k,
                           capacity_int(p), counts, offsets, dropped, dest_row, row_token,

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kPermThreads) void count_rank_kernel(
 __global__ __launch_bounds__(256) void scan_kernel(
     int32_t* __restrict__ block_counts, int nblk, int E, int C,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ dropped, int32_t* __restrict__ mt_prefix, int bm) {
+    int32_t* __restrict__ dropped, int32_t* __restrict__ mt_prefix, int tile_code) {
   __shared__ int32_t s_kept[256];
   __shared__ int32_t s_drop[256];
   __shared__ int32_t s_mt[256];
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void scan_kernel(
     }
   }
   const int kept = (e < E) ? min(run, C) : 0;
-  const int mt = (mt_prefix != nullptr) ? (kept + bm - 1) / bm : 0;
+  const int mt = (mt_prefix != nullptr) ? m_tiles(kept, tile_code) : 0;
   s_kept[e] = kept;
   s_drop[e] = (e < E) ? run - kept : 0;
   s_mt[e] = mt;
@@ -209,9 +209,9 @@ __global__ __launch_bounds__(256) void permute_small_kernel(
     int k, int C, int row_chunks, int tok_per_block, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ dropped,
     int32_t* __restrict__ dest_row, int32_t* __restrict__ row_token,
-    i32x4* __restrict__ X_perm, int32_t* __restrict__ mt_prefix, int bm) {
+    i32x4* __restrict__ X_perm, int32_t* __restrict__ mt_prefix, int tile_code) {
   __shared__ int32_t s_run[256];        // copies of each expert ranked so far
-  __shared__ int32_t s_mt[256];         // tiles of bm rows per expert
+  __shared__ int32_t s_mt[256];         // M-tiles per expert (m_tiles)
   __shared__ int32_t s_wcnt[4][256];    // per-wave copies of each expert in a round
   __shared__ int32_t s_off[256];        // kept-row offsets
   __shared__ int32_t s_drop[256];
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256) void permute_small_kernel(
   // capacity, exclusive scan of the kept counts, dropped total
   const int cnt = (tid < E) ? s_run[tid] : 0;
   const int kept = min(cnt, C);
-  const int mt = (mt_prefix != nullptr) ? (kept + bm - 1) / bm : 0;
+  const int mt = (mt_prefix != nullptr) ? m_tiles(kept, tile_code) : 0;
   s_off[tid] = kept;
   s_drop[tid] = cnt - kept;
   s_mt[tid] = mt;
@@ -314,14 +314,14 @@ hipError_t launch_k(const void* X, bool x_bf16, const int32_t* topk_idx, int T,
                     int d, int E, int k, int C, int32_t* counts,
                     int32_t* offsets, int32_t* dropped, int32_t* dest_row,
                     int32_t* row_token, void* X_perm, int32_t* local_rank,
-                    int32_t* block_counts, int32_t* mt_prefix, int bm, hipStream_t stream) {
+                    int32_t* block_counts, int32_t* mt_prefix, int tile_code, hipStream_t stream) {
   const int nblk = (T + kPermThreads - 1) / kPermThreads;
   count_rank_kernel<KMAX><<<nblk, kPermThreads, 0, stream>>>(
       topk_idx, T, E, k, local_rank, block_counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   scan_kernel<<<1, 256, 0, stream>>>(block_counts, nblk, E, C, counts, offsets, dropped,
-                                     mt_prefix, bm);
+                                     mt_prefix, tile_code);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int row_chunks = d * (x_bf16 ? 2 : 4) / 16;
@@ -345,14 +345,14 @@ hipError_t launch_permute(const void* X, bool x_bf16, const int32_t* topk_idx,
                           int T, int d, int E, int k, int C, int32_t* counts,
                           int32_t* offsets, int32_t* dropped, int32_t* dest_row,
                           int32_t* row_token, void* X_perm, void* scratch,
-                          int32_t* mt_prefix, int bm, hipStream_t stream) {
+                          int32_t* mt_prefix, int tile_code, hipStream_t stream) {
   int32_t* local_rank = static_cast<int32_t*>(scratch);
   int32_t* block_counts = reinterpret_cast<int32_t*>(
       static_cast<char*>(scratch) + align256((size_t)T * k * 4));
   if (T == 0) {
     // still publish empty counts/offsets so callers see a consistent state
     scan_kernel<<<1, 256, 0, stream>>>(block_counts, 0, E, C, counts, offsets, dropped,
-                                       mt_prefix, bm);
+                                       mt_prefix, tile_code);
     return hipGetLastError();
   }
   if ((int64_t)T * k <= kSmallCopies) {
@@ -360,14 +360,14 @@ hipError_t launch_permute(const void* X, bool x_bf16, const int32_t* topk_idx,
     const int tpb = (T + 255) / 256;  // tokens per workgroup: at most 256 workgroups
     permute_small_kernel<<<(unsigned)((T + tpb - 1) / tpb), 256, 0, stream>>>(
         static_cast<const i32x4*>(X), topk_idx, T, E, k, C, row_chunks, tpb, counts,
-        offsets, dropped, dest_row, row_token, static_cast<i32x4*>(X_perm), mt_prefix, bm);
+        offsets, dropped, dest_row, row_token, static_cast<i32x4*>(X_perm), mt_prefix, tile_code);
     return hipGetLastError();
   }
 #define MOE_PERM_CASE(KM)                                                                 \
   if (k <= KM)                                                                            \
     return launch_k<KM>(X, x_bf16, topk_idx, T, d, E, k, C, counts, offsets, dropped,     \
                         dest_row, row_token, X_perm, local_rank, block_counts,       \
-                        mt_prefix, bm, stream);
+                        mt_prefix, tile_code, stream);
   MOE_PERM_CASE(1)
   MOE_PERM_CASE(2)
   MOE_PERM_CASE(4)
