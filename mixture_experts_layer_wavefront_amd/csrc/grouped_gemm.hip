@@ -1030,7 +1030,8 @@ hipError_t launch_grouped_ffn_train(const void* X_perm, const int32_t* offsets,
   if (R == 0) return hipSuccess;
   hipError_t err;
   if (!prefix_ready) {
-    ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, bm, mt_prefix);
+    ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, ffn_tile_code(true, rows_per_expert),
+                                               mt_prefix);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   GemmArgs a{};
@@ -1058,9 +1059,10 @@ hipError_t launch_grouped_ffn_train(const void* X_perm, const int32_t* offsets,
     if (err != hipSuccess) return err;
     return launch_down<2, MOE_NW, 4, MOE_DTN / MOE_NW, MOE_BK, MOE_NS, kNonTemporal, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr);
   }
-  err = launch_gemm_args<2, MOE_NW, 4, 4 / MOE_NW, true, MOE_BK, MOE_NS, 0, false, 1>(a, R, stream);
+  // tall tiles, with the schedule of ffn_tile_code as in launch_grouped_ffn
+  err = launch_gemm_args<2, MOE_NW, 5, 4 / MOE_NW, true, MOE_BK, 2, 0, false, 1>(a, R, stream);
   if (err != hipSuccess) return err;
-  return launch_down<2, MOE_NW, 4, MOE_DTN / MOE_NW, MOE_BK, MOE_NS, 0, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr);
+  return launch_down<2, MOE_NW, 5, MOE_DTN / MOE_NW, MOE_BK, 2, 0, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr);
 }
 
 hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const void* W_gate,
