@@ -30,8 +30,14 @@
 //    banks (rocprof: zero LDS bank conflicts).
 //  * Ragged tiles (an expert's last rows) run a second instance of the K loop
 //    in which each wave only issues the MFMAs of its row sub-tiles that hold
-//    rows; the hardware pairs waves w and w + 4 on one SIMD, and those hold
-//    different row halves, so every SIMD keeps working.
+//    rows; the hardware pairs waves w and w + 4 on one SIMD (read from the
+//    HW_ID register), and those hold different row halves, so every SIMD
+//    keeps working.
+//  * Tall tiles: with more than 256 rows per expert on average, an expert's
+//    remainder of up to 64 rows joins its last 256-row tile (up to 320 rows,
+//    five row sub-tiles per wave) instead of taking a tile of its own, which
+//    would stream the whole weight tile again for a few rows.  The tile
+//    schedule (m_tiles) and the kernels agree through a tile code.
 //  * Schedule: a one-workgroup kernel turns expert_offsets into a prefix of
 //    per-expert M-tile counts.  The grid is a static upper bound; each
 //    workgroup finds its (expert, n-tile, m-tile) from the prefix and exits
