@@ -922,7 +922,7 @@ bool ffn_split_down(bool bf16, int E, int rows_per_expert, int d, int d_ff) {
 
 int ffn_tile_code(bool bf16, int rows_per_expert, bool fp8) {
   const int bm = ffn_tile_rows(bf16, rows_per_expert, fp8);
-  return (bm == 256 && !fp8 && rows_per_expert > MOE_BNT_ROWS) ? kTallTileCode : bm;
+  return (bm == 256 && rows_per_expert > MOE_BNT_ROWS) ? kTallTileCode : bm;
 }
 
 int ffn_tile_rows(bool bf16, int rows_per_expert, bool fp8) {
@@ -1003,11 +1003,11 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
     return launch_down<2, 4, 2, 2, 128, 2, 0, true>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, w_scales, defer);
   }
   if (fp8) {
-    // FP8 weights, many rows per expert: the 256-row tiles of the bf16 path
-    // (the weight tiles are shared by several M-tiles through L2)
-    err = launch_gemm<2, MOE_NW, 4, 4 / MOE_NW, true, MOE_BK, MOE_NS, 0, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales);
+    // FP8 weights, many rows per expert: the tall 256-row tiles of the bf16
+    // path (the weight tiles are shared by several M-tiles through L2)
+    err = launch_gemm<2, MOE_NW, 5, 4 / MOE_NW, true, MOE_BK, 2, 0, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales);
     if (err != hipSuccess) return err;
-    return launch_down<2, MOE_NW, 4, MOE_DTN / MOE_NW, MOE_BK, MOE_NS, 0, true>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, w_scales, defer);
+    return launch_down<2, MOE_NW, 5, MOE_DTN / MOE_NW, MOE_BK, 2, 0, true>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, w_scales, defer);
   }
   if (rows_per_expert <= MOE_BNT_ROWS) {
     // about one M-tile per expert: every weight tile is read once

@@ -42,8 +42,8 @@ hipError_t launch_permute(const void* X, bool x_bf16, const int32_t* topk_idx,
 // half's partial sums need R d fp32 more scratch.
 int ffn_tile_rows(bool bf16, int rows_per_expert, bool fp8 = false);
 // The M-tile code of moe_forward's grouped FFN (m_tiles): ffn_tile_rows, or
-// 256-row tiles that take remainders of up to 64 rows (bf16, more than 256
-// rows per expert).
+// 256-row tiles that take remainders of up to 64 rows (256-row tiles with
+// more than 256 rows per expert, bf16 or FP8 weights).
 int ffn_tile_code(bool bf16, int rows_per_expert, bool fp8 = false);
 bool ffn_split_down(bool bf16, int E, int rows_per_expert, int d, int d_ff);
 size_t ffn_scratch_bytes(int64_t R, int E, int d, int d_ff, bool bf16, int rows_per_expert);

@@ -26,6 +26,7 @@ from parity_util import BF16_TOL, bf16_err, host_f64
 pytestmark = pytest.mark.gpu
 
 COUNTS = [320, 257, 321, 576, 256, 64, 0, 300]   # sum 2094
+COUNTS8 = [576, 577, 640, 641, 512, 64, 0, 1088]  # sum 4098
 
 
 @pytest.mark.parametrize("d, dff", [(264, 200), (520, 2080)])
@@ -74,3 +75,39 @@ def test_tall_tiles(d, dff):
                                Wd["W_up"][e:e + 1], Wd["W_down"][e:e + 1])
         torch.cuda.synchronize()
         assert torch.equal(Y1[:n], Y[lo:lo + n]), f"expert {e} rows {s}..{s + n}"
+
+
+def test_tall_tiles_fp8():
+    """FP8 E4M3 expert weights on the same row counts: bit-identical to the
+    bf16 path given the weights decoded to bf16 (power-of-two scales, same
+    sums in the same order), and within the bf16 bar of the oracle.  FP8
+    weights need d_model and d_ff multiples of 16."""
+    d, dff = 272, 208
+    # more than 512 rows per expert on average (FP8 weights take 256-row
+    # tiles only then): 512 + 64 and 1024 + 64 merge, 512 + 65 does not
+    counts = COUNTS8
+    E, k, T = len(counts), 2, 2200
+    R = T * k
+    print(f"[tall] fp8 d={d} d_ff={dff} counts {counts}", flush=True)
+    wl = W.Workload("tall8", T, d, E, k, dff, W.BF16, W.TOPK_THEN_SOFTMAX, 0.0, 0.0, 73)
+    h8 = W.make_host_fp8(wl)
+    rng = np.random.default_rng(74)
+    N = sum(counts)
+    Xp_d = torch.from_numpy(rng.standard_normal((R, d)).astype(np.float32)).to("cuda").to(
+        torch.bfloat16)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    off_d = torch.from_numpy(off).to("cuda")
+    Q = [torch.from_numpy(h8[q]).to("cuda") for q in ("Q_gate", "Q_up", "Q_down")]
+    sc = torch.from_numpy(h8["scales"]).to("cuda")
+    dec = [(Q[j].view(torch.float8_e4m3fn).to(torch.float32) * sc[:, j].view(E, 1, 1)).to(
+        torch.bfloat16) for j in range(3)]
+    p8 = B.problem(T, d, E, k, dff, 0.0, "bf16", W.TOPK_THEN_SOFTMAX, "f32", w_dtype="fp8")
+    pb = B.problem(T, d, E, k, dff, 0.0, "bf16", W.TOPK_THEN_SOFTMAX, "f32")
+    Y8 = B.moe_grouped_ffn_scaled(p8, Xp_d, off_d, *Q, sc)
+    Yb = B.moe_grouped_ffn(pb, Xp_d, off_d, *dec)
+    torch.cuda.synchronize()
+    assert torch.equal(Y8[:N], Yb[:N]), "FP8 and decoded-bf16 grouped FFN differ"
+    Yo = O.grouped_ffn(host_f64(Xp_d)[:N], off, *[host_f64(t) for t in dec])
+    err = bf16_err(Y8[:N].cpu().numpy(), Yo)
+    print(f"[tall] fp8: err {err:.3e}", flush=True)
+    assert err <= BF16_TOL
