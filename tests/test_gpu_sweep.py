@@ -18,8 +18,9 @@ once at import: T log-uniform in [1, 700], d_model and d_ff multiples of 8
 log-uniform in [8, 520] and [8, 640], E uniform in [1, 64], k uniform in
 [1, min(E, 8)], bf16 with probability 0.8, softmax-then-top-k with
 probability 0.5, a capacity factor in [0.3, 2] with probability 0.35, a
-Zipf(1.2) router bias with probability 0.35.  Every shape prints itself
-before it runs."""
+Zipf(1.2) router bias with probability 0.35.  Eight more shapes (seed
+20261204) have 2-8 experts averaging 300-1000 rows each, for the 256-row and
+merged tall tiles.  Every shape prints itself before it runs."""
 
 import numpy as np
 import pytest
@@ -62,7 +63,25 @@ def _shapes():
     return out
 
 
-SHAPES = _shapes()
+def _tall_shapes():
+    """Few experts with many rows each (mean 300-1000), so the 256-row tiles
+    and the merged tall last tiles run on random counts."""
+    rng = np.random.Generator(np.random.PCG64(20261204))
+    out = []
+    for i in range(8):
+        E = int(rng.integers(2, 9))
+        k = int(rng.integers(1, min(E, 2) + 1))
+        T = int(rng.integers(300, 1001)) * E // k
+        d = _log_uniform_int(rng, 64, 520, 8)
+        dff = _log_uniform_int(rng, 64, 640, 8)
+        gating = W.SOFTMAX_THEN_TOPK if rng.random() < 0.5 else W.TOPK_THEN_SOFTMAX
+        zipf = 1.2 if rng.random() < 0.35 else 0.0
+        out.append(W.Workload(f"sweep_tall{i}", T, d, E, k, dff, W.BF16, gating, 0.0, zipf,
+                              2000 + i))
+    return out
+
+
+SHAPES = _shapes() + _tall_shapes()
 
 
 @pytest.mark.parametrize("wl", SHAPES, ids=[w.name for w in SHAPES])
