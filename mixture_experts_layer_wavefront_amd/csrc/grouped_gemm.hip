@@ -914,10 +914,13 @@ hipError_t launch_down(const void* H, const void* W_down, int d, int d_ff, int E
 bool ffn_split_down(bool bf16, int E, int rows_per_expert, int d, int d_ff) {
   if (!MOE_SPLIT_DOWN || !bf16 || rows_per_expert <= 64) return false;
   if (d_ff < 2048 || d_ff % 32 != 0) return false;
-  // 256 x 256 tiles of the unsplit GEMM: split when they fill the 256 CUs
-  // fewer than four times
+  // 256 x 256 tiles of the unsplit GEMM (from the mean rows per expert):
+  // split when they fill the 256 CUs fewer than four times and leave the
+  // last round at most half full (halves of twice as many tiles then finish
+  // sooner; a full last round gains nothing and the halves cost an add)
   const int64_t tiles = (int64_t)E * ((rows_per_expert + 255) / 256) * ((d + 255) / 256);
-  return tiles < 4 * 256;
+  const int64_t rem = tiles % 256;
+  return tiles < 4 * 256 && rem != 0 && rem <= 128;
 }
 
 int ffn_tile_code(bool bf16, int rows_per_expert, bool fp8) {
