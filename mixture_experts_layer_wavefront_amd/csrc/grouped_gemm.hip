@@ -616,7 +616,8 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
         // MFMAs; left to itself the scheduler waits on each fragment just
         // before its first MFMA (measured: Mixtral layer 2.91 -> 2.78 ms)
         if constexpr (TALL && NA > 0) {
-          __builtin_amdgcn_sched_group_barrier(0x100, NA + NB, 0);  // DS reads
+          // DS reads (a transpose-read fragment takes two)
+          __builtin_amdgcn_sched_group_barrier(0x100, NA * (AT ? 2 : 1) + NB * (BT ? 2 : 1), 0);
           __builtin_amdgcn_sched_group_barrier(0x008, NA * NB, 0);  // MFMAs
         }
       }
@@ -1083,6 +1084,16 @@ hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const v
   ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, bm, mt_prefix);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  // dX runs on tall tiles where the forward does (a schedule of its own in
+  // the second E + 1 entries); dH keeps 256-row tiles (its epilogue stages
+  // the saved G and U of all five sub-tiles in LDS, which does not fit)
+  const int code = ffn_tile_code(true, rows_per_expert, false);
+  const bool tall = code != bm;
+  int32_t* mt_tall = tall ? mt_prefix + (E + 1) : mt_prefix;
+  if (tall) {
+    ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, code, mt_tall);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   // dH = dY_perm Wd (Wd [E, d, d_ff] read along its rows) -> SwiGLU backward
   GemmArgs a{};
   a.A = static_cast<const uint16_t*>(dY_perm);
@@ -1104,7 +1115,7 @@ hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const v
   x.K = d_ff;
   x.E = E;
   x.offsets = offsets;
-  x.mt_prefix = mt_prefix;
+  x.mt_prefix = mt_tall;
   x.C = dX_perm;
   x.C1 = dX_perm + R * d;  // the second K half's partial sums
   x.lda = 2 * d_ff;
@@ -1120,6 +1131,8 @@ hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const v
   }
   err = launch_gemm_args<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, 0, false, 2>(a, R, stream);
   if (err != hipSuccess) return err;
+  if (tall)
+    return launch_gemm_args<2, MOE_NW, 5, MOE_DTN / MOE_NW, false, MOE_BK, 2, 0, false, 4>(x, R, stream);
   return launch_gemm_args<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, 0, false, 4>(x, R, stream);
 }
 
