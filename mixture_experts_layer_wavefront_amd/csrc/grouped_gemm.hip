@@ -59,12 +59,6 @@
 #ifndef MOE_DTN
 #define MOE_DTN 8   // down GEMM: 32-column sub-tiles per 256-row tile
 #endif
-#ifndef MOE_WL
-#define MOE_WL 1
-#endif
-#ifndef MOE_SKIP
-#define MOE_SKIP 1
-#endif
 #ifndef MOE_LW
 #define MOE_LW 4
 #endif
@@ -493,11 +487,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   // wm = wave / NW: the hardware puts waves w and w + 4 on one SIMD, so each
   // SIMD holds waves of different row halves and skipping the empty row
   // sub-tiles of a ragged tile leaves every SIMD with work.
-#if MOE_WL
   const int wm = wave / NW, wn = wave % NW;
-#else
-  const int wm = wave % MW, wn = wave / MW;
-#endif
   // Rows of the wave's sub-tiles: wave row wm covers rows wm * TM * 32 +
   // 32 mi; a tall kernel's tiles of at most 256 rows use 4 sub-tiles per
   // wave row (wm * 128 + 32 mi) so the two wave rows stay balanced, and the
@@ -623,7 +613,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
       }
     }
   };
-  if (!MOE_SKIP || tm_active == TM) kloop(std::integral_constant<int, TM>{});
+  if (tm_active == TM) kloop(std::integral_constant<int, TM>{});
   else if (TALL && tm_active == 4) kloop(std::integral_constant<int, 4>{});
   else kloop(std::integral_constant<int, -1>{});
 
