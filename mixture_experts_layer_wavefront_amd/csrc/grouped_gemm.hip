@@ -667,10 +667,14 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
     // 4x16 block and receives the 4 rows of column (its lane).  Each wave
     // uses its own LDS region (TM sub-tiles x 2 matrices x 2 KB), one column
     // sub-tile at a time.
-    static_assert(NWAVES * TM * 4096 <= NS * STAGE, "epilogue staging fits the stages");
+    // At most four sub-tiles are staged at a time (a tall kernel's fifth
+    // is staged after the first four are done): 8 waves x 4 x 4 KB fit the
+    // two stages.  Sub-tiles without rows are neither staged nor computed.
+    constexpr int CH = TM > 4 ? 4 : TM;
+    static_assert(NWAVES * CH * 4096 <= NS * STAGE, "epilogue staging fits the stages");
     uint16_t* dGU = static_cast<uint16_t*>(Cout);
     __syncthreads();  // every wave is done with the last stage
-    char* wreg = smem + wave * (TM * 4096);
+    char* wreg = smem + wave * (CH * 4096);
     const uint32_t gbytes = (uint32_t)rows * (uint32_t)N * 2u;
     const __amdgpu_buffer_rsrc_t rG = make_rsrc(g.G + (int64_t)m_start * N, gbytes);
     const __amdgpu_buffer_rsrc_t rU = make_rsrc(g.U + (int64_t)m_start * N, gbytes);
@@ -683,43 +687,52 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
 #pragma unroll
     for (int nj = 0; nj < TN; ++nj) {
       const int cb = wn * TN * 32 + nj * 32;  // tile-local first column of the sub-tile
-      if (nj > 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t row = sub_row0(mi) + h * 16 + (lane >> 2);
-          const uint32_t vo = row * (uint32_t)N * 2u + (uint32_t)(n0 + cb + 8 * (lane & 3)) * 2u;
-          char* dg = wreg + mi * 4096 + h * 1024;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rG, MOE_LDS_PTR(dg), 16, vo, 0, 0, 0);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rU, MOE_LDS_PTR(dg + 2048), 16, vo, 0, 0, 0);
-        }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       const int col = cb + col_l;
 #pragma unroll
-      for (int mi = 0; mi < TM; ++mi)
+      for (int c0 = 0; c0 < TM; c0 += CH) {
+        // the previous chunk's transpose reads are done before its region
+        // is written again
+        if (nj > 0 || c0 > 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const char* pg = wreg + mi * 4096 + q * 512 + tr_off;
-          const v4s gq = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(pg));
-          const v4s uq = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(pg + 2048));
+        for (int mi = c0; mi < (c0 + CH < TM ? c0 + CH : TM); ++mi)
+          if (mi < tm_active) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 4 * q + j;
-            const int row = sub_row0(mi) + rlane + 8 * q + j;
-            if (row < rows && col < ncols) {
-              const float gv = bf16_bits_to_f32((uint16_t)gq[j]);
-              const float u = bf16_bits_to_f32((uint16_t)uq[j]);
-              const float sg = 1.f / (1.f + __expf(-gv));
-              const float dh = acc[mi][nj][r];
-              const float dgv = dh * u * (sg * (1.f + gv * (1.f - sg)));
-              const float du = dh * (gv * sg);
-              const int64_t o2 = (int64_t)(m_start + row) * (2 * N) + n0 + col;
-              dGU[o2] = f32_to_bf16_bits(dgv);
-              dGU[o2 + N] = f32_to_bf16_bits(du);
+            for (int h = 0; h < 2; ++h) {
+              const uint32_t row = sub_row0(mi) + h * 16 + (lane >> 2);
+              const uint32_t vo = row * (uint32_t)N * 2u + (uint32_t)(n0 + cb + 8 * (lane & 3)) * 2u;
+              char* dg = wreg + (mi - c0) * 4096 + h * 1024;
+              __builtin_amdgcn_raw_ptr_buffer_load_lds(rG, MOE_LDS_PTR(dg), 16, vo, 0, 0, 0);
+              __builtin_amdgcn_raw_ptr_buffer_load_lds(rU, MOE_LDS_PTR(dg + 2048), 16, vo, 0, 0, 0);
             }
           }
-        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int mi = c0; mi < (c0 + CH < TM ? c0 + CH : TM); ++mi)
+          if (mi < tm_active) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const char* pg = wreg + (mi - c0) * 4096 + q * 512 + tr_off;
+              const v4s gq = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(pg));
+              const v4s uq = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(pg + 2048));
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int r = 4 * q + j;
+                const int row = sub_row0(mi) + rlane + 8 * q + j;
+                if (row < rows && col < ncols) {
+                  const float gv = bf16_bits_to_f32((uint16_t)gq[j]);
+                  const float u = bf16_bits_to_f32((uint16_t)uq[j]);
+                  const float sg = 1.f / (1.f + __expf(-gv));
+                  const float dh = acc[mi][nj][r];
+                  const float dgv = dh * u * (sg * (1.f + gv * (1.f - sg)));
+                  const float du = dh * (gv * sg);
+                  const int64_t o2 = (int64_t)(m_start + row) * (2 * N) + n0 + col;
+                  dGU[o2] = f32_to_bf16_bits(dgv);
+                  dGU[o2 + N] = f32_to_bf16_bits(du);
+                }
+              }
+            }
+          }
+      }
     }
   } else if constexpr (MODE == 3) {
     float* C0 = static_cast<float*>(Cout);
@@ -1071,19 +1084,12 @@ hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const v
                             int32_t* mt_prefix, void* dGU, float* dX_perm, hipStream_t stream) {
   const int bm = ffn_tile_rows(true, rows_per_expert, false);
   if (R == 0) return hipSuccess;
-  ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, bm, mt_prefix);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  // dX runs on tall tiles where the forward does (a schedule of its own in
-  // the second E + 1 entries); dH keeps 256-row tiles (its epilogue stages
-  // the saved G and U of all five sub-tiles in LDS, which does not fit)
+  // dH and dX run on tall tiles where the forward does
   const int code = ffn_tile_code(true, rows_per_expert, false);
   const bool tall = code != bm;
-  int32_t* mt_tall = tall ? mt_prefix + (E + 1) : mt_prefix;
-  if (tall) {
-    ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, code, mt_tall);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
+  ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, code, mt_prefix);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
   // dH = dY_perm Wd (Wd [E, d, d_ff] read along its rows) -> SwiGLU backward
   GemmArgs a{};
   a.A = static_cast<const uint16_t*>(dY_perm);
@@ -1105,7 +1111,7 @@ hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const v
   x.K = d_ff;
   x.E = E;
   x.offsets = offsets;
-  x.mt_prefix = mt_tall;
+  x.mt_prefix = mt_prefix;
   x.C = dX_perm;
   x.C1 = dX_perm + R * d;  // the second K half's partial sums
   x.lda = 2 * d_ff;
@@ -1119,10 +1125,13 @@ hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const v
     if (err != hipSuccess) return err;
     return launch_gemm_args<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, kNonTemporal, false, 4>(x, R, stream);
   }
+  if (tall) {
+    err = launch_gemm_args<2, MOE_NW, 5, MOE_DTN / MOE_NW, false, MOE_BK, 2, 0, false, 2>(a, R, stream);
+    if (err != hipSuccess) return err;
+    return launch_gemm_args<2, MOE_NW, 5, MOE_DTN / MOE_NW, false, MOE_BK, 2, 0, false, 4>(x, R, stream);
+  }
   err = launch_gemm_args<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, 0, false, 2>(a, R, stream);
   if (err != hipSuccess) return err;
-  if (tall)
-    return launch_gemm_args<2, MOE_NW, 5, MOE_DTN / MOE_NW, false, MOE_BK, 2, 0, false, 4>(x, R, stream);
   return launch_gemm_args<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, 0, false, 4>(x, R, stream);
 }
 

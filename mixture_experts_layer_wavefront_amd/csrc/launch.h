@@ -73,7 +73,6 @@ hipError_t launch_grouped_ffn_train(const void* X_perm, const int32_t* offsets,
 // from dH = dY_perm Wd and the saved G, U; dX_perm [2, R, d] fp32 holds the
 // two partial sums dG Wg and dU Wu (their sum is the rows' gradient).
 // The weights are read as stored ([E, out, in]), along their rows.
-// mt_prefix: 2 (E + 1) ints of scratch (the tile schedules of dH and dX).
 hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const void* W_gate,
                             const void* W_up, const void* W_down, const void* G, const void* U,
                             int64_t R, int d, int E, int d_ff, int rows_per_expert,

@@ -219,7 +219,7 @@ BackwardLayout backward_layout(const moe_problem_t* p) {
   B.dgu = o; o += a256(R * 2 * dff * 2);
   B.dxp = o; o += a256(2 * R * d * 4);
   B.dl = o; o += a256(Tk * 4);
-  B.mtp = o; o += a256(2 * (E + 1) * 4);
+  B.mtp = o; o += a256((E + 1) * 4);
   B.rw = o; o += a256(moe::router_wgrad_scratch_bytes(p->T, p->d_model, p->E));
   B.total = o;
   return B;
