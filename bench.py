@@ -55,6 +55,10 @@ def _parse():
                     help="also run the grouped FFN back to back for a few "
                          "seconds while amd-smi samples socket power and the "
                          "graphics clock; reports the MFMA peak at that clock")
+    ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the step captured once in a HIP graph and "
+                         "replayed (the library allocates and synchronises "
+                         "nothing, so a whole layer call can be captured)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -110,6 +114,27 @@ def _time_loop(fn, steps, stream):
     e.record(stream)
     e.synchronize()
     return s.elapsed_time(e) / steps  # ms per call
+
+
+def _graph_time(step, n, stream):
+    """The step captured once in a HIP graph (torch.cuda.CUDAGraph) and
+    replayed n times; ms per replay, event-timed on the given stream."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = _time_loop(g.replay, n, stream)
+    del g
+    return ms
 
 
 def _smi_sample():
@@ -487,6 +512,12 @@ def main():
             "backward_gemm_flops": bwd_flops,
             "backward_tflops": bwd_flops / (t_bwd * 1e-3) / 1e12,
             "backward_frac_of_bf16_peak": bwd_flops / (t_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    if args.graph and shared is None:
+        try:
+            line["graph"] = {"ms_per_step_replayed": _graph_time(step, n, stream),
+                             "ms_per_step_eager": ms}
+        except Exception as ex:  # capture unsupported: report, do not fail the line
+            line["graph"] = {"error": repr(ex)[:200]}
     if args.sample_power:
         line["power"] = _sample_power(lambda: ffn(Y, ffn_ws), ffn_flops, stream)
         if args.library_loop and not args.fp8 and wl.dtype == W.BF16:
