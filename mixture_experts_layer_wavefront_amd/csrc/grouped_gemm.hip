@@ -464,10 +464,12 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
     for (int i = 0; i < IPW; ++i) {
       const int qi = wave + LW * i;
       const bool is_a = qi < NIA;
-      // a tall kernel's 256-row tile: the rows of the 64-row extension are
-      // not loaded (their sub-tiles issue no MFMA; with two stages every
-      // wait is for all of a wave's loads, so the count may vary)
-      if (TALL && is_a && qi * RPIA >= 256 && rows <= 256) continue;
+      // A rows past the tile's rows are not loaded when a whole load (8
+      // rows) lies past them: their sub-tiles issue no MFMA, or only for
+      // rows that are never stored (a partly filled sub-tile reads stale LDS
+      // rows there; MFMA rows are independent).  With two stages every wait
+      // is for all of a wave's loads, so the count may vary.
+      if (NS == 2 && !AT && is_a && qi * RPIA >= rows) continue;
       const uint2 lo = load_off(i);
       const int kc = (int)lo.y;
       uint32_t vo = lo.x + (uint32_t)kt * (is_a ? stepA : stepB);
