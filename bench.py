@@ -281,8 +281,16 @@ def _cpu_baseline(wl, dev, ntok, min_s=10.0, max_s=30.0, shared=None, fp8_scales
         if total + dt > max_s:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    model = None
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": ntok * runs / total, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "host_cpus": os.cpu_count(), "cpu_model": model,
             "sample": f"first {ntok} of the {wl.T} tokens, all {wl.E} experts "
                       f"(full weights{', plus the shared expert' if shared is not None else ''}), "
                       f"fp64 NumPy per-expert loop, {runs} run(s), {total:.1f} s wall"}
@@ -349,9 +357,18 @@ def main():
 
     for _ in range(args.warmup):
         step()
+    # K steps between two events, with an event after each step as well
+    # (their gaps give the per-step median and minimum)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms = _time_loop(step, args.steps, stream)
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    evs[-1].synchronize()
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     st = stats.cpu().numpy()
@@ -423,6 +440,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": per_step[len(per_step) // 2],
+        "ms_per_step_min": per_step[0],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
