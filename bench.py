@@ -458,6 +458,12 @@ def main():
         "roofline": roofline,
         "stages_ms": {"route": t_route, "permute": t_perm, "grouped_ffn": t_ffn,
                       "combine": t_comb},
+        # router logits: 2 T d E algorithmic flops (fp32 logits; computed as
+        # three exact bf16 products on the matrix cores for bf16 layers),
+        # against the fp32 vector peak the survey scores it by
+        "stages_tflops": {"route_logits": 2.0 * T * d * E / (t_route * 1e-3) / 1e12,
+                          "route_frac_of_fp32_peak":
+                              2.0 * T * d * E / (t_route * 1e-3) / 1e12 / 157.3},
         "stages_gbs": {"route": bytes_route / (t_route * 1e6),
                        "permute": bytes_perm / (t_perm * 1e6),
                        "combine": bytes_comb / (t_comb * 1e6),
