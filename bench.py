@@ -116,6 +116,14 @@ def _time_loop(fn, steps, stream):
     return s.elapsed_time(e) / steps  # ms per call
 
 
+def _route_tflops(T, d, E, t_route_ms, x_bf16):
+    tf = 2.0 * T * d * E / (t_route_ms * 1e-3) / 1e12
+    if x_bf16:
+        return {"route_logits": tf, "route_units": "bf16 mfma, three planes",
+                "route_frac": 3.0 * tf / 2500.0}
+    return {"route_logits": tf, "route_units": "fp32 vector fma", "route_frac": tf / 157.3}
+
+
 def _graph_time(step, n, stream):
     """The step captured once in a HIP graph (torch.cuda.CUDAGraph) and
     replayed n times; ms per replay, event-timed on the given stream."""
@@ -458,12 +466,12 @@ def main():
         "roofline": roofline,
         "stages_ms": {"route": t_route, "permute": t_perm, "grouped_ffn": t_ffn,
                       "combine": t_comb},
-        # router logits: 2 T d E algorithmic flops (fp32 logits; computed as
-        # three exact bf16 products on the matrix cores for bf16 layers),
-        # against the fp32 vector peak the survey scores it by
-        "stages_tflops": {"route_logits": 2.0 * T * d * E / (t_route * 1e-3) / 1e12,
-                          "route_frac_of_fp32_peak":
-                              2.0 * T * d * E / (t_route * 1e-3) / 1e12 / 157.3},
+        # router logits: 2 T d E algorithmic flops of fp32 logits per step
+        # (route stage: logits, top-k and gate weights).  fp32 layers compute
+        # them with fp32 vector FMAs (peak 157.3 TFLOP/s); bf16 layers as three
+        # exact bf16 products on the matrix cores, 3x the flops against the
+        # dense bf16 peak (2500 TFLOP/s)
+        "stages_tflops": _route_tflops(T, d, E, t_route, wl.dtype == W.BF16),
         "stages_gbs": {"route": bytes_route / (t_route * 1e6),
                        "permute": bytes_perm / (t_perm * 1e6),
                        "combine": bytes_comb / (t_comb * 1e6),
