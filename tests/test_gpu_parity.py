@@ -36,6 +36,9 @@ SMALL = {
     "decode_s": WL("decode_s", 24, 512, 64, 8, 320, W.BF16, TK, 0.0, 0.0, 16),
     # the widest routing the ABI takes
     "wide_k": WL("wide_k", 300, 64, 256, 32, 64, W.BF16, ST, 0.0, 0.0, 17),
+    # 65..128 experts (expert-split router logits, EP = 128) with a token
+    # tail (333 = 2 x 128 + 77) and d_model not a multiple of 32 (K tail of X)
+    "wide_e": WL("wide_e", 333, 264, 100, 6, 128, W.BF16, ST, 0.0, 0.8, 19),
     # d_ff >= 2048 with few tiles: the down projection runs as two K halves
     # (d_ff / 2 = 1040 leaves a K tail in each half; N tail 520 = 2 x 256 + 8)
     "split_down": WL("split_down", 600, 520, 4, 2, 2080, W.BF16, TK, 0.0, 0.8, 18),
