@@ -263,6 +263,10 @@ __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(
 
 constexpr int kRtTok = 128;  // tokens per logits workgroup (4 waves x 32)
 constexpr int kRtK = 32;     // K per stage: one 16x16x32 MFMA k-step
+#ifndef MOE_RZS
+#define MOE_RZS 2
+#endif
+constexpr int kRtZ = MOE_RZS;  // expert groups of a wide router (EP >= 128)
 
 __device__ __forceinline__ uint32_t rt_swz(uint32_t r) { return ((r >> 1) ^ (r >> 3)) & 3u; }
 
@@ -295,14 +299,16 @@ __global__ __launch_bounds__(256) void router_split_kernel(
   *reinterpret_cast<i32x4*>(Wsplit + 2 * plane + o) = i32x4{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3]};
 }
 
-// Partial logits of 128 tokens x EP experts over K-steps [k-slice of s].
-// Wave w owns tokens 32w + [0, 32) (two 16-row tiles) and all NTE expert
-// tiles; the three weight planes of each K-step are staged in LDS (64-byte
-// rows, chunk-swizzled), X fragments come straight from global memory.
+// Partial logits of 128 tokens x EP experts over K-steps [k-slice of s];
+// the experts are [e0, e0 + EP) with e0 = blockIdx.z EP, of the EPtot rows
+// of each weight plane (and of each partial row).  Wave w owns tokens
+// 32w + [0, 32) (two 16-row tiles) and all NTE expert tiles; the three
+// weight planes of each K-step are staged in LDS (64-byte rows,
+// chunk-swizzled), X fragments come straight from global memory.
 template <int NTE>
 __global__ __launch_bounds__(256) void router_logits_kernel(
     const uint16_t* __restrict__ X, int T, int d, const uint16_t* __restrict__ Wsplit,
-    int d32, int S, float* __restrict__ partial) {
+    int d32, int S, int EPtot, float* __restrict__ partial) {
   constexpr int EP = 16 * NTE;
   constexpr int ROWS = 3 * EP;           // staged rows per K-step
   constexpr int STAGE = ROWS * 64;       // bytes
@@ -313,17 +319,20 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int t0 = blockIdx.x * kRtTok;
   const int s = blockIdx.y;
+  const int e0 = blockIdx.z * EP;
   const int nk = d32 / kRtK;
   const int ks0 = (int)((int64_t)s * nk / S), ks1 = (int)((int64_t)(s + 1) * nk / S);
   const int nks = ks1 - ks0;
 
-  // weight-plane loads: instruction q covers rows 16q..16q+15
-  const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wsplit, (uint32_t)((int64_t)ROWS * d32 * 2));
+  // weight-plane loads: instruction q covers staged rows 16q..16q+15; staged
+  // row R is row e0 + R % EP of plane R / EP
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wsplit, (uint32_t)((int64_t)3 * EPtot * d32 * 2));
   auto issue = [&](int stage, int kstep) {
     for (int q = wave; q < NINSTR; q += 4) {
       const uint32_t R = q * 16 + (lane >> 2);
       const uint32_t c = (lane & 3) ^ rt_swz(R);
-      const uint32_t vo = R * (uint32_t)d32 * 2u + (uint32_t)kstep * (kRtK * 2) + c * 16;
+      const uint32_t G = (R / EP) * (uint32_t)EPtot + (uint32_t)e0 + R % EP;
+      const uint32_t vo = G * (uint32_t)d32 * 2u + (uint32_t)kstep * (kRtK * 2) + c * 16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, MOE_LDS_PTR(smem + stage * STAGE + q * 1024),
                                                16, vo, 0, 0, 0);
     }
@@ -386,7 +395,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
     for (int r = 0; r < 4; ++r) {
       const int t = xt0 + mt * 16 + 4 * (lane >> 4) + r;
       if (t < T) {
-        float* dst = partial + ((int64_t)s * T + t) * EP + (lane & 15);
+        float* dst = partial + ((int64_t)s * T + t) * EPtot + e0 + (lane & 15);
 #pragma unroll
         for (int nt = 0; nt < NTE; ++nt) dst[nt * 16] = acc[mt][nt][r];
       }
@@ -744,13 +753,17 @@ hipError_t launch_route(const void* X, bool x_bf16, const float* W_r,
   const int64_t nthr = (int64_t)P.EP * (P.d32 / 8);
   router_split_kernel<<<(unsigned)((nthr + 255) / 256), 256, 0, stream>>>(W_r, E, d, P.EP, P.d32, Wsplit);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  const dim3 g(P.tiles, P.S);
-  switch (P.NTE) {
-    case 1: router_logits_kernel<1><<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(X), T, d, Wsplit, P.d32, P.S, partial); break;
-    case 2: router_logits_kernel<2><<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(X), T, d, Wsplit, P.d32, P.S, partial); break;
-    case 4: router_logits_kernel<4><<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(X), T, d, Wsplit, P.d32, P.S, partial); break;
-    case 8: router_logits_kernel<8><<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(X), T, d, Wsplit, P.d32, P.S, partial); break;
-    default: router_logits_kernel<16><<<g, 256, 0, stream>>>(static_cast<const uint16_t*>(X), T, d, Wsplit, P.d32, P.S, partial); break;
+  // wide routers: the experts split over Z workgroups (smaller LDS stages,
+  // several workgroups per CU)
+  const int Z = P.NTE >= 8 ? kRtZ : 1;
+  const dim3 g(P.tiles, P.S, Z);
+  const uint16_t* Xb = static_cast<const uint16_t*>(X);
+  switch (P.NTE / Z) {
+    case 1: router_logits_kernel<1><<<g, 256, 0, stream>>>(Xb, T, d, Wsplit, P.d32, P.S, P.EP, partial); break;
+    case 2: router_logits_kernel<2><<<g, 256, 0, stream>>>(Xb, T, d, Wsplit, P.d32, P.S, P.EP, partial); break;
+    case 4: router_logits_kernel<4><<<g, 256, 0, stream>>>(Xb, T, d, Wsplit, P.d32, P.S, P.EP, partial); break;
+    case 8: router_logits_kernel<8><<<g, 256, 0, stream>>>(Xb, T, d, Wsplit, P.d32, P.S, P.EP, partial); break;
+    default: router_logits_kernel<16><<<g, 256, 0, stream>>>(Xb, T, d, Wsplit, P.d32, P.S, P.EP, partial); break;
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   return launch_select(partial, bias, T, E, P.EP, P.S, k, gating, topk_idx, topk_w,
