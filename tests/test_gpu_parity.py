@@ -39,6 +39,8 @@ SMALL = {
     # 65..128 experts (expert-split router logits, EP = 128) with a token
     # tail (333 = 2 x 128 + 77) and d_model not a multiple of 32 (K tail of X)
     "wide_e": WL("wide_e", 333, 264, 100, 6, 128, W.BF16, ST, 0.0, 0.8, 19),
+    # 256 experts (two expert groups of 128) with the same kinds of tails
+    "wide_e256": WL("wide_e256", 200, 136, 256, 8, 64, W.BF16, TK, 0.0, 1.2, 20),
     # d_ff >= 2048 with few tiles: the down projection runs as two K halves
     # (d_ff / 2 = 1040 leaves a K tail in each half; N tail 520 = 2 x 256 + 8)
     "split_down": WL("split_down", 600, 520, 4, 2, 2080, W.BF16, TK, 0.0, 0.8, 18),
