@@ -150,6 +150,10 @@ BOUNDARY = {
     "copies_2080": WL("copies_2080", 65, 200, 64, 32, 96, W.BF16, TK, 0.0, 0.0, 32),
     "k1_2048_tokens": WL("k1_2048_tokens", 2048, 64, 16, 1, 64, W.BF16, TK, 0.0, 0.0, 33),
     "few_tokens_E256": WL("few_tokens_E256", 40, 256, 256, 8, 64, W.BF16, ST, 0.0, 0.0, 34),
+    # the first size on the matrix-core router with 256 experts: one token
+    # tile of 65 rows (two waves without rows), two expert groups, K split 7
+    "mfma_router_65_E256": WL("mfma_router_65_E256", 65, 200, 256, 8, 64, W.BF16, ST, 0.0,
+                              0.0, 37),
     "few_tokens_E4": WL("few_tokens_E4", 10, 136, 4, 2, 64, W.BF16, TK, 0.0, 0.0, 35),
     "few_tokens_cap": WL("few_tokens_cap", 48, 128, 16, 4, 64, W.BF16, TK, 0.5, 1.2, 36),
 }
