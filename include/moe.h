@@ -317,8 +317,11 @@ moe_status_t moe_forward_scaled(const moe_problem_t* p, const void* X,
  * experts and 0 elsewhere, with dw[t,j] = <dout[t], Y_perm[dest[t,j]]>
  * (0 for a dropped copy).  The expert GEMMs take bf16 operands (G, U, H,
  * w dout, dG, dU) with fp32 accumulation; every sum has a fixed order.
- * workspace >= moe_backward_workspace_bytes(p) bytes (it holds transposed
- * copies of the expert weights).  T = 0: nothing is written. */
+ * workspace >= moe_backward_workspace_bytes(p) bytes: it holds w dout in
+ * bf16 [R, d_model], dG | dU in bf16 [R, 2 d_ff], the two fp32 partial sums
+ * of dX_perm [2, R, d_model], the logit gradients [T, top_k], the tile
+ * schedule and the router weight gradient's partial sums (no copy of any
+ * weight).  T = 0: nothing is written. */
 size_t moe_train_state_bytes(const moe_problem_t* p);
 moe_status_t moe_forward_train(const moe_problem_t* p, const void* X,
                                const float* W_r, const float* bias,

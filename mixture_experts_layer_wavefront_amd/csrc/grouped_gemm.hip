@@ -50,57 +50,28 @@
 #include <type_traits>
 #include "launch.h"
 
-#ifndef MOE_BK
-#define MOE_BK 64
-#endif
-#ifndef MOE_NS
-#define MOE_NS 2
-#endif
-#ifndef MOE_DTN
-#define MOE_DTN 8   // down GEMM: 32-column sub-tiles per 256-row tile
-#endif
-#ifndef MOE_LW
-#define MOE_LW 4
-#endif
-#ifndef MOE_NW
-#define MOE_NW 4   // waves across N in the 256-row tile (2 x MOE_NW waves)
-#endif
-#ifndef MOE_SNW
-#define MOE_SNW 4  // 32-row tiles: waves across N (one 32-column sub-tile each)
-#endif
-#ifndef MOE_SBK
-#define MOE_SBK 64 // 32-row tiles: K per stage
-#endif
-#ifndef MOE_SNS
-#define MOE_SNS 3  // 32-row tiles: stages
-#endif
-#ifndef MOE_SBAUX
-#define MOE_SBAUX kNonTemporal  // 32-row tiles: weight loads stream (nt)
-#endif
-#ifndef MOE_SPLIT_DOWN
-#define MOE_SPLIT_DOWN 1  // split the down projection's K when its tiles fill the chip few times
-#endif
-#ifndef MOE_WG_GM
-#define MOE_WG_GM 4  // weight-gradient tiles: M-tiles per group
-#endif
-#ifndef MOE_F8SBK
-#define MOE_F8SBK 128  // 32-row tiles with FP8 weights: K per stage (128-byte weight rows)
-#endif
-#ifndef MOE_F8SNS
-#define MOE_F8SNS 2
-#endif
-#ifndef MOE_F8SNW
-#define MOE_F8SNW 2  // 32-row tiles with FP8 weights: 64 output columns
-#endif
-#ifndef MOE_BNT_ROWS
-#define MOE_BNT_ROWS 256  // 256-row tiles: stream the weights up to this many rows per expert
-#endif
-
 namespace moe {
 namespace {
 
 constexpr int kXcds = 8;
 constexpr int kNonTemporal = 2;  // "nt" bit of a buffer load's cache policy
+
+// Tile parameters of the bf16 grouped GEMM (each measured; the record of the
+// alternatives is kept with the design notes).
+constexpr int kBK = 64;        // 256-row tiles: K per stage
+constexpr int kNS = 2;         // 256-row tiles: LDS stages
+constexpr int kDTN = 8;        // down GEMM: 32-column sub-tiles per 256-row tile
+constexpr int kLW = 4;         // waves that issue the global -> LDS loads
+constexpr int kNW = 4;         // waves across N in the 256-row tile (2 x kNW waves)
+constexpr int kSNW = 4;        // 32-row tiles: waves across N (one 32-column sub-tile each)
+constexpr int kSBK = 64;       // 32-row tiles: K per stage
+constexpr int kSNS = 3;        // 32-row tiles: stages
+constexpr int kSBAUX = kNonTemporal;  // 32-row tiles: weight loads stream (nt)
+constexpr int kWgGroupM = 4;   // weight-gradient tiles: M-tiles per group
+constexpr int kF8SBK = 128;    // 32-row tiles with FP8 weights: K per stage (128-byte rows)
+constexpr int kF8SNS = 2;      // 32-row tiles with FP8 weights: stages
+constexpr int kF8SNW = 2;      // 32-row tiles with FP8 weights: 64 output columns
+constexpr int kBntRows = 256;  // 256-row tiles: stream the weights up to this many rows per expert
 
 // Chunk swizzle of LDS row R (16-byte chunks).  256-byte rows (16 chunks),
 // 128-byte rows (8 chunks) and 64-byte rows (4 chunks): 16, 8 or 16
@@ -186,7 +157,7 @@ struct GemmCfg {
   static constexpr int STAGE = AREG + ROWSB * RBB;
   static constexpr int NINSTR = NIA + NIB;
   // the first LW waves issue the global -> LDS loads (LW <= NWAVES)
-  static constexpr int LW = (MOE_LW < NWAVES) ? MOE_LW : NWAVES;
+  static constexpr int LW = (kLW < NWAVES) ? kLW : NWAVES;
   static constexpr int IPW = NINSTR / LW;
   static_assert(NINSTR % LW == 0, "loads must split evenly over waves");
   static_assert(RBA <= 1024 && RBB <= 1024, "a row must fit one wave-level load");
@@ -332,7 +303,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
     const int local = logical - e * per_e;
     // groups of 4 M-tiles walk the N-tiles together: the 32 tiles an XCD
     // runs at once cover about 4 x 8 (M, N) tiles and share their operands
-    constexpr int kGroupM = MOE_WG_GM;
+    constexpr int kGroupM = kWgGroupM;
     const int grp = local / (kGroupM * n_nt);
     const int first_m = grp * kGroupM;
     const int gsize = min(kGroupM, n_mt - first_m);
@@ -918,7 +889,7 @@ hipError_t launch_down(const void* H, const void* W_down, int d, int d_ff, int E
 }  // namespace
 
 bool ffn_split_down(bool bf16, int E, int rows_per_expert, int d, int d_ff) {
-  if (!MOE_SPLIT_DOWN || !bf16 || rows_per_expert <= 64) return false;
+  if (!bf16 || rows_per_expert <= 64) return false;
   if (d_ff < 2048 || d_ff % 32 != 0) return false;
   // 256 x 256 tiles of the unsplit GEMM (from the mean rows per expert):
   // split when they fill the 256 CUs fewer than four times and leave the
@@ -931,7 +902,7 @@ bool ffn_split_down(bool bf16, int E, int rows_per_expert, int d, int d_ff) {
 
 int ffn_tile_code(bool bf16, int rows_per_expert, bool fp8) {
   const int bm = ffn_tile_rows(bf16, rows_per_expert, fp8);
-  return (bm == 256 && rows_per_expert > MOE_BNT_ROWS) ? kTallTileCode : bm;
+  return (bm == 256 && rows_per_expert > kBntRows) ? kTallTileCode : bm;
 }
 
 int ffn_tile_rows(bool bf16, int rows_per_expert, bool fp8) {
@@ -985,13 +956,13 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (fp8) {
-      err = launch_gemm<1, MOE_F8SNW, 1, 1, true, MOE_F8SBK, MOE_F8SNS, MOE_SBAUX, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales);
+      err = launch_gemm<1, kF8SNW, 1, 1, true, kF8SBK, kF8SNS, kSBAUX, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales);
       if (err != hipSuccess) return err;
-      return launch_gemm<1, MOE_F8SNW, 1, 1, false, MOE_F8SBK, MOE_F8SNS, MOE_SBAUX, true>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream, w_scales);
+      return launch_gemm<1, kF8SNW, 1, 1, false, kF8SBK, kF8SNS, kSBAUX, true>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream, w_scales);
     }
-    err = launch_gemm<1, MOE_SNW, 1, 1, true, MOE_SBK, MOE_SNS, MOE_SBAUX>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
+    err = launch_gemm<1, kSNW, 1, 1, true, kSBK, kSNS, kSBAUX>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
     if (err != hipSuccess) return err;
-    return launch_gemm<1, MOE_SNW, 1, 1, false, MOE_SBK, MOE_SNS, MOE_SBAUX>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
+    return launch_gemm<1, kSNW, 1, 1, false, kSBK, kSNS, kSBAUX>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
   }
   const int code = ffn_tile_code(bf16, rows_per_expert, fp8);
   if (!prefix_ready) {
@@ -1014,21 +985,21 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
   if (fp8) {
     // FP8 weights, many rows per expert: the tall 256-row tiles of the bf16
     // path (the weight tiles are shared by several M-tiles through L2)
-    err = launch_gemm<2, MOE_NW, 5, 4 / MOE_NW, true, MOE_BK, 2, 0, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales);
+    err = launch_gemm<2, kNW, 5, 4 / kNW, true, kBK, 2, 0, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales);
     if (err != hipSuccess) return err;
-    return launch_down<2, MOE_NW, 5, MOE_DTN / MOE_NW, MOE_BK, 2, 0, true>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, w_scales, defer);
+    return launch_down<2, kNW, 5, kDTN / kNW, kBK, 2, 0, true>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, w_scales, defer);
   }
-  if (rows_per_expert <= MOE_BNT_ROWS) {
+  if (rows_per_expert <= kBntRows) {
     // about one M-tile per expert: every weight tile is read once
-    err = launch_gemm<2, MOE_NW, 4, 4 / MOE_NW, true, MOE_BK, MOE_NS, kNonTemporal>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
+    err = launch_gemm<2, kNW, 4, 4 / kNW, true, kBK, kNS, kNonTemporal>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
     if (err != hipSuccess) return err;
-    return launch_down<2, MOE_NW, 4, MOE_DTN / MOE_NW, MOE_BK, MOE_NS, kNonTemporal, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr, defer);
+    return launch_down<2, kNW, 4, kDTN / kNW, kBK, kNS, kNonTemporal, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr, defer);
   }
   // several M-tiles per expert: tall tiles (the schedule merges remainders
   // of up to 64 rows into the expert's last tile)
-  err = launch_gemm<2, MOE_NW, 5, 4 / MOE_NW, true, MOE_BK, 2, 0>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
+  err = launch_gemm<2, kNW, 5, 4 / kNW, true, kBK, 2, 0>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
   if (err != hipSuccess) return err;
-  return launch_down<2, MOE_NW, 5, MOE_DTN / MOE_NW, MOE_BK, 2, 0, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr, defer);
+  return launch_down<2, kNW, 5, kDTN / kNW, kBK, 2, 0, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr, defer);
 }
 
 }  // namespace moe
@@ -1062,22 +1033,22 @@ hipError_t launch_grouped_ffn_train(const void* X_perm, const int32_t* offsets,
   a.G = static_cast<uint16_t*>(G);
   a.U = static_cast<uint16_t*>(U);
   if (bm == 32) {
-    err = launch_gemm_args<1, MOE_SNW, 1, 1, true, MOE_SBK, MOE_SNS, MOE_SBAUX, false, 1>(a, R, stream);
+    err = launch_gemm_args<1, kSNW, 1, 1, true, kSBK, kSNS, kSBAUX, false, 1>(a, R, stream);
     if (err != hipSuccess) return err;
-    return launch_gemm<1, MOE_SNW, 1, 1, false, MOE_SBK, MOE_SNS, MOE_SBAUX>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
+    return launch_gemm<1, kSNW, 1, 1, false, kSBK, kSNS, kSBAUX>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
   }
   // the down projection as in launch_grouped_ffn (same split, same scratch
   // place for the second K half), so the output equals moe_forward's
   float* Y_half = ffn_half_sums(mt_prefix, R, E, d, d_ff, true, rows_per_expert);
-  if (rows_per_expert <= MOE_BNT_ROWS) {
-    err = launch_gemm_args<2, MOE_NW, 4, 4 / MOE_NW, true, MOE_BK, MOE_NS, kNonTemporal, false, 1>(a, R, stream);
+  if (rows_per_expert <= kBntRows) {
+    err = launch_gemm_args<2, kNW, 4, 4 / kNW, true, kBK, kNS, kNonTemporal, false, 1>(a, R, stream);
     if (err != hipSuccess) return err;
-    return launch_down<2, MOE_NW, 4, MOE_DTN / MOE_NW, MOE_BK, MOE_NS, kNonTemporal, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr);
+    return launch_down<2, kNW, 4, kDTN / kNW, kBK, kNS, kNonTemporal, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr);
   }
   // tall tiles, with the schedule of ffn_tile_code as in launch_grouped_ffn
-  err = launch_gemm_args<2, MOE_NW, 5, 4 / MOE_NW, true, MOE_BK, 2, 0, false, 1>(a, R, stream);
+  err = launch_gemm_args<2, kNW, 5, 4 / kNW, true, kBK, 2, 0, false, 1>(a, R, stream);
   if (err != hipSuccess) return err;
-  return launch_down<2, MOE_NW, 5, MOE_DTN / MOE_NW, MOE_BK, 2, 0, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr);
+  return launch_down<2, kNW, 5, kDTN / kNW, kBK, 2, 0, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr);
 }
 
 hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const void* W_gate,
@@ -1118,23 +1089,23 @@ hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const v
   x.C1 = dX_perm + R * d;  // the second K half's partial sums
   x.lda = 2 * d_ff;
   if (bm == 32) {
-    err = launch_gemm_args<1, MOE_SNW, 1, 1, false, MOE_SBK, MOE_SNS, MOE_SBAUX, false, 2>(a, R, stream);
+    err = launch_gemm_args<1, kSNW, 1, 1, false, kSBK, kSNS, kSBAUX, false, 2>(a, R, stream);
     if (err != hipSuccess) return err;
-    return launch_gemm_args<1, MOE_SNW, 1, 1, false, MOE_SBK, MOE_SNS, MOE_SBAUX, false, 4>(x, R, stream);
+    return launch_gemm_args<1, kSNW, 1, 1, false, kSBK, kSNS, kSBAUX, false, 4>(x, R, stream);
   }
-  if (rows_per_expert <= MOE_BNT_ROWS) {
-    err = launch_gemm_args<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, kNonTemporal, false, 2>(a, R, stream);
+  if (rows_per_expert <= kBntRows) {
+    err = launch_gemm_args<2, kNW, 4, kDTN / kNW, false, kBK, kNS, kNonTemporal, false, 2>(a, R, stream);
     if (err != hipSuccess) return err;
-    return launch_gemm_args<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, kNonTemporal, false, 4>(x, R, stream);
+    return launch_gemm_args<2, kNW, 4, kDTN / kNW, false, kBK, kNS, kNonTemporal, false, 4>(x, R, stream);
   }
   if (tall) {
-    err = launch_gemm_args<2, MOE_NW, 5, MOE_DTN / MOE_NW, false, MOE_BK, 2, 0, false, 2>(a, R, stream);
+    err = launch_gemm_args<2, kNW, 5, kDTN / kNW, false, kBK, 2, 0, false, 2>(a, R, stream);
     if (err != hipSuccess) return err;
-    return launch_gemm_args<2, MOE_NW, 5, MOE_DTN / MOE_NW, false, MOE_BK, 2, 0, false, 4>(x, R, stream);
+    return launch_gemm_args<2, kNW, 5, kDTN / kNW, false, kBK, 2, 0, false, 4>(x, R, stream);
   }
-  err = launch_gemm_args<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, 0, false, 2>(a, R, stream);
+  err = launch_gemm_args<2, kNW, 4, kDTN / kNW, false, kBK, kNS, 0, false, 2>(a, R, stream);
   if (err != hipSuccess) return err;
-  return launch_gemm_args<2, MOE_NW, 4, MOE_DTN / MOE_NW, false, MOE_BK, MOE_NS, 0, false, 4>(x, R, stream);
+  return launch_gemm_args<2, kNW, 4, kDTN / kNW, false, kBK, kNS, 0, false, 4>(x, R, stream);
 }
 
 hipError_t launch_wgrad(const void* A, int lda, int M, const void* B, int ldb, int N,

@@ -263,10 +263,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(
 
 constexpr int kRtTok = 128;  // tokens per logits workgroup (4 waves x 32)
 constexpr int kRtK = 32;     // K per stage: one 16x16x32 MFMA k-step
-#ifndef MOE_RZS
-#define MOE_RZS 2
-#endif
-constexpr int kRtZ = MOE_RZS;  // expert groups of a wide router (EP >= 128)
+constexpr int kRtZ = 2;  // expert groups of a wide router (EP >= 128)
 
 __device__ __forceinline__ uint32_t rt_swz(uint32_t r) { return ((r >> 1) ^ (r >> 3)) & 3u; }
 
@@ -437,10 +434,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
 
 // Few tokens (bf16): K-split FMA partial logits (no W_r split) + select.
 constexpr int kSmallT = 64;
-#ifndef MOE_RKS
-#define MOE_RKS 64
-#endif
-constexpr int kSmallKS = MOE_RKS;  // K per workgroup
+constexpr int kSmallKS = 64;  // K per workgroup
 
 // Router statistics (monitoring).  Same selection as router_select_kernel,
 // one wavefront per token; each lane also forms, for the experts it holds,
