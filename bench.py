@@ -3,9 +3,12 @@
 One step = one moe_forward call (router, permute, grouped SwiGLU FFN,
 combine) over one batch of the Mixtral-8x7B-shaped workload (T=4096,
 d_model=4096, E=8, top-2, d_ff=14336, bf16 with fp32 accumulation, router in
-fp32), inputs resident in HBM.  Prints one JSON line.
+fp32), inputs resident in HBM.  Prints one JSON line.  After the headline
+workload the other workloads run in the same process (`configs`: each one's
+step time, grouped-FFN roofline fraction and stage rates).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-configs]
                     [--no-cpu-baseline] [--cpu-sample-tokens N]
 """
 
@@ -59,6 +62,11 @@ def _parse():
                     help="also time the step captured once in a HIP graph and "
                          "replayed (the library allocates and synchronises "
                          "nothing, so a whole layer call can be captured)")
+    ap.add_argument("--configs", action=argparse.BooleanOptionalAction, default=True,
+                    help="after the headline workload, run every other workload "
+                         "in the same process and report each one's step time, "
+                         "grouped-FFN roofline fraction and stage rates (the "
+                         "`configs` object)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -304,6 +312,153 @@ def _cpu_baseline(wl, dev, ntok, min_s=10.0, max_s=30.0, shared=None, fp8_scales
                       f"fp64 NumPy per-expert loop, {runs} run(s), {total:.1f} s wall"}
 
 
+def _layer_bytes(wl, N, active, a_b, w_b):
+    """Algorithmic HBM bytes of each stage (inputs read once, outputs written
+    once): route reads X and W_r and writes ids and weights; the permute reads
+    X and the ids and writes X_perm and the index maps; the FFN reads the
+    active experts' weights and X_perm and writes Y_perm (fp32); the combine
+    reads Y_perm, the dest rows and weights and writes the fp32 output."""
+    T, d, E, k, dff = wl.T, wl.d_model, wl.E, wl.top_k, wl.d_ff
+    return {"route": T * d * a_b + E * d * 4 + T * k * 8,
+            "permute": T * d * a_b + N * d * a_b + T * k * 24 + N * 4,
+            "grouped_ffn": 3 * active * d * dff * w_b + N * d * a_b + N * d * 4,
+            "combine": N * d * 4 + T * d * 4 + T * k * 8}
+
+
+def _run_layer(wl, steps, warmup, fp8=False):
+    """Inputs of workload `wl` on the device, `warmup` untimed then `steps`
+    timed moe_forward calls (two events around them, one after each), then
+    each stage through its own entry point.  Returns a dict of the timings,
+    the routing outcome and the objects the optional extras reuse."""
+    import torch
+
+    import mixture_experts_layer_wavefront_amd as M
+    from mixture_experts_layer_wavefront_amd import workloads as W
+
+    w_scales = None
+    if fp8:
+        d8 = W.make_device_fp8(wl, "cuda")
+        dev = dict(X=d8["X"], W_r=d8["W_r"], bias=d8["bias"], W_gate=d8["Q_gate"],
+                   W_up=d8["Q_up"], W_down=d8["Q_down"])
+        w_scales = d8["scales"]
+    else:
+        dev = W.make_device(wl, "cuda")
+    p = M.problem(wl.T, wl.d_model, wl.E, wl.top_k, wl.d_ff,
+                  wl.capacity_factor, wl.dtype, wl.gating, "f32",
+                  w_dtype="fp8" if fp8 else None)
+    ws = torch.empty(M.workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    out = torch.empty((wl.T, wl.d_model), dtype=torch.float32, device="cuda")
+    stats = torch.empty(2 * wl.E + 2, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    a = (dev["X"], dev["W_r"], dev["bias"], dev["W_gate"], dev["W_up"], dev["W_down"])
+
+    def step():
+        if fp8:
+            M.moe_forward_scaled(p, *a, w_scales, out=out, stats=stats, workspace=ws)
+        else:
+            M.moe_forward(p, *a, out=out, stats=stats, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(steps):
+        step()
+        evs[i + 1].record(stream)
+    evs[-1].synchronize()
+    ms = evs[0].elapsed_time(evs[-1]) / steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = stats.cpu().numpy()
+    N = int(st[2 * wl.E])                       # kept token copies
+    counts = st[:wl.E]
+    active = int(np.count_nonzero(st[wl.E + 1:2 * wl.E + 1] - st[wl.E:2 * wl.E]))
+
+    # ---- per stage (same kernels, called through the stage entry points) ----
+    idx, w = M.moe_route(p, dev["X"], dev["W_r"], dev["bias"])
+    perm = M.moe_permute(p, dev["X"], idx)
+    if fp8:
+        ffn = lambda Yo=None, w=None: M.moe_grouped_ffn_scaled(  # noqa: E731
+            p, perm["X_perm"], perm["offsets"], dev["W_gate"], dev["W_up"],
+            dev["W_down"], w_scales, Yo, w)
+    else:
+        ffn = lambda Yo=None, w=None: M.moe_grouped_ffn(  # noqa: E731
+            p, perm["X_perm"], perm["offsets"], dev["W_gate"], dev["W_up"],
+            dev["W_down"], Yo, w)
+    Y = ffn()
+    o2 = M.moe_combine(p, Y, perm["dest_row"], w)
+    ffn_ws = torch.empty(M.grouped_ffn_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    perm_ws = torch.empty(M.permute_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    n = max(steps, 5)
+    t_route = _time_loop(lambda: M.moe_route(p, dev["X"], dev["W_r"], dev["bias"], idx, w),
+                         n, stream)
+    t_perm = _time_loop(lambda: M.moe_permute(p, dev["X"], idx, perm_ws, out=perm), n, stream)
+    t_ffn = _time_loop(lambda: ffn(Y, ffn_ws), n, stream)
+    t_comb = _time_loop(lambda: M.moe_combine(p, Y, perm["dest_row"], w, o2), n, stream)
+    torch.cuda.synchronize()
+
+    a_b = 2 if wl.dtype == W.BF16 else 4
+    w_b = 1 if fp8 else a_b
+    by = _layer_bytes(wl, N, active, a_b, w_b)
+    ffn_flops = 6.0 * N * wl.d_model * wl.d_ff
+    return dict(wl=wl, p=p, dev=dev, a=a, ws=ws, out=out, stats=stats, stream=stream,
+                step=step, w_scales=w_scales, ms=ms, per_step=per_step, wall=wall, st=st,
+                N=N, counts=counts, active=active, idx=idx, w=w, perm=perm, ffn=ffn, Y=Y,
+                ffn_ws=ffn_ws, n=n, bytes=by, ffn_flops=ffn_flops,
+                stages_ms={"route": t_route, "permute": t_perm, "grouped_ffn": t_ffn,
+                           "combine": t_comb})
+
+
+def _ffn_roofline(r):
+    """The grouped FFN launch against its binding roofline: MFMA when its
+    algorithmic flops per algorithmic HBM byte reach the machine balance (bf16
+    MFMA peak / HBM peak), else HBM."""
+    t_ffn = r["stages_ms"]["grouped_ffn"]
+    flops, by = r["ffn_flops"], r["bytes"]["grouped_ffn"]
+    if flops / by >= PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3:
+        tf = flops / (t_ffn * 1e-3) / 1e12
+        return dict(bound="mfma", achieved=tf, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=tf / PEAK_BF16_TFLOPS)
+    gbs = by / (t_ffn * 1e6)
+    return dict(bound="hbm", achieved=gbs, peak=PEAK_HBM_GBS, unit="GB/s",
+                frac=gbs / PEAK_HBM_GBS)
+
+
+def _workload_text(wl):
+    return (f"{wl.name}: one MoE FFN layer forward, T={wl.T}, d_model={wl.d_model}, "
+            f"E={wl.E}, top-{wl.top_k}, SwiGLU d_ff={wl.d_ff}, {wl.dtype} "
+            f"weights/activations, fp32 router and accumulation, fp32 output"
+            + (f", capacity factor {wl.capacity_factor}" if wl.capacity_factor > 0 else "")
+            + (f", Zipf({wl.zipf_s}) router bias" if wl.zipf_s > 0 else ""))
+
+
+def _config_summary(r):
+    """One workload's figures for the `configs` object of the JSON line."""
+    from mixture_experts_layer_wavefront_amd import workloads as W
+    wl, sm, by = r["wl"], r["stages_ms"], r["bytes"]
+    step_bytes = sum(by.values())
+    ffn = _ffn_roofline(r)
+    return {
+        "workload": _workload_text(wl),
+        "ms_per_step": r["ms"], "ms_per_step_median": r["per_step"][len(r["per_step"]) // 2],
+        "ms_per_step_min": r["per_step"][0],
+        "tokens_per_s": wl.T / (r["ms"] * 1e-3),
+        "step_algorithmic_bytes": step_bytes,
+        "step_hbm_frac": step_bytes / (r["ms"] * 1e-3) / (PEAK_HBM_GBS * 1e9),
+        "ffn": dict(ffn, ms=sm["grouped_ffn"], flops=r["ffn_flops"],
+                    bytes=by["grouped_ffn"]),
+        "stages_ms": sm,
+        "stages_gbs": {k: by[k] / (sm[k] * 1e6) for k in ("route", "permute", "combine")},
+        "routing": {"kept_copies": r["N"], "dropped": int(r["st"][-1]),
+                    "active_experts": r["active"],
+                    "max_over_mean_load": float(r["counts"].max() /
+                                                max(r["counts"].mean(), 1e-9))},
+    }
+
+
 def main():
     args = _parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -323,121 +478,25 @@ def main():
 
     wl = W.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
-    if args.fp8:
-        if args.shared_dff or args.router_stats:
-            sys.exit("--fp8 combines with neither --shared-dff nor --router-stats")
-        d8 = W.make_device_fp8(wl, "cuda")
-        dev = dict(X=d8["X"], W_r=d8["W_r"], bias=d8["bias"], W_gate=d8["Q_gate"],
-                   W_up=d8["Q_up"], W_down=d8["Q_down"])
-        w_scales = d8["scales"]
-    else:
-        dev = W.make_device(wl, "cuda")
-    p = M.problem(wl.T, wl.d_model, wl.E, wl.top_k, wl.d_ff,
-                  wl.capacity_factor, wl.dtype, wl.gating, "f32",
-                  w_dtype="fp8" if args.fp8 else None)
-    ws = torch.empty(M.workspace_bytes(p), dtype=torch.uint8, device="cuda")
-    out = torch.empty((wl.T, wl.d_model), dtype=torch.float32, device="cuda")
-    stats = torch.empty(2 * wl.E + 2, dtype=torch.int32, device="cuda")
-    stream = torch.cuda.current_stream()
-    a = (dev["X"], dev["W_r"], dev["bias"], dev["W_gate"], dev["W_up"],
-         dev["W_down"])
-
-    def step():
-        if args.fp8:
-            M.moe_forward_scaled(p, *a, w_scales, out=out, stats=stats, workspace=ws)
-        else:
-            M.moe_forward(p, *a, out=out, stats=stats, workspace=ws)
-
-    shared = None
-    if args.shared_dff > 0:
-        S = W.make_shared_device(wl, args.shared_dff, "cuda")
-        ws_sh = torch.empty(M.forward_shared_workspace_bytes(p, args.shared_dff),
-                            dtype=torch.uint8, device="cuda")
-
-        def step():  # noqa: F811
-            M.moe_forward_shared(p, args.shared_dff, *a, *S, out=out, stats=stats,
-                                 workspace=ws_sh)
-
-        def step_serial():
-            M.moe_forward_shared(p, args.shared_dff, *a, *S, out=out, stats=stats,
-                                 workspace=ws_sh, side_stream=None)
-        shared = (S, ws_sh, step_serial)
-
-    for _ in range(args.warmup):
-        step()
-    # K steps between two events, with an event after each step as well
-    # (their gaps give the per-step median and minimum)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    evs[0].record(stream)
-    for i in range(args.steps):
-        step()
-        evs[i + 1].record(stream)
-    evs[-1].synchronize()
-    ms = evs[0].elapsed_time(evs[-1]) / args.steps
-    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    st = stats.cpu().numpy()
-    N = int(st[2 * wl.E])                       # kept token copies
-    counts = st[:wl.E]
-    active = int(np.count_nonzero(st[wl.E + 1:2 * wl.E + 1] - st[wl.E:2 * wl.E]))
-
-    # ---- per stage (same kernels, called through the stage entry points) ----
-    idx, w = M.moe_route(p, dev["X"], dev["W_r"], dev["bias"])
-    perm = M.moe_permute(p, dev["X"], idx)
-    if args.fp8:
-        ffn = lambda Yo=None, w=None: M.moe_grouped_ffn_scaled(  # noqa: E731
-            p, perm["X_perm"], perm["offsets"], dev["W_gate"], dev["W_up"],
-            dev["W_down"], w_scales, Yo, w)
-    else:
-        ffn = lambda Yo=None, w=None: M.moe_grouped_ffn(  # noqa: E731
-            p, perm["X_perm"], perm["offsets"], dev["W_gate"], dev["W_up"],
-            dev["W_down"], Yo, w)
-    Y = ffn()
-    o2 = M.moe_combine(p, Y, perm["dest_row"], w)
-    ffn_ws = torch.empty(M.grouped_ffn_workspace_bytes(p), dtype=torch.uint8,
-                         device="cuda")
-    perm_ws = torch.empty(M.permute_workspace_bytes(p), dtype=torch.uint8,
-                          device="cuda")
-    n = max(args.steps, 5)
-    t_route = _time_loop(lambda: M.moe_route(p, dev["X"], dev["W_r"], dev["bias"],
-                                             idx, w), n, stream)
-    t_perm = _time_loop(lambda: M.moe_permute(p, dev["X"], idx, perm_ws, out=perm),
-                        n, stream)
-    t_ffn = _time_loop(lambda: ffn(Y, ffn_ws), n, stream)
-    t_comb = _time_loop(lambda: M.moe_combine(p, Y, perm["dest_row"], w, o2),
-                        n, stream)
-    torch.cuda.synchronize()
-
-    a_b = 2 if wl.dtype == W.BF16 else 4
-    w_b = 1 if args.fp8 else a_b
+    if args.fp8 and (args.shared_dff or args.router_stats):
+        sys.exit("--fp8 combines with neither --shared-dff nor --router-stats")
+    r = _run_layer(wl, args.steps, args.warmup, fp8=args.fp8)
+    p, dev, a, ws, out, stats, stream = (r[k] for k in ("p", "dev", "a", "ws", "out",
+                                                          "stats", "stream"))
+    step, ms, per_step, n, N = r["step"], r["ms"], r["per_step"], r["n"], r["N"]
+    ffn, Y, ffn_ws, perm, w_scales = r["ffn"], r["Y"], r["ffn_ws"], r["perm"], r["w_scales"]
     T, d, E, k, dff = wl.T, wl.d_model, wl.E, wl.top_k, wl.d_ff
-    ffn_flops = 6.0 * N * d * dff
-    ffn_tflops = ffn_flops / (t_ffn * 1e-3) / 1e12
-    bytes_route = T * d * a_b + E * d * 4 + T * k * 8
-    bytes_perm = T * d * a_b + N * d * a_b + T * k * 24 + N * 4
-    bytes_comb = N * d * 4 + T * d * 4 + T * k * 8
-    bytes_ffn = 3 * active * d * dff * w_b + N * d * a_b + N * d * 4
+    ffn_flops, by = r["ffn_flops"], r["bytes"]
+    t_route = r["stages_ms"]["route"]
 
-    # the FFN's bound: MFMA when its algorithmic flops per HBM byte exceed the
-    # machine balance (bf16 MFMA peak / HBM peak), else HBM
-    roofline = {"kernel": "grouped SwiGLU FFN (gate/up GEMM + SwiGLU epilogue, "
-                          "down GEMM)",
-                "traffic": None if args.fp8 else _traffic(args.workload),
-                "flops_per_launch": ffn_flops, "bytes_per_launch": bytes_ffn,
-                "ms_per_launch": t_ffn}
-    if ffn_flops / bytes_ffn >= PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3:
-        roofline.update(bound="mfma", achieved=ffn_tflops, peak=PEAK_BF16_TFLOPS,
-                        unit="TFLOP/s", frac=ffn_tflops / PEAK_BF16_TFLOPS)
-    else:
-        gbs = bytes_ffn / (t_ffn * 1e6)
-        roofline.update(bound="hbm", achieved=gbs, peak=PEAK_HBM_GBS, unit="GB/s",
-                        frac=gbs / PEAK_HBM_GBS)
-    roofline = {k: roofline[k] for k in ("bound", "kernel", "achieved", "peak", "unit",
-                                         "frac", "traffic", "flops_per_launch",
-                                         "bytes_per_launch", "ms_per_launch")}
+    roofline = dict(_ffn_roofline(r),
+                    kernel="grouped SwiGLU FFN (gate/up GEMM + SwiGLU epilogue, down GEMM)",
+                    traffic=None if args.fp8 else _traffic(args.workload),
+                    flops_per_launch=ffn_flops, bytes_per_launch=by["grouped_ffn"],
+                    ms_per_launch=r["stages_ms"]["grouped_ffn"])
+    roofline = {k_: roofline[k_] for k_ in ("bound", "kernel", "achieved", "peak", "unit",
+                                            "frac", "traffic", "flops_per_launch",
+                                            "bytes_per_launch", "ms_per_launch")}
 
     line = {
         "metric": "MoE-layer tokens/s + grouped-GEMM TFLOP/s (% bf16 MFMA peak), "
@@ -456,31 +515,68 @@ def main():
         "dtype": ("bf16 (fp8 e4m3 expert weights)" if args.fp8 else "bf16")
                  if wl.dtype == W.BF16 else "f32",
         "data": "synthetic (seeded; random weights of the layer's shape)",
-        "config": {"workload": f"{wl.name}: one MoE FFN layer forward, T={T}, "
-                               f"d_model={d}, E={E}, top-{k}, SwiGLU d_ff={dff}, "
-                               f"{wl.dtype} weights/activations, fp32 router and "
-                               f"accumulation, fp32 output",
+        "config": {"workload": _workload_text(wl),
                    "T": T, "d_model": d, "E": E, "top_k": k, "d_ff": dff,
                    "capacity_factor": wl.capacity_factor,
                    "gating": ["topk_then_softmax", "softmax_then_topk"][wl.gating]},
         "roofline": roofline,
-        "stages_ms": {"route": t_route, "permute": t_perm, "grouped_ffn": t_ffn,
-                      "combine": t_comb},
+        "stages_ms": r["stages_ms"],
         # router logits: 2 T d E algorithmic flops of fp32 logits per step
         # (route stage: logits, top-k and gate weights).  fp32 layers compute
         # them with fp32 vector FMAs (peak 157.3 TFLOP/s); bf16 layers as three
         # exact bf16 products on the matrix cores, 3x the flops against the
         # dense bf16 peak (2500 TFLOP/s)
         "stages_tflops": _route_tflops(T, d, E, t_route, wl.dtype == W.BF16),
-        "stages_gbs": {"route": bytes_route / (t_route * 1e6),
-                       "permute": bytes_perm / (t_perm * 1e6),
-                       "combine": bytes_comb / (t_comb * 1e6),
-                       "grouped_ffn_weights_and_rows": bytes_ffn / (t_ffn * 1e6)},
-        "routing": {"kept_copies": N, "dropped": int(st[-1]),
-                    "active_experts": active,
-                    "max_over_mean_load": float(counts.max() / max(counts.mean(), 1e-9))},
-        "wall_s_timed": wall,
+        "stages_gbs": {"route": by["route"] / (t_route * 1e6),
+                       "permute": by["permute"] / (r["stages_ms"]["permute"] * 1e6),
+                       "combine": by["combine"] / (r["stages_ms"]["combine"] * 1e6),
+                       "grouped_ffn_weights_and_rows":
+                           by["grouped_ffn"] / (r["stages_ms"]["grouped_ffn"] * 1e6)},
+        "routing": {"kept_copies": N, "dropped": int(r["st"][-1]),
+                    "active_experts": r["active"],
+                    "max_over_mean_load": float(r["counts"].max() /
+                                                max(r["counts"].mean(), 1e-9))},
+        "wall_s_timed": r["wall"],
     }
+    shared = None
+    if args.shared_dff > 0:
+        S = W.make_shared_device(wl, args.shared_dff, "cuda")
+        ws_sh = torch.empty(M.forward_shared_workspace_bytes(p, args.shared_dff),
+                            dtype=torch.uint8, device="cuda")
+
+        def step():  # noqa: F811 -- the headline step is the layer with the shared expert
+            M.moe_forward_shared(p, args.shared_dff, *a, *S, out=out, stats=stats,
+                                 workspace=ws_sh)
+
+        def step_serial():
+            M.moe_forward_shared(p, args.shared_dff, *a, *S, out=out, stats=stats,
+                                 workspace=ws_sh, side_stream=None)
+        shared = (S, ws_sh, step_serial)
+        for _ in range(args.warmup):
+            step()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for i in range(args.steps):
+            step()
+            evs[i + 1].record(stream)
+        evs[-1].synchronize()
+        t_routed = ms
+        ms = evs[0].elapsed_time(evs[-1]) / args.steps
+        per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+        line.update(value=T / (ms * 1e-3), ms_per_step=ms,
+                    ms_per_step_median=per_step[len(per_step) // 2],
+                    ms_per_step_min=per_step[0])
+        for _ in range(2):
+            step_serial()
+        t_serial = _time_loop(step_serial, n, stream)
+        line["config"]["shared_d_ff"] = args.shared_dff
+        line["config"]["workload"] += (f", plus a shared expert (SwiGLU d_ff="
+                                       f"{args.shared_dff}) on every token")
+        line["shared_expert"] = {
+            "ms_per_step_side_stream": ms, "ms_per_step_one_stream": t_serial,
+            "ms_routed_layer_alone": t_routed,
+            "shared_ffn_flops": 6.0 * T * d * args.shared_dff}
     if args.router_stats:
         ws_st = torch.empty(M.forward_stats_workspace_bytes(p), dtype=torch.uint8,
                             device="cuda")
@@ -499,19 +595,6 @@ def main():
                                 "ms_per_step_without": t_plain,
                                 "aux_loss": float(rs[2 * wl.E]),
                                 "z_loss": float(rs[2 * wl.E + 1])}
-    if shared is not None:
-        S, ws_sh, step_serial = shared
-        for _ in range(2):
-            step_serial()
-        t_serial = _time_loop(step_serial, n, stream)
-        t_routed = _time_loop(lambda: M.moe_forward(p, *a, out=out, stats=stats,
-                                                    workspace=ws), n, stream)
-        sh_flops = 6.0 * T * d * args.shared_dff
-        line["config"]["shared_d_ff"] = args.shared_dff
-        line["config"]["workload"] += f", plus a shared expert (SwiGLU d_ff={args.shared_dff}) on every token"
-        line["shared_expert"] = {
-            "ms_per_step_side_stream": ms, "ms_per_step_one_stream": t_serial,
-            "ms_routed_layer_alone": t_routed, "shared_ffn_flops": sh_flops}
     if args.backward:
         if args.fp8 or wl.dtype != W.BF16:
             sys.exit("--backward needs a bf16 layer without --fp8")
@@ -563,6 +646,18 @@ def main():
             wl, dev, args.cpu_sample_tokens,
             shared=None if shared is None else [t.float().cpu().numpy() for t in shared[0]],
             fp8_scales=w_scales.cpu().numpy() if args.fp8 else None)
+    if args.configs:
+        # the other workloads, one after the other in the same process (the
+        # headline's tensors are released first)
+        del r, dev, a, ws, out, stats, perm, Y, ffn, ffn_ws, shared, step
+        line["configs"] = {}
+        for name, cw in W.WORKLOADS.items():
+            if name == wl.name:
+                continue
+            torch.cuda.empty_cache()
+            rc = _run_layer(cw, args.steps, args.warmup)
+            line["configs"][name] = _config_summary(rc)
+            del rc
     print(json.dumps(line), flush=True)
 
 
