@@ -26,36 +26,46 @@ BF16_TOL = 2e-2
 GATE_W_TOL = 1e-4
 
 
-U_BF16 = 2.0 ** -8   # bf16 unit roundoff
+# Shapes with a tiny d_ff have heavy-tailed outputs: there, rounding the
+# hidden activation H to bf16 (the activation dtype H is stored in) can alone
+# move the largest output elements by more than 2e-2 of the RMS.  For such a
+# shape the bar is H_MARGIN times the error of a CPU emulation that rounds
+# the oracle's exact H correctly (nearest even) and finishes in fp64; the
+# margin covers the few H elements lying so close to a rounding midpoint that
+# the kernel's fp32 G and U round them the other way.
+H_MARGIN = 1.25
 
 
-def h_rounding_bound(X_perm, offsets, W_gate, W_up, W_down):
-    """Per kept row r and output column i, u * sum_j |H_rj| |W_down[e]_ij|
-    (u = 2^-8): the largest change of Y_perm that rounding the hidden
-    activation H (stored in the activation dtype, bf16) can cause, since each
-    H element moves by at most u |H|.  From fp64 values of the oracle's own
-    H; rows in expert order as in X_perm."""
+def bf16_rne(x):
+    """fp64 values rounded to bf16 (via fp32, round to nearest even)."""
+    x = np.asarray(x, np.float64).astype(np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
+    return r.view(np.float32).astype(np.float64)
+
+
+def y_with_rounded_h(X_perm, offsets, W_gate, W_up, W_down):
+    """The oracle's expert FFN on the rows of X_perm (expert order) with only
+    H = silu(G) U rounded to bf16: G, U, H and the down projection in fp64,
+    the fp64 H rounded once to the nearest bf16."""
     X_perm = np.asarray(X_perm, np.float64)
-    out = np.zeros((X_perm.shape[0], np.shape(W_down)[1]))
+    Y = np.zeros((X_perm.shape[0], np.shape(W_down)[1]))
     for e in range(len(offsets) - 1):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi == lo:
             continue
         A = X_perm[lo:hi]
-        G = A @ np.asarray(W_gate[e], np.float64).T
-        U = A @ np.asarray(W_up[e], np.float64).T
-        H = O.silu(G) * U
-        out[lo:hi] = U_BF16 * (np.abs(H) @ np.abs(np.asarray(W_down[e], np.float64)).T)
-    return out
+        H = O.silu(A @ np.asarray(W_gate[e], np.float64).T) * \
+            (A @ np.asarray(W_up[e], np.float64).T)
+        Y[lo:hi] = bf16_rne(H) @ np.asarray(W_down[e], np.float64).T
+    return Y
 
 
-def bounded_err(g, o, B):
-    """max |g - o| / (BF16_TOL rms(o) + B), elementwise allowance B."""
-    g = np.asarray(g, np.float64)
-    o = np.asarray(o, np.float64)
-    if o.size == 0:
-        return 0.0
-    return float(np.max(np.abs(g - o) / (BF16_TOL * rms(o) + B + 1e-300)))
+def emulated_tol(e_emul):
+    """The bar of a bf16 comparison whose correctly rounded bf16-H emulation
+    has error e_emul (max |.| / rms): the plain bar, or H_MARGIN e_emul when
+    the rounding of H alone exceeds it."""
+    return max(BF16_TOL, H_MARGIN * e_emul)
 
 
 def rms(o):

@@ -13,9 +13,11 @@ errors of independent terms add in quadrature); every element of every
 gradient must satisfy |g - o| <= 6 sigma + 1e-5 rms(o) (the second term
 covers fp32 accumulation).  The same model applied to a CPU simulation of
 the rounding points gives at most 3.7 sigma on the shapes below.  Over each
-tensor, rms(g - o) / rms(o) <= 1e-2 as well, or, where the exact values
-cancel (a router-bias gradient of three experts sums terms of both signs),
-rms(g - o) <= 2 rms(sigma).  Exact checks: zero
+tensor, rms(g - o) / rms(o) <= 1e-2 as well.  One exception: the router-bias
+gradient dbias[e] = sum_t dl[t, e] sums terms of both signs, and where those
+cancel (rms(dbias) <= 0.1 rms of the sums of the terms' magnitudes, as with
+three experts) its exact values are small against the rounding noise of the
+terms; for it rms(g - o) <= 2 rms(sigma) is required instead.  Exact checks: zero
 gradients of unused experts and of fully dropped tokens, zero router
 gradient at top-1 with the softmax of the selected logit, the training
 forward's output equal to moe_forward's bit for bit, two backward runs
@@ -153,11 +155,23 @@ def _error_sigma(host, dout, k, cf, gating, idx):
     return {n: np.sqrt(v) for n, v in var.items()}
 
 
+CANCEL_MAX = 0.1     # dbias: rms(exact) / rms(sum of |terms|) at which it cancels
+
+
+def _dbias_cancellation(o):
+    """rms of the exact router-bias gradient over the rms of the sums of its
+    terms' magnitudes (dbias[e] = sum_t dl[t, e]): near 1 without
+    cancellation, near 0 when the terms cancel."""
+    mag = np.abs(o["dl"]).sum(axis=0)
+    return float(np.sqrt(np.mean(o["dbias"] ** 2)) /
+                 max(np.sqrt(np.mean(mag ** 2)), 1e-300))
+
+
 def check_gradients(name, wl, g, o, sigma):
     """Every gradient element within Z_MAX sigma of the oracle (plus the fp32
-    floor), rms error <= BWD_RMS_TOL or at most twice the rms of sigma,
-    unused experts exactly zero, and no router gradient at top-1 with the
-    softmax of the selected logit."""
+    floor), rms error <= BWD_RMS_TOL (a cancelling dbias: at most twice the
+    rms of sigma), unused experts exactly zero, and no router gradient at
+    top-1 with the softmax of the selected logit."""
     kept = np.diff(o["offsets"]) > 0
     exact_router = wl.top_k == 1 and wl.gating == TK
     ratio, rms_errs, rms_sig = {}, {}, {}
@@ -181,10 +195,17 @@ def check_gradients(name, wl, g, o, sigma):
     print(f"[backward] {name}: rms(g - o) / rms(o) " +
           ", ".join(f"{k} {v:.2e}" for k, v in rms_errs.items()) +
           f"; unused experts {int((~kept).sum())}", flush=True)
+    cancel = _dbias_cancellation(o) if "dbias" in ratio else None
     for key in ratio:
         assert ratio[key] <= Z_MAX, f"{key}: error {ratio[key]:.2f} sigma"
-        assert rms_errs[key] <= BWD_RMS_TOL or rms_sig[key] <= 2.0, \
-            f"{key}: rms {rms_errs[key]:.3e} ({rms_sig[key]:.2f} rms sigma)"
+        if key == "dbias" and cancel <= CANCEL_MAX and rms_errs[key] > BWD_RMS_TOL:
+            print(f"[backward] {name}: dbias cancels ({cancel:.3f}): rms error "
+                  f"{rms_sig[key]:.2f} rms sigma", flush=True)
+            assert rms_sig[key] <= 2.0, \
+                f"{key}: rms {rms_errs[key]:.3e} ({rms_sig[key]:.2f} rms sigma)"
+        else:
+            assert rms_errs[key] <= BWD_RMS_TOL, \
+                f"{key}: rms {rms_errs[key]:.3e} ({rms_sig[key]:.2f} rms sigma)"
 
 
 @pytest.mark.parametrize("name", list(CASES))

@@ -13,8 +13,8 @@ import oracle as O
 from mixture_experts_layer_wavefront_amd import binding as B
 from mixture_experts_layer_wavefront_amd import workloads as W
 
-from parity_util import (bf16_err, bounded_err, check_permute, check_routing,
-                         h_rounding_bound, host_f64, oracle_capacity, out_err,
+from parity_util import (bf16_err, check_permute, check_routing, emulated_tol,
+                         host_f64, oracle_capacity, out_err, y_with_rounded_h,
                          out_tol, problem_of, run_stages, to_device)
 
 pytestmark = pytest.mark.gpu
@@ -47,14 +47,15 @@ SMALL = {
 }
 
 
-def _run_and_check(wl, host=None, groups=None, h_bound=False):
+def _run_and_check(wl, host=None, groups=None, h_emul=False):
     """Runs every stage and the whole layer and checks them.  `groups`
     (optional) maps a token-index array to a row population whose output
     scale differs by orders of magnitude from the rest; the output tolerance
-    is applied to each population with its own RMS.  `h_bound` (bf16 layers):
-    an element may also differ by the worst-case effect of rounding H to
-    bf16 (parity_util.h_rounding_bound), added to the RMS bar."""
-    h_bound = h_bound and wl.dtype == W.BF16
+    is applied to each population with its own RMS.  `h_emul` (bf16 layers
+    with a tiny d_ff): each bar is the larger of the plain one and
+    H_MARGIN times the error of the correctly rounded bf16-H emulation
+    (parity_util.y_with_rounded_h) of the same comparison."""
+    h_emul = h_emul and wl.dtype == W.BF16
     host = W.make_host(wl) if host is None else host
     print(f"[parity] {wl.name} T={wl.T} d={wl.d_model} E={wl.E} k={wl.top_k} "
           f"d_ff={wl.d_ff} {wl.dtype} cf={wl.capacity_factor}", flush=True)
@@ -82,22 +83,21 @@ def _run_and_check(wl, host=None, groups=None, h_bound=False):
     Yo = O.grouped_ffn(host_f64(g["X_perm"][:N]), a["offsets"], host["W_gate"],
                        host["W_up"], host["W_down"])
     Yg = g["Y"][:N].cpu().numpy()
-    if h_bound:
-        BY = h_rounding_bound(host_f64(g["X_perm"][:N]), a["offsets"], host["W_gate"],
+    tol_y = out_tol(wl)
+    if h_emul:
+        Yr = y_with_rounded_h(host_f64(g["X_perm"][:N]), a["offsets"], host["W_gate"],
                               host["W_up"], host["W_down"])
-        e_b = bounded_err(Yg, Yo, BY)
-        print(f"[parity] {wl.name}: Y_perm err {out_err(wl, Yg, Yo):.3e} / rms, "
-              f"{e_b:.3f} of the bar with the H-rounding bound", flush=True)
-        assert e_b <= 1.0, e_b
-    else:
-        assert out_err(wl, Yg, Yo) <= out_tol(wl), out_err(wl, Yg, Yo)
+        tol_y = emulated_tol(bf16_err(Yr, Yo))
+        print(f"[parity] {wl.name}: Y_perm err {out_err(wl, Yg, Yo):.4f} / rms, "
+              f"bf16-H emulation {bf16_err(Yr, Yo):.4f}, bar {tol_y:.4f}", flush=True)
+    assert out_err(wl, Yg, Yo) <= tol_y, out_err(wl, Yg, Yo)
     # combine on the GPU's Y, dest rows and weights
     oc = O.combine(Yg, a["dest"], g["w"].cpu().numpy(), wl.T)
     assert out_err(wl, host_f64(g["out"]), oc) <= out_tol(wl)
-    if h_bound:  # the bound of each output row: its copies' bounds, gate-weighted
-        Bo = O.combine(h_rounding_bound(o["X_perm"], o["offsets"], host["W_gate"],
-                                        host["W_up"], host["W_down"]),
-                       o["dest"], np.abs(o["w"]), wl.T)
+    if h_emul:  # the layer output of the emulation, oracle routing throughout
+        out_r = O.combine(y_with_rounded_h(o["X_perm"], o["offsets"], host["W_gate"],
+                                           host["W_up"], host["W_down"]),
+                          o["dest"], o["w"], wl.T)
 
     # the whole layer vs the oracle's own routing, near ties excluded
     stats = torch.empty(2 * wl.E + 2, dtype=torch.int32, device="cuda")
@@ -127,13 +127,12 @@ def _run_and_check(wl, host=None, groups=None, h_bound=False):
         print(f"[parity] {wl.name}: out err {err:.3e} (tol {out_tol(wl)}) over "
               f"{int(m.sum())} rows, near ties {n_near}, dropped "
               f"{a['dropped']}, N {N}", flush=True)
-        if h_bound:
-            e_b = bounded_err(gout[m], o["out"][m], Bo[m])
-            print(f"[parity] {wl.name}: {e_b:.3f} of the bar with the H-rounding "
-                  f"bound", flush=True)
-            assert e_b <= 1.0
-        else:
-            assert err <= out_tol(wl)
+        tol = out_tol(wl)
+        if h_emul:
+            tol = emulated_tol(bf16_err(out_r[m], o["out"][m]))
+            print(f"[parity] {wl.name}: bf16-H emulation "
+                  f"{bf16_err(out_r[m], o['out'][m]):.4f}, bar {tol:.4f}", flush=True)
+        assert err <= tol
     return o, g, a
 
 

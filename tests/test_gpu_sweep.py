@@ -6,12 +6,13 @@ skew), each checked against the oracle stage by stage and as a whole layer
 training path's gradients against the oracle's backward (the
 propagated-rounding tolerance of the backward parity tests).
 
-Output tolerance of bf16 shapes: the 2e-2 RMS bar plus, elementwise, the
-worst-case effect of storing the hidden activation H in bf16 (u |H| |W_down|^T,
-u = 2^-8; parity_util.h_rounding_bound).  With a small d_ff the outputs are
-heavy-tailed (max/rms near 10 at d_ff = 24) and an exact CPU emulation of a
-correctly rounded bf16 H already misses the plain bar by a few percent; the
-named workloads keep the plain bar.
+Output tolerance of bf16 shapes: the 2e-2 RMS bar, or, where a CPU emulation
+that rounds the oracle's exact hidden activation H correctly to bf16 (the
+dtype H is stored in) already misses it, 1.25 times that emulation's error
+(parity_util.emulated_tol).  With a d_ff of 8 to 88 the outputs are
+heavy-tailed and the rounding of H alone reaches 0.021-0.027 of the RMS on
+three shapes here (sweep23, sweep29, sweep_tall5); the named workloads keep
+the plain bar.
 
 The shapes come from one fixed generator (numpy PCG64, seed 20261203), drawn
 once at import: T log-uniform in [1, 700], d_model and d_ff multiples of 8
@@ -86,7 +87,7 @@ SHAPES = _shapes() + _tall_shapes()
 
 @pytest.mark.parametrize("wl", SHAPES, ids=[w.name for w in SHAPES])
 def test_sweep_forward(wl):
-    _run_and_check(wl, h_bound=True)
+    _run_and_check(wl, h_emul=True)
 
 
 BWD_SHAPES = [w for w in SHAPES if w.dtype == W.BF16]
