@@ -1,14 +1,31 @@
 """Parity at the workloads' full sizes, through moe_forward with a single
-workspace exactly as the benchmark launches it.
+workspace exactly as the benchmark launches it, on every token:
 
   * routing (ids bit-exact, near ties excluded; gate weights to 1e-4) and the
     permute (counts, offsets, drops, dest rows, inverse map: bit-exact,
-    against the oracle's assignment of the GPU's ids) on ALL tokens;
+    against the oracle's assignment of the GPU's ids);
   * X_perm is a bit-exact row gather of X (all rows, on the device);
-  * expert FFN rows, the combine and the whole layer on sampled tokens the
-    oracle computes one at a time;
+  * every kept row of Y_perm (the grouped FFN's output) against the oracle's
+    expert FFN of the same row, wherever the GPU and the oracle gave an
+    expert the same rows (all experts unless a near tie flipped a choice);
+  * the combine on the GPU's own Y_perm, dest rows and gate weights (fp32
+    sums: 1e-5) for every token;
+  * the layer output against the oracle's own forward pass (its routing,
+    assignment, per-expert loop and combine; one expert's weights on the
+    host at a time) for every token except near ties;
   * two runs are bit-identical.
+
+Bars: the plain ones (bf16 layers 2e-2 of the RMS, the fp32 layer 1e-4),
+except where a CPU emulation that rounds the oracle's exact H correctly to
+bf16 (the dtype H is stored in) misses the plain bar by itself; there the bar
+is 1.25 times the emulation's error (parity_util.emulated_tol).  At full size
+that happens for one comparison: the layer output of the Qwen3-shaped layer
+with capacity 1.25 and Zipf skew, whose drops leave most tokens one or two
+small-weight copies (a low output RMS) while a few tokens keep a copy with a
+weight near 1 (emulation 0.036 of the RMS).
 """
+
+import time
 
 import numpy as np
 import pytest
@@ -18,24 +35,47 @@ import oracle as O
 from mixture_experts_layer_wavefront_amd import binding as B
 from mixture_experts_layer_wavefront_amd import workloads as W
 
-from parity_util import (bf16_err, check_permute, check_routing, fp32_err,
-                         host_f64, oracle_capacity, out_err, out_tol,
-                         problem_of)
+from parity_util import (bf16_err, check_permute, check_routing, emulated_tol,
+                         fp32_err, host_f64, oracle_capacity, out_err, out_tol,
+                         problem_of, y_with_rounded_h)
 
 pytestmark = pytest.mark.gpu
-
-SAMPLES = {"tiny": 16, "mixtral": 4, "gptoss": 6, "deepseekv3": 3,
-           "qwen3_cap": 12, "qwen3_decode": 32}
 
 
 def _expert_fetch(dev, e):
     return tuple(host_f64(dev[k][e]) for k in ("W_gate", "W_up", "W_down"))
 
 
-@pytest.mark.timeout(600)
+def _oracle_forward_streamed(X, W_r, bias, wl, C, fetch, emulate):
+    """oracle.moe_forward's steps in its order (route, assign, gather, the
+    per-expert loop, combine) with expert e's weights taken from fetch(e)
+    one expert at a time, so the whole weight set never sits on the host.
+    emulate: also the correctly rounded bf16-H emulation of Y_perm and of
+    the output (same weights, same routing)."""
+    idx, w, near, logits = O.route(X, W_r, bias, wl.top_k, wl.gating)
+    a = O.assign(idx, wl.E, C)
+    Xp = O.gather_rows(X, a["row_token"])
+    Y = np.zeros((len(a["row_token"]), wl.d_model))
+    Yr = np.zeros_like(Y) if emulate else None
+    off = a["offsets"]
+    for e in range(wl.E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            Wg, Wu, Wd = fetch(e)
+            Y[lo:hi] = O.expert_ffn(Xp[lo:hi], Wg, Wu, Wd)
+            if emulate:
+                Yr[lo:hi] = y_with_rounded_h(Xp[lo:hi], [0, hi - lo], [Wg], [Wu], [Wd])
+    out = O.combine(Y, a["dest"], w, wl.T)
+    out_r = O.combine(Yr, a["dest"], w, wl.T) if emulate else None
+    return dict(idx=idx, w=w, near_tie=near, logits=logits, Y_perm=Y, out=out,
+                Y_emul=Yr, out_emul=out_r, **a)
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", list(W.WORKLOADS))
 def test_full_size(name):
     wl = W.WORKLOADS[name]
+    t0 = time.time()
     print(f"[full] {name}: generating inputs on the device", flush=True)
     dev = W.make_device(wl, "cuda")
     p = problem_of(wl)
@@ -58,66 +98,77 @@ def test_full_size(name):
     torch.cuda.synchronize()
     assert torch.equal(out, out2), "two runs differ"
     assert torch.equal(out, out_s), "forward != stage-by-stage"
+    del ws, out2, out_s
     print(f"[full] {name}: N={N} kept copies; checking routing", flush=True)
 
     X = host_f64(dev["X"])
     W_r = dev["W_r"].cpu().numpy()
     bias = None if dev["bias"] is None else dev["bias"].cpu().numpy()
-    o_idx, o_w, near, logits = O.route(X, W_r, bias, wl.top_k, wl.gating)
+    bf = wl.dtype == W.BF16
+    o = _oracle_forward_streamed(X, W_r, bias, wl, C, lambda e: _expert_fetch(dev, e), bf)
+    print(f"[full] {name}: oracle forward done ({time.time() - t0:.1f} s)", flush=True)
     g_idx = idx.cpu().numpy()
-    n_near, differ = check_routing(g_idx, w.cpu().numpy(), o_idx, o_w, near,
-                                   logits)
+    g_w = w.cpu().numpy()
+    n_near, differ = check_routing(g_idx, g_w, o["idx"], o["w"], o["near_tie"],
+                                   o["logits"])
     a = check_permute(perm, g_idx, wl.E, C, wl.T, wl.top_k)
     s = stats.cpu().numpy()
     np.testing.assert_array_equal(s[:wl.E], a["counts"])
     np.testing.assert_array_equal(s[wl.E:2 * wl.E + 1], a["offsets"])
     assert s[-1] == a["dropped"]
     print(f"[full] {name}: routing and permute exact (near ties {n_near}, "
-          f"dropped {a['dropped']}, max/mean load "
+          f"flipped {len(differ)}, dropped {a['dropped']}, max/mean load "
           f"{a['counts'].max() / a['counts'].mean():.2f})", flush=True)
 
-    # sampled tokens (non-near-tie), spread over the batch
-    rng = np.random.default_rng(0)
-    cand = np.flatnonzero(~near)
-    ns = min(SAMPLES[name], len(cand))
-    toks = np.unique(np.concatenate([cand[[0, -1]],
-                                     rng.choice(cand, ns, replace=False)]))[:ns]
-    o_a = O.assign(o_idx, wl.E, C)
-    Yg = Y.cpu().numpy()
-    # expert rows on the GPU's own rows: Y_perm[r] vs the oracle FFN of X_perm[r]
-    rows_by_e = {}
-    for t in toks:
-        for j in range(wl.top_k):
-            r = a["dest"][t, j]
-            if r >= 0:
-                rows_by_e.setdefault(int(g_idx[t, j]), []).append(int(r))
-    Xp = perm["X_perm"]
-    y_g, y_o = [], []
-    for e in sorted(rows_by_e)[:6]:
-        Wg, Wu, Wd = _expert_fetch(dev, e)
-        rr = rows_by_e[e]
-        y_o.append(O.expert_ffn(host_f64(Xp[rr]), Wg, Wu, Wd))
-        y_g.append(Yg[rr])
-    if y_o:
-        err = out_err(wl, np.concatenate(y_g), np.concatenate(y_o))
-        print(f"[full] {name}: expert FFN rows err {err:.3e}", flush=True)
-        assert err <= out_tol(wl)
-    # combine, on the GPU's Y / dest rows / weights (fp32 output: tight)
-    oc = O.combine(Yg, a["dest"][toks], w.cpu().numpy()[toks], len(toks))
-    assert fp32_err(host_f64(out)[toks], oc) <= 1e-5
+    # every kept Y_perm row of every expert whose rows agree with the oracle's
+    Yg = Y[:N].cpu().numpy()
+    g_rt = a["row_token"]
+    max_abs, sumsq, rows, experts = 0.0, 0.0, 0, 0
+    max_emul = 0.0   # the bf16-H emulation's max |error| on the same rows
+    small = []   # fp32 layer (tiny): the rows themselves, for the per-element bar
+    for e in range(wl.E):
+        lo, hi = int(a["offsets"][e]), int(a["offsets"][e + 1])
+        olo, ohi = int(o["offsets"][e]), int(o["offsets"][e + 1])
+        if hi == lo or (hi - lo) != (ohi - olo) or \
+                not np.array_equal(g_rt[lo:hi], o["row_token"][olo:ohi]):
+            continue
+        yo, yg = o["Y_perm"][olo:ohi], Yg[lo:hi].astype(np.float64)
+        d = np.abs(yg - yo)
+        max_abs = max(max_abs, float(d.max()))
+        if bf:
+            max_emul = max(max_emul, float(np.abs(o["Y_emul"][olo:ohi] - yo).max()))
+        sumsq += float(np.sum(yo * yo))
+        if wl.dtype == W.F32:
+            small.append((yg, yo))
+        rows += hi - lo
+        experts += 1
+    assert experts == int(np.count_nonzero(np.diff(a["offsets"]))) or differ
+    rms_y = np.sqrt(sumsq / max(rows * wl.d_model, 1))
+    err_y = max_abs / rms_y if rows else 0.0
+    tol_y = emulated_tol(max_emul / rms_y if rows else 0.0) if bf else out_tol(wl)
+    if small:
+        err_y = fp32_err(np.concatenate([g_ for g_, _ in small]),
+                         np.concatenate([o_ for _, o_ in small]))
+    print(f"[full] {name}: Y_perm err {err_y:.3e} (bar {tol_y:.4f}) over {rows} rows "
+          f"of {experts} experts", flush=True)
+    assert err_y <= tol_y
+
+    # combine, on the GPU's Y, dest rows and weights (fp32 sums: tight)
+    oc = O.combine(Yg, a["dest"], g_w, wl.T)
+    g_out = host_f64(out)
+    assert fp32_err(g_out, oc) <= 1e-5
+    del oc
+
     # the whole layer, oracle routing and assignment throughout
-    o_out = O.moe_forward_tokens(toks, X, o_idx, o_w, o_a["dest"],
-                                 lambda e: _expert_fetch(dev, e), wl.d_model)
-    g_out = host_f64(out)[toks]
-    empty = np.all(o_a["dest"][toks] < 0, axis=1)
+    keep = ~o["near_tie"]
+    if differ:   # a flipped near tie may move later capacity decisions
+        keep &= np.all((o["dest"] >= 0) == (a["dest"] >= 0), axis=1)
+    empty = np.all(o["dest"] < 0, axis=1) & keep
     assert np.all(g_out[empty] == 0.0)
-    if differ:
-        same = np.all((o_a["dest"][toks] >= 0) == (a["dest"][toks] >= 0), axis=1)
-    else:
-        same = np.ones(len(toks), dtype=bool)
-    m = ~empty & same
-    if m.any():
-        err = out_err(wl, g_out[m], o_out[m])
-        print(f"[full] {name}: layer output err {err:.3e} over {int(m.sum())} "
-              f"sampled tokens ({int(empty.sum())} fully dropped)", flush=True)
-        assert err <= out_tol(wl)
+    m = keep & ~empty
+    err = out_err(wl, g_out[m], o["out"][m])
+    tol = emulated_tol(bf16_err(o["out_emul"][m], o["out"][m])) if bf else out_tol(wl)
+    print(f"[full] {name}: layer output err {err:.3e} (bar {tol:.4f}) over "
+          f"{int(m.sum())} tokens ({int(empty.sum())} fully dropped) "
+          f"({time.time() - t0:.1f} s)", flush=True)
+    assert err <= tol
