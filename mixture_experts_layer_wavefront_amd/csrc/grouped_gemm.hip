@@ -42,9 +42,10 @@
 //    per-expert M-tile counts.  The grid is a static upper bound; each
 //    workgroup finds its (expert, n-tile, m-tile) from the prefix and exits
 //    if it has none -- no host round trip.  Tiles are ordered expert-major,
-//    then n, then m, and remapped so that the hardware's round-robin of
-//    workgroups over the 8 XCDs gives each XCD a contiguous run of tiles:
-//    the tiles sharing one expert's weights and rows share one L2.
+//    then in bands of four M-tiles that walk the N-tiles together, and
+//    remapped so that the hardware's round-robin of workgroups over the 8
+//    XCDs gives each XCD a contiguous run of tiles: the tiles sharing one
+//    expert's weights and rows share one L2.
 #include "common.h"
 
 #include <type_traits>
@@ -68,6 +69,7 @@ constexpr int kSBK = 64;       // 32-row tiles: K per stage
 constexpr int kSNS = 3;        // 32-row tiles: stages
 constexpr int kSBAUX = kNonTemporal;  // 32-row tiles: weight loads stream (nt)
 constexpr int kWgGroupM = 4;   // weight-gradient tiles: M-tiles per group
+constexpr int kGroupM = 4;     // grouped GEMM tiles: M-tiles per band
 constexpr int kF8SBK = 128;    // 32-row tiles with FP8 weights: K per stage (128-byte rows)
 constexpr int kF8SNS = 2;      // 32-row tiles with FP8 weights: stages
 constexpr int kF8SNW = 2;      // 32-row tiles with FP8 weights: 64 output columns
@@ -303,11 +305,10 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
     const int local = logical - e * per_e;
     // groups of 4 M-tiles walk the N-tiles together: the 32 tiles an XCD
     // runs at once cover about 4 x 8 (M, N) tiles and share their operands
-    constexpr int kGroupM = kWgGroupM;
-    const int grp = local / (kGroupM * n_nt);
-    const int first_m = grp * kGroupM;
-    const int gsize = min(kGroupM, n_mt - first_m);
-    const int in_grp = local - grp * kGroupM * n_nt;
+    const int grp = local / (kWgGroupM * n_nt);
+    const int first_m = grp * kWgGroupM;
+    const int gsize = min(kWgGroupM, n_mt - first_m);
+    const int in_grp = local - grp * kWgGroupM * n_nt;
     const int m_t = first_m + in_grp % gsize, n_t = in_grp / gsize;
     m_start = m_t * BM;
     rows = min(BM, g.M - m_start);
@@ -340,7 +341,14 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
     int local = logical - s_pref[e] * n_nt * NH;
     half = local / (mt_e * n_nt);
     local -= half * mt_e * n_nt;
-    const int n_t = local / mt_e, m_t = local % mt_e;
+    // bands of kGroupM M-tiles walk the N-tiles together, so the tiles an
+    // XCD runs at once share a few activation panels and weight tiles
+    // (an expert of many M-tiles would otherwise re-read all its rows for
+    // every N-tile)
+    const int first_m = local / (kGroupM * n_nt) * kGroupM;
+    const int gsize = min(kGroupM, mt_e - first_m);
+    const int in_band = local - first_m * n_nt;
+    const int m_t = first_m + in_band % gsize, n_t = in_band / gsize;
     const int row_end = offsets[e + 1];
     m_start = offsets[e] + m_t * MSTEP;
     rows = (m_t == mt_e - 1) ? row_end - m_start : MSTEP;
