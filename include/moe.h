@@ -27,7 +27,8 @@
  *   코드를 직접 돌려봤습니다" (thakicloud.com), section "설치 및 통합".
  * - Ownership: the caller owns every buffer, including the workspace.  The
  *   library never allocates, frees or synchronises, and keeps no mutable
- *   global state.  Calls on distinct streams with distinct buffers and
+ *   global state (one exception: moe_forward_noalloc's fixed per-GPU
+ *   scratch array).  Calls on distinct streams with distinct buffers and
  *   workspaces may run concurrently.
  * - Every call only enqueues kernels on `stream` and returns; no host
  *   synchronisation happens inside any call (no per-expert size is read
@@ -60,7 +61,9 @@ typedef enum {
   MOE_ERR_INVALID_ARG = -1, /* NULL required pointer, negative size, k > E */
   MOE_ERR_UNSUPPORTED = -2, /* outside the supported envelope above */
   MOE_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than required */
-  MOE_ERR_HIP = -4          /* a kernel launch failed */
+  MOE_ERR_HIP = -4,         /* a kernel launch failed */
+  MOE_ERR_SCRATCH_LIMIT = -5 /* moe_forward_noalloc: the problem's workspace
+                                exceeds MOE_NOALLOC_SCRATCH_BYTES */
 } moe_status_t;
 
 typedef enum {
@@ -201,6 +204,31 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* X,
                          const void* W_gate, const void* W_up,
                          const void* W_down, void* out, int32_t* stats,
                          void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* moe_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels and results as moe_forward (bit for bit), without
+ * the workspace: the intermediates live in a fixed array of
+ * MOE_NOALLOC_SCRATCH_BYTES (64 MiB) inside the library, one per GPU, held
+ * from the library's first use on that GPU until the process ends.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine);
+ * its first call on a device looks up the array's address there (the
+ * current device must be the one `stream` belongs to).
+ *   Limit: a problem whose moe_workspace_bytes(p) exceeds
+ *   MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_SCRATCH_LIMIT (nothing is
+ *   enqueued); e.g. decode batches and prefill chunks of a few hundred
+ *   tokens at d_model 2048 fit.
+ *   Concurrency: every call on one GPU shares that GPU's array, and each
+ *   call leaves its intermediates there.  Calls that may overlap on one GPU
+ *   (other streams, other threads) race on it: order them on one stream or
+ *   use moe_forward with separate workspaces.  Nothing in the array needs to
+ *   start at zero. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status_t moe_forward_noalloc(const moe_problem_t* p, const void* X,
+                                 const float* W_r, const float* bias,
+                                 const void* W_gate, const void* W_up,
+                                 const void* W_down, void* out, int32_t* stats,
+                                 hipStream_t stream);
 
 /* Router statistics for monitoring (forward values only), computed by the
  * router's selection kernel while it reads the logits and reduced in a fixed

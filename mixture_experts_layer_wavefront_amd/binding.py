@@ -18,6 +18,8 @@ MOE_ERR_INVALID_ARG = -1
 MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
+MOE_ERR_SCRATCH_LIMIT = -5
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 
 MOE_F32 = 0
 MOE_BF16 = 1
@@ -30,7 +32,7 @@ SYMBOLS = ("moe_capacity", "moe_rows_bound", "moe_route_workspace_bytes",
            "moe_permute_workspace_bytes",
            "moe_grouped_ffn_workspace_bytes", "moe_workspace_bytes",
            "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
-           "moe_forward", "moe_route_stats_workspace_bytes", "moe_route_stats",
+           "moe_forward", "moe_forward_noalloc", "moe_route_stats_workspace_bytes", "moe_route_stats",
            "moe_forward_stats_workspace_bytes", "moe_forward_stats",
            "moe_forward_shared_workspace_bytes", "moe_forward_shared",
            "moe_grouped_ffn_scaled", "moe_forward_scaled",
@@ -84,6 +86,7 @@ def load(path: str = LIB_PATH):
         "moe_combine": (ctypes.c_int, [P, vp, vp, vp, vp, st]),
         "moe_forward": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        sz, st]),
+        "moe_forward_noalloc": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, st]),
         "moe_route_stats_workspace_bytes": (sz, [P]),
         "moe_route_stats": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, sz, st]),
         "moe_forward_stats_workspace_bytes": (sz, [P]),
@@ -299,6 +302,24 @@ def moe_forward(p, X, W_r, bias, W_gate, W_up, W_down, out=None, stats=None,
         _ptr(out, _out_dtype(p), "out"), _ptr(stats, torch.int32, "stats"),
         _ptr(ws),
         ws.numel(), _stream(stream)), "moe_forward")
+    return out
+
+
+def moe_forward_noalloc(p, X, W_r, bias, W_gate, W_up, W_down, out=None, stats=None,
+                        stream=None):
+    """moe_forward with the library's own fixed scratch instead of a
+    workspace (the call allocates no device memory; `out` and `stats` are
+    allocated here only when not given).  Returns out."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((p.T, p.d_model), dtype=_out_dtype(p), device=X.device)
+    wt = _act_dtype(p)
+    _check(load().moe_forward_noalloc(
+        ctypes.byref(p), _ptr(X, wt, "X"), _ptr(W_r, torch.float32, "W_r"),
+        _ptr(bias, torch.float32, "bias"), _ptr(W_gate, wt, "W_gate"),
+        _ptr(W_up, wt, "W_up"), _ptr(W_down, wt, "W_down"),
+        _ptr(out, _out_dtype(p), "out"), _ptr(stats, torch.int32, "stats"),
+        _stream(stream)), "moe_forward_noalloc")
     return out
 
 

@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <climits>
 #include <cmath>
+#include <mutex>
 
 #include "launch.h"
 
@@ -163,6 +164,52 @@ hipError_t enqueue_routed(const moe_problem_t* p, const void* X, const float* W_
                                  p->d_model, p->E, p->d_ff, mean_rows_per_expert(p), y_perm,
                                  ws + L.ffn_scratch, mt_prefix != nullptr, stream, w_scales,
                                  /*defer_half_sum=*/true);
+}
+
+// The whole layer with its intermediates carved from `ws` (L.total bytes).
+moe_status_t enqueue_forward(const moe_problem_t* p, const void* X, const float* W_r,
+                             const float* bias, const void* W_gate, const void* W_up,
+                             const void* W_down, void* out, int32_t* stats, char* ws,
+                             const ForwardLayout& L, hipStream_t stream) {
+  RoutedOut r{};
+  hipError_t e = enqueue_routed(p, X, W_r, bias, W_gate, W_up, W_down, stats, nullptr, ws, L,
+                                stream, &r);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_combine(r.y_perm, r.dest_row, r.topk_w, p->T, p->d_model, p->top_k,
+                          nullptr, out_bf16(p), out, stream, r.y_half);
+  return hip_status(e);
+}
+
+// ---- the workspace of moe_forward_noalloc ----------------------------------
+// A fixed device array in this library's code object: each GPU that loads
+// the library holds its own copy until the process ends.  Host code never
+// passes `scratch` itself to a kernel (on the host the name only stands in
+// for the symbol); it looks up the array's device address on the current
+// device once and passes that address.
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_addr[kMaxDevices];  // device address of `scratch`, per device
+
+// The device address of `scratch` on the current device (looked up on the
+// first call on that device, then kept).
+hipError_t scratch_address(char** addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (a == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = static_cast<char*>(a);
+  }
+  *addr = g_scratch_addr[dev];
+  return hipSuccess;
 }
 
 // ---- training ---------------------------------------------------------------
@@ -355,14 +402,23 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* X, const float* W_r
   if (!X || !W_r || !W_gate || !W_up || !W_down || !out) return MOE_ERR_INVALID_ARG;
   const ForwardLayout L = forward_layout(p);
   if (!workspace || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-  char* ws = static_cast<char*>(workspace);
-  RoutedOut r{};
-  hipError_t e = enqueue_routed(p, X, W_r, bias, W_gate, W_up, W_down, stats, nullptr, ws, L,
-                                stream, &r);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  e = moe::launch_combine(r.y_perm, r.dest_row, r.topk_w, p->T, p->d_model, p->top_k,
-                          nullptr, out_bf16(p), out, stream, r.y_half);
-  return hip_status(e);
+  return enqueue_forward(p, X, W_r, bias, W_gate, W_up, W_down, out, stats,
+                         static_cast<char*>(workspace), L, stream);
+}
+
+moe_status_t moe_forward_noalloc(const moe_problem_t* p, const void* X, const float* W_r,
+                                 const float* bias, const void* W_gate, const void* W_up,
+                                 const void* W_down, void* out, int32_t* stats,
+                                 hipStream_t stream) {
+  moe_status_t st = validate(p);
+  if (st != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;
+  if (!X || !W_r || !W_gate || !W_up || !W_down || !out) return MOE_ERR_INVALID_ARG;
+  const ForwardLayout L = forward_layout(p);
+  if (L.total > kScratchBytes) return MOE_ERR_SCRATCH_LIMIT;
+  char* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return MOE_ERR_HIP;
+  return enqueue_forward(p, X, W_r, bias, W_gate, W_up, W_down, out, stats, ws, L, stream);
 }
 
 size_t moe_forward_stats_workspace_bytes(const moe_problem_t* p) {
@@ -603,6 +659,9 @@ const char* moe_status_string(moe_status_t s) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: outside the supported envelope";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a kernel launch failed";
+    case MOE_ERR_SCRATCH_LIMIT:
+      return "MOE_ERR_SCRATCH_LIMIT: the problem needs more workspace than the library's "
+             "static scratch holds (MOE_NOALLOC_SCRATCH_BYTES, 64 MiB)";
   }
   return "unknown moe_status_t";
 }

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     for s in (B.MOE_OK, B.MOE_ERR_INVALID_ARG, B.MOE_ERR_UNSUPPORTED,
-              B.MOE_ERR_WORKSPACE, B.MOE_ERR_HIP):
+              B.MOE_ERR_WORKSPACE, B.MOE_ERR_HIP, B.MOE_ERR_SCRATCH_LIMIT):
         assert B.status_string(s).startswith("MOE_")
 
 

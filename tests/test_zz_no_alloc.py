@@ -1,0 +1,74 @@
+"""moe_forward_noalloc (the workspace-free entry point, for callers that
+cannot allocate device memory) against moe_forward on the same inputs: two
+calls in a row, the second on a smaller problem, so that the second runs on
+the scratch the first left behind.  The two entry points run the same
+kernels, so the outputs and routing statistics must be equal bit for bit;
+both are also checked against the CPU oracle at the layer's bar (2e-2 of the
+RMS, or 1.25 times the error of the correctly rounded bf16-H emulation where
+that alone misses it, as on capacity-limited skewed layers).  A problem whose
+workspace exceeds the scratch is rejected on the host."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mixture_experts_layer_wavefront_amd import binding as B
+from mixture_experts_layer_wavefront_amd import workloads as W
+
+from parity_util import (bf16_err, emulated_tol, host_f64, oracle_capacity, out_err,
+                         problem_of, to_device, y_with_rounded_h)
+
+pytestmark = pytest.mark.gpu
+
+TK = W.TOPK_THEN_SOFTMAX
+# a prefill chunk of a Qwen3-30B-A3B-like layer (capacity, skew), then a
+# smaller decode-sized batch of another shape
+FIRST = W.Workload("noalloc_chunk", 256, 2048, 128, 8, 768, W.BF16, TK, 1.25, 1.2, 71)
+SECOND = W.Workload("noalloc_decode", 24, 1024, 64, 4, 512, W.BF16, TK, 0.0, 0.0, 72)
+
+
+def _check(wl):
+    host = W.make_host(wl)
+    dev = to_device(host, wl)
+    p = problem_of(wl)
+    assert B.workspace_bytes(p) <= B.NOALLOC_SCRATCH_BYTES
+    args = (dev["X"], dev["W_r"], dev["bias"], dev["W_gate"], dev["W_up"], dev["W_down"])
+    s_ref = torch.empty(2 * wl.E + 2, dtype=torch.int32, device="cuda")
+    s_na = torch.full_like(s_ref, -7)
+    ref = B.moe_forward(p, *args, stats=s_ref)
+    out = torch.full_like(ref, float("nan"))
+    B.moe_forward_noalloc(p, *args, out=out, stats=s_na)
+    torch.cuda.synchronize()
+    print(f"[noalloc] {wl.name}: T={wl.T} workspace {B.workspace_bytes(p)} bytes", flush=True)
+    assert torch.equal(out, ref), "moe_forward_noalloc differs from moe_forward"
+    assert torch.equal(s_na, s_ref)
+    cf = float(np.float32(wl.capacity_factor))
+    o = O.moe_forward(host["X"], host["W_r"], host["bias"], host["W_gate"], host["W_up"],
+                      host["W_down"], wl.top_k, cf if cf > 0 else None, wl.gating)
+    assert o["C"] == oracle_capacity(wl)
+    g = host_f64(out)
+    keep = ~o["near_tie"] & ~np.all(o["dest"] < 0, axis=1)
+    err = out_err(wl, g[keep], o["out"][keep])
+    out_r = O.combine(y_with_rounded_h(o["X_perm"], o["offsets"], host["W_gate"],
+                                       host["W_up"], host["W_down"]), o["dest"], o["w"], wl.T)
+    tol = emulated_tol(bf16_err(out_r[keep], o["out"][keep]))
+    print(f"[noalloc] {wl.name}: err {err:.3e} vs the oracle (bar {tol:.4f})", flush=True)
+    assert err <= tol
+
+
+def test_noalloc_matches_moe_forward_on_two_calls():
+    _check(FIRST)
+    _check(SECOND)
+
+
+def test_noalloc_rejects_a_problem_beyond_the_scratch():
+    wl = W.WORKLOADS["mixtral"]
+    p = problem_of(wl)
+    assert B.workspace_bytes(p) > B.NOALLOC_SCRATCH_BYTES
+    x = torch.empty(8, device="cuda")   # never read: the call fails on the host
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_forward_noalloc(p, x.to(torch.bfloat16), x, None, x.to(torch.bfloat16),
+                              x.to(torch.bfloat16), x.to(torch.bfloat16),
+                              out=torch.empty(1, device="cuda"))
+    assert ei.value.status == B.MOE_ERR_SCRATCH_LIMIT
