@@ -23,9 +23,12 @@ constexpr int kTokPerBlock = 4;
 constexpr int kColsPerWave = 8 * kWave;  // 8 columns per lane
 
 // One wavefront per (token, slice of kColsPerWave columns): blockIdx.x picks
-// kTokPerBlock tokens, blockIdx.y the column slice.  The k source rows are
-// read eight slots at a time (all loads issued before the FMAs, which run in
-// slot order).
+// kTokPerBlock tokens, blockIdx.y the column slice.  A slice is 128 chunks
+// of four fp32 columns; lane l owns chunks l and l + 64, so every load and
+// store instruction of the wave covers 1 KB of contiguous memory.  The k
+// source rows are read eight slots at a time (all loads issued before the
+// FMAs, which run in slot order); each source row is read once, past the
+// caches (non-temporal).
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kTokPerBlock * kWave) void combine_kernel(
     const float* __restrict__ Y, const float* __restrict__ Y2,
@@ -45,20 +48,19 @@ __global__ __launch_bounds__(kTokPerBlock * kWave) void combine_kernel(
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  const int c = blockIdx.y * kWave + lane;  // 8-column chunk
-  if (c >= d / 8) return;
-  float acc[8];
+  const int nq = d / 4;                                // chunks of 4 columns per row
+  const int q0 = blockIdx.y * (2 * kWave) + lane;      // this lane's chunks: q0, q1
+  const int q1 = q0 + kWave;
+  if (q0 >= nq) return;
+  const bool has1 = q1 < nq;
+  f32x4 acc0, acc1;
   if (add_rows != nullptr) {
-    const f32x4* a0 = reinterpret_cast<const f32x4*>(add_rows + (int64_t)t * d) + 2 * c;
-    const f32x4 u = a0[0], v = a0[1];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[i] = u[i];
-      acc[4 + i] = v[i];
-    }
+    const f32x4* a0 = reinterpret_cast<const f32x4*>(add_rows + (int64_t)t * d);
+    acc0 = a0[q0];
+    acc1 = has1 ? a0[q1] : f32x4{0.f, 0.f, 0.f, 0.f};
   } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc1 = acc0;
   }
   for (int j0 = 0; j0 < k; j0 += 8) {
     f32x4 a[8], b[8];
@@ -67,17 +69,18 @@ __global__ __launch_bounds__(kTokPerBlock * kWave) void combine_kernel(
     for (int u = 0; u < 8; ++u) {
       r[u] = (j0 + u < k) ? s_dest[wv][j0 + u] : -1;
       if (r[u] >= 0) {
-        const f32x4* src = reinterpret_cast<const f32x4*>(Y + (int64_t)r[u] * d) + 2 * c;
-        a[u] = src[0];
-        b[u] = src[1];
+        const f32x4* src = reinterpret_cast<const f32x4*>(Y + (int64_t)r[u] * d);
+        a[u] = __builtin_nontemporal_load(src + q0);
+        b[u] = has1 ? __builtin_nontemporal_load(src + q1) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
     if (Y2 != nullptr) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (r[u] < 0) continue;
-        const f32x4* src = reinterpret_cast<const f32x4*>(Y2 + (int64_t)r[u] * d) + 2 * c;
-        const f32x4 a2 = src[0], b2 = src[1];
+        const f32x4* src = reinterpret_cast<const f32x4*>(Y2 + (int64_t)r[u] * d);
+        const f32x4 a2 = __builtin_nontemporal_load(src + q0);
+        const f32x4 b2 = has1 ? __builtin_nontemporal_load(src + q1) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           a[u][i] = a[u][i] + a2[i];
@@ -91,22 +94,23 @@ __global__ __launch_bounds__(kTokPerBlock * kWave) void combine_kernel(
       const float w = s_w[wv][j0 + u];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[i] = fmaf(w, a[u][i], acc[i]);
-        acc[4 + i] = fmaf(w, b[u][i], acc[4 + i]);
+        acc0[i] = fmaf(w, a[u][i], acc0[i]);
+        acc1[i] = fmaf(w, b[u][i], acc1[i]);
       }
     }
   }
   if constexpr (OUT_BF16) {
-    i32x4 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = (int)((uint32_t)f32_to_bf16_bits(acc[2 * i]) |
-                   ((uint32_t)f32_to_bf16_bits(acc[2 * i + 1]) << 16));
-    reinterpret_cast<i32x4*>(static_cast<uint16_t*>(out) + (int64_t)t * d)[c] = o;
+    uint2* o = reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (int64_t)t * d);
+    auto pack = [](f32x4 v) {
+      return uint2{(uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16),
+                   (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16)};
+    };
+    o[q0] = pack(acc0);
+    if (has1) o[q1] = pack(acc1);
   } else {
-    f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(out) + (int64_t)t * d) + 2 * c;
-    dst[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
-    dst[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(out) + (int64_t)t * d);
+    o[q0] = acc0;
+    if (has1) o[q1] = acc1;
   }
 }
 
