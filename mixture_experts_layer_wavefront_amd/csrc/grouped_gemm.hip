@@ -74,6 +74,7 @@ constexpr int kF8SBK = 128;    // 32-row tiles with FP8 weights: K per stage (12
 constexpr int kF8SNS = 2;      // 32-row tiles with FP8 weights: stages
 constexpr int kF8SNW = 2;      // 32-row tiles with FP8 weights: 64 output columns
 constexpr int kBntRows = 256;  // 256-row tiles: stream the weights up to this many rows per expert
+constexpr int kStreamRows = 160;  // few rows per expert: 160-row tiles, 4 waves, 3 stages
 
 // Chunk swizzle of LDS row R (16-byte chunks).  256-byte rows (16 chunks),
 // 128-byte rows (8 chunks) and 64-byte rows (4 chunks): 16, 8 or 16
@@ -273,8 +274,8 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   // also takes a remainder of up to 64 rows (the schedule merges it instead
   // of giving it a tile of its own that would stream the whole weight tile
   // for a few rows).
-  constexpr bool TALL = TM == 5;
-  static_assert(!TALL || (MW == 2 && NS == 2 && !AT), "tall tiles: 2 wave rows, 2 stages, NT A");
+  constexpr bool TALL = TM == 5 && MW == 2;
+  static_assert(!TALL || (NS == 2 && !AT), "tall tiles: 2 stages, NT A");
   constexpr int MSTEP = TALL ? 256 : BM;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   int32_t* s_pref = reinterpret_cast<int32_t*>(smem + NS * STAGE);
@@ -595,7 +596,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
     }
   };
   if (tm_active == TM) kloop(std::integral_constant<int, TM>{});
-  else if (TALL && tm_active == 4) kloop(std::integral_constant<int, 4>{});
+  else if (TM == 5 && tm_active == 4) kloop(std::integral_constant<int, 4>{});
   else kloop(std::integral_constant<int, -1>{});
 
   // FP8 weights: the expert's scales multiply the accumulators
@@ -816,7 +817,7 @@ hipError_t launch_gemm_args(const GemmArgs& a, int64_t R, hipStream_t stream) {
     tiles = (int64_t)a.E * ((a.M + Cfg::BM - 1) / Cfg::BM) * n_nt;
   } else {
     // upper bound on M-tiles: every expert may add one partial tile
-    constexpr int MSTEP = TM == 5 ? 256 : Cfg::BM;  // tall tiles step by 256 rows
+    constexpr int MSTEP = (TM == 5 && MW == 2) ? 256 : Cfg::BM;  // tall tiles step by 256 rows
     const int64_t mt_max = (R + MSTEP - 1) / MSTEP + std::min<int64_t>(a.E, R);
     tiles = mt_max * n_nt * ((MODE == 4 || MODE == 5) ? 2 : 1);
   }
@@ -916,7 +917,13 @@ int ffn_tile_code(bool bf16, int rows_per_expert, bool fp8) {
 int ffn_tile_rows(bool bf16, int rows_per_expert, bool fp8) {
   if (!bf16) return 0;
   if (rows_per_expert <= 64) return 32;
-  return (fp8 && rows_per_expert <= 512) ? 128 : 256;
+  if (fp8) return rows_per_expert <= 512 ? 128 : 256;
+  return rows_per_expert <= kStreamRows ? kStreamRows : 256;
+}
+
+int ffn_train_tile_code(int rows_per_expert) {
+  if (rows_per_expert <= 64) return 32;
+  return rows_per_expert > kBntRows ? kTallTileCode : 256;
 }
 
 float* ffn_half_sums(void* scratch, int64_t R, int E, int d, int d_ff, bool bf16,
@@ -997,6 +1004,16 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
     if (err != hipSuccess) return err;
     return launch_down<2, kNW, 5, kDTN / kNW, kBK, 2, 0, true>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, w_scales, defer);
   }
+  if (bm == kStreamRows) {
+    // up to 160 rows per expert on average (one M-tile for most experts):
+    // the weights stream once, so the bytes in flight per CU set the rate.
+    // 160-row tiles of 4 waves (160 x 64 wave tiles) leave room for three
+    // 52 KB stages (two in flight while one is multiplied); 128-byte
+    // weight-row pieces per stage, read past the caches
+    err = launch_gemm<1, 4, 5, 1, true, kBK, 3, kNonTemporal>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
+    if (err != hipSuccess) return err;
+    return launch_down<1, 4, 5, 2, kBK, 3, kNonTemporal, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr, defer);
+  }
   if (rows_per_expert <= kBntRows) {
     // about one M-tile per expert: every weight tile is read once
     err = launch_gemm<2, kNW, 4, 4 / kNW, true, kBK, kNS, kNonTemporal>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
@@ -1020,11 +1037,11 @@ hipError_t launch_grouped_ffn_train(const void* X_perm, const int32_t* offsets,
                                     int64_t R, int d, int E, int d_ff, int rows_per_expert,
                                     int32_t* mt_prefix, bool prefix_ready, void* H, void* G,
                                     void* U, float* Y_perm, hipStream_t stream) {
-  const int bm = ffn_tile_rows(true, rows_per_expert, false);
+  const int bm = rows_per_expert <= 64 ? 32 : 256;
   if (R == 0) return hipSuccess;
   hipError_t err;
   if (!prefix_ready) {
-    ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, ffn_tile_code(true, rows_per_expert),
+    ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, ffn_train_tile_code(rows_per_expert),
                                                mt_prefix);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
@@ -1053,7 +1070,7 @@ hipError_t launch_grouped_ffn_train(const void* X_perm, const int32_t* offsets,
     if (err != hipSuccess) return err;
     return launch_down<2, kNW, 4, kDTN / kNW, kBK, kNS, kNonTemporal, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr);
   }
-  // tall tiles, with the schedule of ffn_tile_code as in launch_grouped_ffn
+  // tall tiles, with the schedule of ffn_train_tile_code
   err = launch_gemm_args<2, kNW, 5, 4 / kNW, true, kBK, 2, 0, false, 1>(a, R, stream);
   if (err != hipSuccess) return err;
   return launch_down<2, kNW, 5, kDTN / kNW, kBK, 2, 0, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr);
@@ -1063,10 +1080,10 @@ hipError_t launch_ffn_dgrad(const void* dY_perm, const int32_t* offsets, const v
                             const void* W_up, const void* W_down, const void* G, const void* U,
                             int64_t R, int d, int E, int d_ff, int rows_per_expert,
                             int32_t* mt_prefix, void* dGU, float* dX_perm, hipStream_t stream) {
-  const int bm = ffn_tile_rows(true, rows_per_expert, false);
+  const int bm = rows_per_expert <= 64 ? 32 : 256;
   if (R == 0) return hipSuccess;
-  // dH and dX run on tall tiles where the forward does
-  const int code = ffn_tile_code(true, rows_per_expert, false);
+  // dH and dX run on tall tiles where the training forward does
+  const int code = ffn_train_tile_code(rows_per_expert);
   const bool tall = code != bm;
   ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, code, mt_prefix);
   hipError_t err = hipGetLastError();

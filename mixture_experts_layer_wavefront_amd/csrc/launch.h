@@ -45,6 +45,9 @@ int ffn_tile_rows(bool bf16, int rows_per_expert, bool fp8 = false);
 // 256-row tiles that take remainders of up to 64 rows (256-row tiles with
 // more than 256 rows per expert, bf16 or FP8 weights).
 int ffn_tile_code(bool bf16, int rows_per_expert, bool fp8 = false);
+// The M-tile code of the training forward's and the backward's GEMMs (their
+// own tile shapes: 32-row, 256-row or tall tiles).
+int ffn_train_tile_code(int rows_per_expert);
 bool ffn_split_down(bool bf16, int E, int rows_per_expert, int d, int d_ff);
 size_t ffn_scratch_bytes(int64_t R, int E, int d, int d_ff, bool bf16, int rows_per_expert);
 hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,

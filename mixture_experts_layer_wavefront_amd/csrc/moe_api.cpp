@@ -574,7 +574,7 @@ moe_status_t moe_forward_train(const moe_problem_t* p, const void* X, const floa
   hipError_t e = moe::launch_route(X, true, W_r, bias, p->T, p->d_model, p->E, p->top_k,
                                    (int)p->gating, topk_idx, topk_w, ws + L.route_scratch,
                                    nullptr, stream);
-  const int bm = moe::ffn_tile_code(true, rows, false);
+  const int bm = moe::ffn_train_tile_code(rows);
   int32_t* mt_prefix = reinterpret_cast<int32_t*>(ws + L.ffn_scratch);
   if (e == hipSuccess)
     e = moe::launch_permute(X, true, topk_idx, p->T, p->d_model, p->E, p->top_k,
