@@ -18,6 +18,7 @@
 // descending-logit order.
 #include "common.h"
 #include "launch.h"
+#include "topk.h"
 
 #include <algorithm>
 
@@ -50,67 +51,6 @@ struct XLoad<uint16_t> {
     }
   }
 };
-
-// Top-k of one token's logits held across a wavefront (lane l holds experts
-// l, l+64, ...; -inf beyond E), then its gate weights; lanes j < k store slot
-// j.  k rounds of a 64-lane butterfly argmax pick the experts in descending
-// logit order, ties to the lower id.
-template <int VPL>
-__device__ __forceinline__ void topk_softmax_store(float (&v)[VPL], int E, int k, int gating,
-                                                   int lane, int32_t* __restrict__ idx_out,
-                                                   float* __restrict__ w_out,
-                                                   int* sel_id = nullptr, float* sel_w = nullptr) {
-  // softmax over all experts needs the untouched logits: its denominator first
-  float M = v[0];
-#pragma unroll
-  for (int i = 1; i < VPL; ++i) M = fmaxf(M, v[i]);
-  M = wave_max(M);
-  float Z = 0.f;
-  if (gating != 0) {
-    float z = 0.f;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (lane + kWave * i < E) z += expf(v[i] - M);
-    Z = wave_sum(z);
-  }
-  float my_s = -INFINITY;
-  int my_id = 0;
-  for (int j = 0; j < k; ++j) {
-    float bv = v[0];
-    int be = lane;
-#pragma unroll
-    for (int i = 1; i < VPL; ++i)
-      if (v[i] > bv) { bv = v[i]; be = lane + kWave * i; }
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oe = __shfl_xor(be, o, kWave);
-      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-    }
-    if (lane == j) { my_s = bv; my_id = be; }
-#pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (be == lane + kWave * i) v[i] = -INFINITY;
-  }
-  float w;
-  if (gating == 0) {
-    // softmax over the selected logits, shifted by the largest of them
-    const float ex = (lane < k) ? expf(my_s - M) : 0.f;
-    w = ex / wave_sum(ex);
-  } else {
-    // softmax over all experts, then renormalised over the selected ones
-    const float pj = (lane < k) ? expf(my_s - M) / Z : 0.f;
-    w = pj / wave_sum(pj);
-  }
-  if (lane < k) {
-    idx_out[lane] = my_id;
-    w_out[lane] = w;
-  }
-  if (sel_id != nullptr) {
-    *sel_id = my_id;
-    *sel_w = w;
-  }
-}
 
 // fp32 layers: one fused kernel.  TX threads across experts (expert
 // e = tx + TX*j, j < RE), TY = 256/TX
