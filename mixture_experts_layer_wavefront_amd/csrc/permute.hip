@@ -119,11 +119,18 @@ __global__ __launch_bounds__(256) void scan_kernel(
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    for (int b = 0; b < nblk; ++b) {
-      int32_t* p = block_counts + (int64_t)b * E + e;
-      const int c = *p;
-      *p = run;  // becomes the block's base rank within expert e
-      run += c;
+    // sixteen blocks' counts are loaded before any is overwritten, so the
+    // loads overlap instead of waiting for each other
+    for (int b0 = 0; b0 < nblk; b0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        c[u] = (b0 + u < nblk) ? block_counts[(int64_t)(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (b0 + u < nblk) block_counts[(int64_t)(b0 + u) * E + e] = run;  // the block's base rank
+        run += c[u];
+      }
     }
   }
   const int kept = (e < E) ? min(run, C) : 0;
