@@ -44,6 +44,10 @@ SMALL = {
     # d_ff >= 2048 with few tiles: the down projection runs as two K halves
     # (d_ff / 2 = 1040 leaves a K tail in each half; N tail 520 = 2 x 256 + 8)
     "split_down": WL("split_down", 600, 520, 4, 2, 2080, W.BF16, TK, 0.0, 0.8, 18),
+    # 16 experts averaging 375 rows with strong Zipf skew (2999, 2495, 418,
+    # 68, 14 and 6 rows; ten experts without rows): tall tiles next to
+    # nearly empty ones, with a down projection in two K halves
+    "skew16": WL("skew16", 3000, 264, 16, 2, 2112, W.BF16, TK, 0.0, 1.2, 21),
 }
 
 
