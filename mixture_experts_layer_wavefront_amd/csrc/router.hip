@@ -27,6 +27,11 @@ namespace {
 
 constexpr int kRouterThreads = 256;
 constexpr int kRouterDK = 32;
+// Selection with a group of lanes per token: for k up to kGroupSelKMax and at
+// least kGroupSelMinT tokens (decode batches keep one wavefront per token,
+// which spreads their few tokens over more SIMDs).
+constexpr int kGroupSelKMax = 8;
+constexpr int kGroupSelMinT = 128;
 
 template <typename XT>
 struct XLoad;
@@ -372,6 +377,50 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   topk_softmax_store<VPL>(v, E, k, gating, lane, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
 }
 
+// The same with a group of G lanes per token (64 / G tokens per wavefront):
+// lane g of a group holds experts g + G i, i < NV.  The partials are added in
+// the same order (s = 0, 1, ...; SB of them loaded at a time), so the logits,
+// the selection and the gate weights equal router_select_kernel's bit for bit.
+// Groups past T compute on token T - 1 and store nothing.
+template <int G, int NV>
+__global__ __launch_bounds__(256) void router_select_group_kernel(
+    const float* __restrict__ partial, const float* __restrict__ bias, int T, int E,
+    int EP, int S, int k, int gating, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w) {
+  constexpr int TPW = kWave / G;
+  constexpr int SB = NV >= 16 ? 4 : (NV >= 8 ? 8 : 16);
+  const int lane = threadIdx.x % kWave;
+  const int g = lane % G;
+  const int t = (blockIdx.x * (256 / kWave) + threadIdx.x / kWave) * TPW + lane / G;
+  const bool valid = t < T;
+  const int tl = valid ? t : T - 1;
+  float acc[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) acc[i] = 0.f;
+  for (int s0 = 0; s0 < S; s0 += SB) {
+    float pv[SB][NV];
+#pragma unroll
+    for (int u = 0; u < SB; ++u)
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        pv[u][i] = (s0 + u < S && g + G * i < E)
+                       ? partial[((int64_t)(s0 + u) * T + tl) * EP + g + G * i] : 0.f;
+#pragma unroll
+    for (int u = 0; u < SB; ++u)
+      if (s0 + u < S)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) acc[i] += pv[u][i];
+  }
+  float v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = g + G * i;
+    v[i] = e < E ? acc[i] + (bias != nullptr ? bias[e] : 0.f) : -INFINITY;
+  }
+  group_topk_softmax_store<G, NV, kGroupSelKMax>(v, E, k, gating, g, valid,
+                                                 topk_idx + (int64_t)tl * k, topk_w + (int64_t)tl * k);
+}
+
 // Few tokens (bf16): K-split FMA partial logits (no W_r split) + select.
 constexpr int kSmallT = 64;
 constexpr int kSmallKS = 64;  // K per workgroup
@@ -617,6 +666,23 @@ hipError_t launch_select(const float* partial, const float* bias, int T, int E, 
                          int S, int k, int gating, int32_t* topk_idx, float* topk_w,
                          float* stat_part, float* router_stats, hipStream_t stream) {
   if (router_stats == nullptr) {
+    if (k <= kGroupSelKMax && T >= kGroupSelMinT && E <= 256) {
+      // 4 wavefronts per workgroup, 64 / G tokens per wavefront
+      const unsigned g8 = (unsigned)((T + 31) / 32), g16 = (unsigned)((T + 15) / 16);
+      if (E <= 8)
+        router_select_group_kernel<8, 1><<<g8, 256, 0, stream>>>(partial, bias, T, E, EP, S, k, gating, topk_idx, topk_w);
+      else if (E <= 16)
+        router_select_group_kernel<8, 2><<<g8, 256, 0, stream>>>(partial, bias, T, E, EP, S, k, gating, topk_idx, topk_w);
+      else if (E <= 32)
+        router_select_group_kernel<8, 4><<<g8, 256, 0, stream>>>(partial, bias, T, E, EP, S, k, gating, topk_idx, topk_w);
+      else if (E <= 64)
+        router_select_group_kernel<8, 8><<<g8, 256, 0, stream>>>(partial, bias, T, E, EP, S, k, gating, topk_idx, topk_w);
+      else if (E <= 128)
+        router_select_group_kernel<16, 8><<<g16, 256, 0, stream>>>(partial, bias, T, E, EP, S, k, gating, topk_idx, topk_w);
+      else
+        router_select_group_kernel<16, 16><<<g16, 256, 0, stream>>>(partial, bias, T, E, EP, S, k, gating, topk_idx, topk_w);
+      return hipGetLastError();
+    }
     const unsigned gs = (unsigned)((T + 3) / 4);
     if (E <= 64)
       router_select_kernel<1><<<gs, 256, 0, stream>>>(partial, bias, T, E, EP, S, k, gating, topk_idx, topk_w);
