@@ -616,7 +616,44 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   //   row = wm*TM*32 + mi*32 + 8*(r/4) + 4*(lane/32) + r%4,  col = lane%32 (+ sub-tile base)
   const int col_l = lane & 31;
   const int rlane = 4 * (lane >> 5);
-  if constexpr (GATEUP) {
+  if constexpr (GATEUP && MODE == 0) {
+    // H goes out through the LDS, one row sub-tile at a time: the wave writes
+    // its 32 x TN*32 block of bf16 row-major (rows padded by 32 bytes, so the
+    // two row groups of one LDS write fall on different banks), then stores
+    // it with 16 bytes per lane, 16 / TN rows of TN*64 contiguous bytes per
+    // instruction -- an eighth of the instructions of 2-byte stores.
+    constexpr int RS = TN * 64 + 32;  // staged row stride (bytes)
+    constexpr int CPRW = TN * 4;      // 16-byte chunks per staged row
+    constexpr int RPI = kWave / CPRW;  // rows per store instruction
+    static_assert(NWAVES * 32 * RS <= NS * STAGE, "the staging fits the stages");
+    uint16_t* H = static_cast<uint16_t*>(Cout);
+    __syncthreads();  // every wave is done with the last stage
+    char* wreg = smem + wave * (32 * RS);
+    const int rsub = lane / CPRW, ch = lane % CPRW;
+    const int colc = wn * TN * 32 + ch * 8;  // tile-local first column of the chunk
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi) {
+      if (mi >= tm_active) continue;  // uniform: no rows of the tile here
+#pragma unroll
+      for (int nj = 0; nj < TN; ++nj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float gv = acc[mi][nj][r], u = acc[mi][nj + TN][r];
+          const float h = gv / (1.f + __expf(-gv)) * u;
+          const int rl = rlane + 8 * (r >> 2) + (r & 3);
+          *reinterpret_cast<uint16_t*>(wreg + rl * RS + (nj * 32 + col_l) * 2) =
+              f32_to_bf16_bits(h);
+        }
+#pragma unroll
+      for (int r0 = 0; r0 < 32; r0 += RPI) {
+        const int rl = r0 + rsub;
+        const int row = sub_row0(mi) + rl;
+        const i32x4 v = *reinterpret_cast<const i32x4*>(wreg + rl * RS + ch * 16);
+        if (row < rows && colc < ncols)
+          *reinterpret_cast<i32x4*>(H + (int64_t)(m_start + row) * N + n0 + colc) = v;
+      }
+    }
+  } else if constexpr (GATEUP) {
     uint16_t* H = static_cast<uint16_t*>(Cout);
 #pragma unroll
     for (int nj = 0; nj < TN; ++nj) {
@@ -738,18 +775,36 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
         }
     }
   } else {
+    // fp32 results through the LDS as for H above: 32 x TN*32 fp32 per row
+    // sub-tile (rows padded by 32 bytes), then 16-byte stores, 64 / (TN*8)
+    // rows of TN*128 contiguous bytes per instruction
+    constexpr int RS = TN * 128 + 32;
+    constexpr int CPRW = TN * 8;
+    constexpr int RPI = kWave / CPRW;
+    static_assert(NWAVES * 32 * RS <= NS * STAGE, "the staging fits the stages");
     float* Y = static_cast<float*>(Cout);
+    __syncthreads();  // every wave is done with the last stage
+    char* wreg = smem + wave * (32 * RS);
+    const int rsub = lane / CPRW, ch = lane % CPRW;
+    const int colc = wn * TN * 32 + ch * 4;
 #pragma unroll
-    for (int nj = 0; nj < TN; ++nj) {
-      const int col = wn * TN * 32 + nj * 32 + col_l;
-      if (col >= ncols) continue;
+    for (int mi = 0; mi < TM; ++mi) {
+      if (mi >= tm_active) continue;
 #pragma unroll
-      for (int mi = 0; mi < TM; ++mi)
+      for (int nj = 0; nj < TN; ++nj)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = sub_row0(mi) + rlane + 8 * (r >> 2) + (r & 3);
-          if (row < rows) Y[(int64_t)(m_start + row) * N + n0 + col] = acc[mi][nj][r];
+          const int rl = rlane + 8 * (r >> 2) + (r & 3);
+          *reinterpret_cast<float*>(wreg + rl * RS + (nj * 32 + col_l) * 4) = acc[mi][nj][r];
         }
+#pragma unroll
+      for (int r0 = 0; r0 < 32; r0 += RPI) {
+        const int rl = r0 + rsub;
+        const int row = sub_row0(mi) + rl;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(wreg + rl * RS + ch * 16);
+        if (row < rows && colc < ncols)
+          *reinterpret_cast<f32x4*>(Y + (int64_t)(m_start + row) * N + n0 + colc) = v;
+      }
     }
   }
 }
