@@ -132,6 +132,12 @@ def _route_tflops(T, d, E, t_route_ms, x_bf16):
     return {"route_logits": tf, "route_units": "fp32 vector fma", "route_frac": tf / 157.3}
 
 
+def _progress(msg):
+    """One line per finished stage on stderr (the JSON line stays alone on
+    stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def _graph_time(step, n, stream):
     """The step captured once in a HIP graph (torch.cuda.CUDAGraph) and
     replayed n times; ms per replay, event-timed on the given stream."""
@@ -481,6 +487,7 @@ def main():
     if args.fp8 and (args.shared_dff or args.router_stats):
         sys.exit("--fp8 combines with neither --shared-dff nor --router-stats")
     r = _run_layer(wl, args.steps, args.warmup, fp8=args.fp8)
+    _progress(f"{wl.name}: {r['ms']:.3f} ms per step")
     p, dev, a, ws, out, stats, stream = (r[k] for k in ("p", "dev", "a", "ws", "out",
                                                           "stats", "stream"))
     step, ms, per_step, n, N = r["step"], r["ms"], r["per_step"], r["n"], r["N"]
@@ -635,13 +642,16 @@ def main():
         except Exception as ex:  # capture unsupported: report, do not fail the line
             line["graph"] = {"error": repr(ex)[:200]}
     if args.sample_power:
+        _progress("sampling socket power")
         line["power"] = _sample_power(lambda: ffn(Y, ffn_ws), ffn_flops, stream)
         if args.library_loop and not args.fp8 and wl.dtype == W.BF16:
             lib = _library_loop(wl, dev, perm, 1, stream, ffn_flops, fns_only=True)
             line["power_library_gemms"] = _sample_power(lib, ffn_flops, stream)
     if args.library_loop and not args.fp8 and wl.dtype == W.BF16:
+        _progress("vendor-library loop")
         line["library_loop"] = _library_loop(wl, dev, perm, n, stream, ffn_flops)
     if not args.no_cpu_baseline:
+        _progress("CPU baseline (the oracle on the host)")
         line["cpu_baseline"] = _cpu_baseline(
             wl, dev, args.cpu_sample_tokens,
             shared=None if shared is None else [t.float().cpu().numpy() for t in shared[0]],
@@ -656,6 +666,7 @@ def main():
                 continue
             torch.cuda.empty_cache()
             rc = _run_layer(cw, args.steps, args.warmup)
+            _progress(f"{name}: {rc['ms']:.3f} ms per step")
             line["configs"][name] = _config_summary(rc)
             del rc
     print(json.dumps(line), flush=True)

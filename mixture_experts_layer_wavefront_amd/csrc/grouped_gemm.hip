@@ -616,6 +616,12 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   //   row = wm*TM*32 + mi*32 + 8*(r/4) + 4*(lane/32) + r%4,  col = lane%32 (+ sub-tile base)
   const int col_l = lane & 31;
   const int rlane = 4 * (lane >> 5);
+  // SwiGLU: silu(g) u = g u / (1 + e^-g), the quotient by the hardware
+  // reciprocal (within 1 ulp of fp32, far below the bf16 rounding of H that
+  // follows; for large -g, e^-g = inf gives 0 as the division would).  Two
+  // transcendental instructions per element run at a quarter of the VALU
+  // rate, so the division's correction steps were a visible part of the
+  // epilogue.
   if constexpr (GATEUP && MODE == 0) {
     // H goes out through the LDS, one row sub-tile at a time: the wave writes
     // its 32 x TN*32 block of bf16 row-major (rows padded by 32 bytes, so the
@@ -639,7 +645,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float gv = acc[mi][nj][r], u = acc[mi][nj + TN][r];
-          const float h = gv / (1.f + __expf(-gv)) * u;
+          const float h = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * u;
           const int rl = rlane + 8 * (r >> 2) + (r & 3);
           *reinterpret_cast<uint16_t*>(wreg + rl * RS + (nj * 32 + col_l) * 2) =
               f32_to_bf16_bits(h);
@@ -666,7 +672,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
           const int row = sub_row0(mi) + rlane + 8 * (r >> 2) + (r & 3);
           if (row < rows) {
             const float gv = acc[mi][nj][r], u = acc[mi][nj + TN][r];
-            const float h = gv / (1.f + __expf(-gv)) * u;
+            const float h = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * u;
             const int64_t o = (int64_t)(m_start + row) * N + n0 + col;
             H[o] = f32_to_bf16_bits(h);
             if constexpr (MODE == 1) {
