@@ -342,15 +342,31 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
     int local = logical - s_pref[e] * n_nt * NH;
     half = local / (mt_e * n_nt);
     local -= half * mt_e * n_nt;
-    // bands of kGroupM M-tiles walk the N-tiles together, so the tiles an
-    // XCD runs at once share a few activation panels and weight tiles
-    // (an expert of many M-tiles would otherwise re-read all its rows for
-    // every N-tile)
-    const int first_m = local / (kGroupM * n_nt) * kGroupM;
-    const int gsize = min(kGroupM, mt_e - first_m);
-    const int in_band = local - first_m * n_nt;
-    const int m_t = first_m + in_band % gsize, n_t = in_band / gsize;
     const int row_end = offsets[e + 1];
+    // A tall last M-tile (more than MSTEP rows) is the expert's longest:
+    // its N-tiles come first, so a round's longest tiles start early and the
+    // last tiles to start are short ones (when the tiles fill the CUs only
+    // twice, as the Mixtral-shaped down projection's do, a CU drawing two
+    // tall tiles would otherwise set the time).  The other M-tiles follow in
+    // bands.
+    const bool tall_first = TALL && mt_e > 1 && row_end - (offsets[e] + (mt_e - 1) * MSTEP) > MSTEP;
+    int m_t, n_t;
+    if (tall_first && local < n_nt) {
+      m_t = mt_e - 1;
+      n_t = local;
+    } else {
+      // bands of kGroupM M-tiles walk the N-tiles together, so the tiles an
+      // XCD runs at once share a few activation panels and weight tiles (an
+      // expert of many M-tiles would otherwise re-read all its rows for
+      // every N-tile)
+      const int lb = tall_first ? local - n_nt : local;  // index among the banded tiles
+      const int mt_b = tall_first ? mt_e - 1 : mt_e;
+      const int first_m = lb / (kGroupM * n_nt) * kGroupM;
+      const int gsize = min(kGroupM, mt_b - first_m);
+      const int in_band = lb - first_m * n_nt;
+      m_t = first_m + in_band % gsize;
+      n_t = in_band / gsize;
+    }
     m_start = offsets[e] + m_t * MSTEP;
     rows = (m_t == mt_e - 1) ? row_end - m_start : MSTEP;
     n0 = n_t * BN;
