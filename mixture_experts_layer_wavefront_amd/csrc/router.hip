@@ -244,18 +244,29 @@ __global__ __launch_bounds__(256) void router_split_kernel(
 // Partial logits of 128 tokens x EP experts over K-steps [k-slice of s];
 // the experts are [e0, e0 + EP) with e0 = blockIdx.z EP, of the EPtot rows
 // of each weight plane (and of each partial row).  Wave w owns tokens
-// 32w + [0, 32) (two 16-row tiles) and all NTE expert tiles; the three
-// weight planes of each K-step are staged in LDS (64-byte rows,
-// chunk-swizzled), X fragments come straight from global memory.
+// 32w + [0, 32) (two 16-row tiles) and all NTE expert tiles.  Each K-step's
+// three weight planes and 128 token rows are staged in LDS (64-byte rows,
+// chunk-swizzled).  The loads run NSR - 1 K-steps ahead (NSR stages): a
+// K-step's matrix work is short (3 NTE x 2 MFMAs per wave), so with one step
+// ahead every step waited for a whole memory latency.
 template <int NTE>
 __global__ __launch_bounds__(256) void router_logits_kernel(
     const uint16_t* __restrict__ X, int T, int d, const uint16_t* __restrict__ Wsplit,
     int d32, int S, int EPtot, float* __restrict__ partial) {
   constexpr int EP = 16 * NTE;
-  constexpr int ROWS = 3 * EP;           // staged rows per K-step
-  constexpr int STAGE = ROWS * 64;       // bytes
-  constexpr int NINSTR = ROWS / 16;      // 1 KB wave-level loads per stage
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  constexpr int ROWS = 3 * EP;           // staged weight rows per K-step
+  constexpr int WBYTES = ROWS * 64;      // weight part of a stage
+  constexpr int STAGE = WBYTES + kRtTok * 64;  // + the token rows
+  constexpr int NINSTR = ROWS / 16;      // 1 KB wave-level weight loads per stage
+  constexpr int NSR = NTE >= 8 ? 2 : 4;  // stages (K-steps in flight + 1)
+  constexpr int D = NSR - 1;             // K-steps requested ahead
+  // vector-memory loads of one K-step issued by the wave with the fewest:
+  // its share of the weight loads and its two token-row loads (loads
+  // complete in order, so waiting until at most this many per later step
+  // are outstanding finishes the step's loads; waves with more wait a
+  // little longer)
+  constexpr int CMIN = NINSTR / 4 + 2;
+  __shared__ __attribute__((aligned(1024))) char smem[NSR * STAGE];
 
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -267,30 +278,33 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
   const int nks = ks1 - ks0;
 
   // weight-plane loads: instruction q covers staged rows 16q..16q+15; staged
-  // row R is row e0 + R % EP of plane R / EP
+  // row R is row e0 + R % EP of plane R / EP.  Token rows: this wave's 32
+  // tokens, 16 rows per load (rows past T read zero, and so do K chunks
+  // past d).
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wsplit, (uint32_t)((int64_t)3 * EPtot * d32 * 2));
+  const int xt0 = t0 + wave * 32;
+  const int xrows = __builtin_amdgcn_readfirstlane(max(0, min(32, T - xt0)));
+  const int xbase = __builtin_amdgcn_readfirstlane(min(xt0, max(T - 1, 0)));
+  const __amdgpu_buffer_rsrc_t rX =
+      make_rsrc(X + (int64_t)xbase * d, (uint32_t)xrows * (uint32_t)d * 2u);
   auto issue = [&](int stage, int kstep) {
+    char* st = smem + stage * STAGE;
     for (int q = wave; q < NINSTR; q += 4) {
       const uint32_t R = q * 16 + (lane >> 2);
       const uint32_t c = (lane & 3) ^ rt_swz(R);
       const uint32_t G = (R / EP) * (uint32_t)EPtot + (uint32_t)e0 + R % EP;
       const uint32_t vo = G * (uint32_t)d32 * 2u + (uint32_t)kstep * (kRtK * 2) + c * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, MOE_LDS_PTR(smem + stage * STAGE + q * 1024),
-                                               16, vo, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, MOE_LDS_PTR(st + q * 1024), 16, vo, 0, 0, 0);
     }
-  };
-  // X fragments: lane holds token (l % 16) of a 16-row tile, k chunk (l / 16)
-  const int xt0 = t0 + wave * 32;
-  const int xrows = max(0, min(32, T - xt0));
-  const __amdgpu_buffer_rsrc_t rX =
-      make_rsrc(X + (int64_t)min(xt0, max(T - 1, 0)) * d, (uint32_t)xrows * (uint32_t)d * 2u);
-  auto load_x = [&](int kstep, bf16x8 (&x)[2]) {
-    const int kk = kstep * kRtK + 8 * (lane >> 4);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const uint32_t vo = (kk < d) ? ((uint32_t)(mt * 16 + (lane & 15)) * (uint32_t)d + kk) * 2u : kOob;
-      const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rX, vo, 0, 0);
-      x[mt] = __builtin_bit_cast(bf16x8, v);
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t r = h * 16 + (lane >> 2);  // row within the wave's 32
+      const uint32_t R = wave * 32 + r;         // staged token row
+      const uint32_t c = (lane & 3) ^ rt_swz(R);
+      const int kk = kstep * kRtK + c * 8;
+      const uint32_t vo = kk < d ? (r * (uint32_t)d + kk) * 2u : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, MOE_LDS_PTR(st + WBYTES + (wave * 2 + h) * 1024),
+                                               16, vo, 0, 0, 0);
     }
   };
   f32x4 acc[2][NTE];
@@ -299,34 +313,44 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 #pragma unroll
     for (int nt = 0; nt < NTE; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  bf16x8 xc[2], xn[2];
-  issue(0, ks0);
-  load_x(ks0, xc);
-  for (int j = 0; j < nks; ++j) {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (j + 1 < nks) {
-      issue((j + 1) & 1, ks0 + j + 1);
-      load_x(ks0 + j + 1, xn);
-    }
-    const char* st = smem + (j & 1) * STAGE;
 #pragma unroll
-    for (int p = 0; p < 3; ++p)
+  for (int u = 0; u < D; ++u)
+    if (u < nks) issue(u, ks0 + u);
+  // step j consumes stage j % NSR (the loop is unrolled by NSR)
+  for (int j0 = 0; j0 < nks; j0 += NSR) {
 #pragma unroll
-      for (int nt = 0; nt < NTE; ++nt) {
-        // B fragment of expert tile nt, plane p: row p*EP + nt*16 + (l % 16),
-        // chunk l / 16
-        const uint32_t R = p * EP + nt * 16 + (lane & 15);
-        const uint32_t off = R * 64 + (((lane >> 4) ^ rt_swz(R)) * 16);
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(st + off);
+    for (int u = 0; u < NSR; ++u) {
+      const int j = j0 + u;
+      if (j >= nks) break;
+      // step j's loads have landed once at most the later steps' loads are
+      // outstanding; every wave is then done with stage (j - 1) % NSR
+      if (D > 1 && j + D - 1 < nks)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(CMIN * (D > 1 ? D - 1 : 0)) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (j + D < nks) issue((u + D) % NSR, ks0 + j + D);
+      const char* st = smem + u * STAGE;
+      // A fragments: token (l % 16) of 16-row tile mt of this wave, chunk l / 16
+      bf16x8 xa[2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xc[mt], b, acc[mt][nt], 0, 0, 0);
+      for (int mt = 0; mt < 2; ++mt) {
+        const uint32_t R = wave * 32 + mt * 16 + (lane & 15);
+        xa[mt] = *reinterpret_cast<const bf16x8*>(st + WBYTES + R * 64 + (((lane >> 4) ^ rt_swz(R)) * 16));
       }
-    if (j + 1 < nks) {
-      xc[0] = xn[0];
-      xc[1] = xn[1];
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int nt = 0; nt < NTE; ++nt) {
+          // B fragment of expert tile nt, plane p: row p*EP + nt*16 + (l % 16),
+          // chunk l / 16
+          const uint32_t R = p * EP + nt * 16 + (lane & 15);
+          const uint32_t off = R * 64 + (((lane >> 4) ^ rt_swz(R)) * 16);
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(st + off);
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mt], b, acc[mt][nt], 0, 0, 0);
+        }
     }
   }
 
