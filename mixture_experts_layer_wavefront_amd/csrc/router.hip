@@ -9,13 +9,14 @@
 // 확인하기" (the largest selected logit is subtracted before exponentiating).
 //
 // bf16 layers: the logits run on the matrix cores (exact three-way bf16 split
-// of W_r, K split over workgroups), then one wavefront per token adds the
-// partial logits and the bias and takes the top-k.  fp32 layers: one fused
-// kernel accumulates a [TT x E] logit tile with fp32 FMAs from LDS-staged
-// slices of X and W_r and keeps it in LDS for the top-k.  The top-k itself:
-// every lane holds up to four of the E logits, and k rounds of a 64-lane
-// butterfly argmax (ties to the lower expert id) pick the experts in
-// descending-logit order.
+// of W_r, K split over workgroups), then a selection kernel adds the partial
+// logits and the bias and takes the top-k: a group of 8 or 16 lanes per
+// token (k <= 8, at least 128 tokens), else one wavefront per token.  fp32
+// layers: one fused kernel accumulates a [TT x E] logit tile with fp32 FMAs
+// from LDS-staged slices of X and W_r and keeps it in LDS for the top-k.
+// The top-k itself: k rounds of an argmax over the lanes holding the
+// token's logits (ties to the lower expert id) pick the experts in
+// descending-logit order; both layouts give the same bits (topk.h).
 #include "common.h"
 #include "launch.h"
 #include "topk.h"
