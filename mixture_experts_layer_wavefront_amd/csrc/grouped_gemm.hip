@@ -19,7 +19,10 @@
 //    For gate/up one wavefront holds the gate AND the up accumulator of the
 //    same output columns, so SwiGLU is applied in registers before the
 //    single bf16 store of H.  256-row tiles use 8 wavefronts (2 x 4) with
-//    128 x 64 wave tiles; 32-row tiles (few rows per expert) use 4.
+//    128 x 64 wave tiles; 160-row tiles (65-160 rows per expert on average)
+//    4 wavefronts and three stages; 32-row tiles (few rows per expert) 4.
+//    The epilogue writes each 32-row sub-tile into the free LDS stages and
+//    stores it with 16-byte stores.
 //  * Operands are staged global -> LDS with buffer_load_dwordx4 ... lds (no
 //    VGPR round trip), double-buffered, issued by half of the wavefronts so
 //    that on every SIMD one wave keeps issuing MFMAs while the other issues
@@ -27,7 +30,7 @@
 //    expert's end, columns past N and the K tail read as zero.  LDS rows are
 //    128 B (64 bf16 of K); the 16-byte chunks of row R are XOR-swizzled by
 //    ((R ^ (R >> 3)) & 7) so the ds_read_b128 fragment reads hit distinct
-//    banks (rocprof: zero LDS bank conflicts).
+//    banks (rocprof: no LDS bank conflicts in the K loop).
 //  * Ragged tiles (an expert's last rows) run a second instance of the K loop
 //    in which each wave only issues the MFMAs of its row sub-tiles that hold
 //    rows; the hardware pairs waves w and w + 4 on one SIMD (read from the
@@ -42,10 +45,11 @@
 //    per-expert M-tile counts.  The grid is a static upper bound; each
 //    workgroup finds its (expert, n-tile, m-tile) from the prefix and exits
 //    if it has none -- no host round trip.  Tiles are ordered expert-major,
-//    then in bands of four M-tiles that walk the N-tiles together, and
-//    remapped so that the hardware's round-robin of workgroups over the 8
-//    XCDs gives each XCD a contiguous run of tiles: the tiles sharing one
-//    expert's weights and rows share one L2.
+//    an expert's tall tile first (longest first), then in bands of four
+//    M-tiles that walk the N-tiles together, and remapped so that the
+//    hardware's round-robin of workgroups over the 8 XCDs gives each XCD a
+//    contiguous run of tiles: the tiles sharing one expert's weights and
+//    rows share one L2.
 #include "common.h"
 
 #include <type_traits>
