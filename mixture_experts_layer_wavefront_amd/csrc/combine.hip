@@ -28,26 +28,21 @@ constexpr int kColsPerWave = 8 * kWave;  // 8 columns per lane
 // store instruction of the wave covers 1 KB of contiguous memory.  The k
 // source rows are read eight slots at a time (all loads issued before the
 // FMAs, which run in slot order); each source row is read once, past the
-// caches (non-temporal).
+// caches (non-temporal).  The token's destination rows and gate weights are
+// the same for the whole wavefront: scalar loads fetch them, so the row
+// loads start without a round trip through the LDS.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kTokPerBlock * kWave) void combine_kernel(
     const float* __restrict__ Y, const float* __restrict__ Y2,
     const int32_t* __restrict__ dest_row, const float* __restrict__ topk_w, int T, int d,
     int k, const float* __restrict__ add_rows, void* __restrict__ out) {
-  __shared__ int32_t s_dest[kTokPerBlock][32];
-  __shared__ float s_w[kTokPerBlock][32];
   const int lane = threadIdx.x % kWave;
-  const int wv = threadIdx.x / kWave;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int t = blockIdx.x * kTokPerBlock + wv;
   if (t >= T) return;  // uniform per wavefront; no block-wide barrier below
-  // the token's (row, weight) pairs go through LDS: lanes past the row's end
-  // are idle when d is small, so cross-lane shuffles could read inactive lanes
-  if (lane < k) {
-    s_dest[wv][lane] = dest_row[(int64_t)t * k + lane];
-    s_w[wv][lane] = topk_w[(int64_t)t * k + lane];
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  // the token's (row, weight) pairs: the same for the whole wavefront
+  const int32_t* __restrict__ td = dest_row + (int64_t)t * k;
+  const float* __restrict__ tw = topk_w + (int64_t)t * k;
   const int nq = d / 4;                                // chunks of 4 columns per row
   const int q0 = blockIdx.y * (2 * kWave) + lane;      // this lane's chunks: q0, q1
   const int q1 = q0 + kWave;
@@ -67,7 +62,7 @@ __global__ __launch_bounds__(kTokPerBlock * kWave) void combine_kernel(
     int r[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      r[u] = (j0 + u < k) ? s_dest[wv][j0 + u] : -1;
+      r[u] = (j0 + u < k) ? td[j0 + u] : -1;
       if (r[u] >= 0) {
         const f32x4* src = reinterpret_cast<const f32x4*>(Y + (int64_t)r[u] * d);
         a[u] = __builtin_nontemporal_load(src + q0);
@@ -91,7 +86,7 @@ __global__ __launch_bounds__(kTokPerBlock * kWave) void combine_kernel(
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (r[u] < 0) continue;
-      const float w = s_w[wv][j0 + u];
+      const float w = tw[j0 + u];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc0[i] = fmaf(w, a[u][i], acc0[i]);
