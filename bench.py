@@ -241,6 +241,8 @@ def _library_loop(wl, dev, perm, n, stream, flops, fns_only=False):
     import torch.nn.functional as F
     o = perm["offsets"].cpu().tolist()
     Xp, Wd, dff = perm["X_perm"], dev["W_down"], wl.d_ff
+    if Xp is None:  # the forward's permute copies no rows: gather them here
+        Xp = dev["X"].index_select(0, perm["row_token"][:o[-1]].long())
     Wgu = torch.cat([dev["W_gate"], dev["W_up"]], dim=1).contiguous()
     Hf = torch.empty((o[-1], dff), dtype=torch.bfloat16, device="cuda").normal_(0.0, 0.05)
     live = [e for e in range(wl.E) if o[e + 1] > o[e]]
@@ -318,15 +320,17 @@ def _cpu_baseline(wl, dev, ntok, min_s=10.0, max_s=30.0, shared=None, fp8_scales
                       f"fp64 NumPy per-expert loop, {runs} run(s), {total:.1f} s wall"}
 
 
-def _layer_bytes(wl, N, active, a_b, w_b):
+def _layer_bytes(wl, N, active, a_b, w_b, gather):
     """Algorithmic HBM bytes of each stage (inputs read once, outputs written
     once): route reads X and W_r and writes ids and weights; the permute reads
-    X and the ids and writes X_perm and the index maps; the FFN reads the
-    active experts' weights and X_perm and writes Y_perm (fp32); the combine
-    reads Y_perm, the dest rows and weights and writes the fp32 output."""
+    the ids and writes the index maps, and without `gather` also reads X and
+    writes X_perm; the FFN reads the active experts' weights and each kept
+    copy's input row (of X_perm, or gathered from X) and writes Y_perm
+    (fp32); the combine reads Y_perm, the dest rows and weights and writes the
+    fp32 output."""
     T, d, E, k, dff = wl.T, wl.d_model, wl.E, wl.top_k, wl.d_ff
     return {"route": T * d * a_b + E * d * 4 + T * k * 8,
-            "permute": T * d * a_b + N * d * a_b + T * k * 24 + N * 4,
+            "permute": (0 if gather else T * d * a_b + N * d * a_b) + T * k * 24 + N * 4,
             "grouped_ffn": 3 * active * d * dff * w_b + N * d * a_b + N * d * 4,
             "combine": N * d * 4 + T * d * 4 + T * k * 8}
 
@@ -384,12 +388,15 @@ def _run_layer(wl, steps, warmup, fp8=False):
     active = int(np.count_nonzero(st[wl.E + 1:2 * wl.E + 1] - st[wl.E:2 * wl.E]))
 
     # ---- per stage (same kernels, called through the stage entry points) ----
+    # bf16 activations: the forward's permute copies no rows and its grouped
+    # FFN reads them from X through row_token (moe_grouped_ffn_rows)
+    gather = wl.dtype == W.BF16
     idx, w = M.moe_route(p, dev["X"], dev["W_r"], dev["bias"])
-    perm = M.moe_permute(p, dev["X"], idx)
-    if fp8:
-        ffn = lambda Yo=None, w=None: M.moe_grouped_ffn_scaled(  # noqa: E731
-            p, perm["X_perm"], perm["offsets"], dev["W_gate"], dev["W_up"],
-            dev["W_down"], w_scales, Yo, w)
+    perm = M.moe_permute(p, dev["X"], idx, copy_rows=not gather)
+    if gather:
+        ffn = lambda Yo=None, w=None: M.moe_grouped_ffn_rows(  # noqa: E731
+            p, dev["X"], perm["row_token"], perm["offsets"], dev["W_gate"], dev["W_up"],
+            dev["W_down"], Yo, w, w_scales=w_scales)
     else:
         ffn = lambda Yo=None, w=None: M.moe_grouped_ffn(  # noqa: E731
             p, perm["X_perm"], perm["offsets"], dev["W_gate"], dev["W_up"],
@@ -408,7 +415,7 @@ def _run_layer(wl, steps, warmup, fp8=False):
 
     a_b = 2 if wl.dtype == W.BF16 else 4
     w_b = 1 if fp8 else a_b
-    by = _layer_bytes(wl, N, active, a_b, w_b)
+    by = _layer_bytes(wl, N, active, a_b, w_b, gather)
     ffn_flops = 6.0 * N * wl.d_model * wl.d_ff
     return dict(wl=wl, p=p, dev=dev, a=a, ws=ws, out=out, stats=stats, stream=stream,
                 step=step, w_scales=w_scales, ms=ms, per_step=per_step, wall=wall, st=st,

@@ -154,7 +154,9 @@ moe_status_t moe_route(const moe_problem_t* p, const void* X, const float* W_r,
  *   dest_row       [T, top_k] int32 out: row in X_perm, -1 if dropped
  *   row_token      [R] int32 out: token of each row (rows >= offsets[E]
  *                  are not written)
- *   X_perm         [R, d_model] act dtype out: X_perm[r] = X[row_token[r]]
+ *   X_perm         [R, d_model] act dtype out: X_perm[r] = X[row_token[r]];
+ *                  or NULL: no row is copied (for moe_grouped_ffn_rows,
+ *                  which reads the rows of X through row_token)
  *   workspace      >= moe_permute_workspace_bytes(p) bytes */
 moe_status_t moe_permute(const moe_problem_t* p, const void* X,
                          const int32_t* topk_idx, int32_t* expert_counts,
@@ -180,6 +182,27 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* X_perm,
                              float* Y_perm, void* workspace, size_t ws_bytes,
                              hipStream_t stream);
 
+/* Step 5 without the permuted copy of the input: moe_grouped_ffn with
+ * X_perm[r] read as X[row_token[r]] (the same steps as above; the expert
+ * rows are fetched from X by the gate/up GEMM's own loads, so the reorder of
+ * step 4 only assigns rows).  Same result as moe_grouped_ffn on the X_perm
+ * that moe_permute writes, bit for bit (and, with FP8 expert weights, as
+ * moe_grouped_ffn_scaled).  bf16 activations with T * d_model * 2 < 2^31
+ * bytes (else MOE_ERR_UNSUPPORTED).
+ *   X              [T, d_model] bf16
+ *   row_token      [R] int32: token of each row r < offsets[E] (moe_permute)
+ *   expert_offsets [E+1] int32 (device)
+ *   w_scales       [E, 3] fp32 when p->w_dtype is MOE_FP8_E4M3 (as in
+ *                  moe_grouped_ffn_scaled), else NULL; a mismatch is
+ *                  MOE_ERR_INVALID_ARG
+ *   Y_perm         [R, d_model] fp32 out (rows >= offsets[E] not written)
+ *   workspace      >= moe_grouped_ffn_workspace_bytes(p) bytes */
+moe_status_t moe_grouped_ffn_rows(const moe_problem_t* p, const void* X,
+                                  const int32_t* row_token, const int32_t* expert_offsets,
+                                  const void* W_gate, const void* W_up, const void* W_down,
+                                  const float* w_scales, float* Y_perm, void* workspace,
+                                  size_t ws_bytes, hipStream_t stream);
+
 /* Step 6: out[t] = sum over j ascending with dest_row[t, j] >= 0 of
  * topk_w[t, j] * Y_perm[dest_row[t, j]], accumulated in fp32 and stored in
  * out_dtype (one rounding when that is BF16).  A token with every copy dropped gets a zero row.
@@ -194,7 +217,9 @@ moe_status_t moe_combine(const moe_problem_t* p, const float* Y_perm,
                          void* out, hipStream_t stream);
 
 /* The whole layer: moe_route, moe_permute, moe_grouped_ffn, moe_combine in
- * order on `stream`, intermediates carved from the workspace.
+ * order on `stream`, intermediates carved from the workspace.  bf16 layers
+ * (T * d_model * 2 < 2^31 bytes) run the permute without its row copy and
+ * moe_grouped_ffn_rows in place of moe_grouped_ffn (same result, bit for bit).
  *   out   [T, d_model] out_dtype out
  *   stats [E + (E+1) + 1] int32 out, or NULL: expert_counts | expert_offsets
  *         | num_dropped (routing statistics for monitoring)

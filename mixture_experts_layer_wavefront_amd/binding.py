@@ -31,7 +31,8 @@ MOE_SOFTMAX_THEN_TOPK = 1
 SYMBOLS = ("moe_capacity", "moe_rows_bound", "moe_route_workspace_bytes",
            "moe_permute_workspace_bytes",
            "moe_grouped_ffn_workspace_bytes", "moe_workspace_bytes",
-           "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
+           "moe_route", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_rows",
+           "moe_combine",
            "moe_forward", "moe_forward_noalloc", "moe_route_stats_workspace_bytes", "moe_route_stats",
            "moe_forward_stats_workspace_bytes", "moe_forward_stats",
            "moe_forward_shared_workspace_bytes", "moe_forward_shared",
@@ -83,6 +84,8 @@ def load(path: str = LIB_PATH):
                                        sz, st]),
         "moe_grouped_ffn": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, sz,
                                            st]),
+        "moe_grouped_ffn_rows": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp,
+                                                vp, vp, sz, st]),
         "moe_combine": (ctypes.c_int, [P, vp, vp, vp, vp, st]),
         "moe_forward": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        sz, st]),
@@ -227,8 +230,10 @@ def moe_route(p, X, W_r, bias=None, topk_idx=None, topk_w=None,
     return topk_idx, topk_w
 
 
-def moe_permute(p, X, topk_idx, workspace=None, stream=None, out=None):
-    """Counts, offsets, drops, dest rows, inverse map and X_perm (dict)."""
+def moe_permute(p, X, topk_idx, workspace=None, stream=None, out=None,
+                copy_rows=True):
+    """Counts, offsets, drops, dest rows, inverse map and X_perm (dict).
+    copy_rows=False: no X_perm (None), for moe_grouped_ffn_rows."""
     torch = _torch()
     dev = X.device
     R = rows_bound(p)
@@ -238,8 +243,8 @@ def moe_permute(p, X, topk_idx, workspace=None, stream=None, out=None):
         dropped=torch.empty(1, dtype=torch.int32, device=dev),
         dest_row=torch.empty((p.T, p.top_k), dtype=torch.int32, device=dev),
         row_token=torch.empty(max(R, 1), dtype=torch.int32, device=dev),
-        X_perm=torch.empty((max(R, 1), p.d_model), dtype=_act_dtype(p),
-                           device=dev))
+        X_perm=(torch.empty((max(R, 1), p.d_model), dtype=_act_dtype(p),
+                            device=dev) if copy_rows else None))
     ws = _workspace(permute_workspace_bytes(p), dev, workspace)
     _check(load().moe_permute(
         ctypes.byref(p), _ptr(X, _act_dtype(p), "X"),
@@ -268,6 +273,30 @@ def moe_grouped_ffn(p, X_perm, offsets, W_gate, W_up, W_down, Y_perm=None,
         _ptr(W_up, wt, "W_up"), _ptr(W_down, wt, "W_down"),
         _ptr(Y_perm, torch.float32, "Y_perm"), _ptr(ws), ws.numel(),
         _stream(stream)), "moe_grouped_ffn")
+    return Y_perm
+
+
+def moe_grouped_ffn_rows(p, X, row_token, offsets, W_gate, W_up, W_down,
+                         Y_perm=None, workspace=None, stream=None, w_scales=None):
+    """moe_grouped_ffn with row r of X_perm read as X[row_token[r]] (bf16
+    activations): no permuted copy of X.  FP8 expert weights (uint8 codes)
+    take their scales [E, 3] in `w_scales`.  Returns Y_perm (fp32)."""
+    torch = _torch()
+    dev = X.device
+    R = rows_bound(p)
+    if Y_perm is None:
+        Y_perm = torch.empty((max(R, 1), p.d_model), dtype=torch.float32,
+                             device=dev)
+    ws = _workspace(grouped_ffn_workspace_bytes(p), dev, workspace)
+    wt = _act_dtype(p)
+    qt = torch.uint8 if w_scales is not None else wt
+    _check(load().moe_grouped_ffn_rows(
+        ctypes.byref(p), _ptr(X, wt, "X"), _ptr(row_token, torch.int32, "row_token"),
+        _ptr(offsets, torch.int32, "offsets"), _ptr(W_gate, qt, "W_gate"),
+        _ptr(W_up, qt, "W_up"), _ptr(W_down, qt, "W_down"),
+        _ptr(w_scales, torch.float32, "w_scales"),
+        _ptr(Y_perm, torch.float32, "Y_perm"), _ptr(ws), ws.numel(),
+        _stream(stream)), "moe_grouped_ffn_rows")
     return Y_perm
 
 

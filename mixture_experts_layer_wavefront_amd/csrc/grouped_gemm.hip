@@ -79,6 +79,7 @@ constexpr int kF8SNS = 2;      // 32-row tiles with FP8 weights: stages
 constexpr int kF8SNW = 2;      // 32-row tiles with FP8 weights: 64 output columns
 constexpr int kBntRows = 256;  // 256-row tiles: stream the weights up to this many rows per expert
 constexpr int kStreamRows = 160;  // few rows per expert: 160-row tiles, 4 waves, 3 stages
+constexpr int kPrefixBytes = 1040;  // LDS copy of the tile prefix (E + 1 <= 257 entries)
 
 // Chunk swizzle of LDS row R (16-byte chunks).  256-byte rows (16 chunks),
 // 128-byte rows (8 chunks) and 64-byte rows (4 chunks): 16, 8 or 16
@@ -173,7 +174,8 @@ struct GemmCfg {
   static_assert((!AT || CPRA >= 16) && (!BT || CPRB >= 16), "T rows: at least 256 bytes");
   static_assert(!(GATEUP && BT) && !(BF8 && BT), "T layout: one bf16 B");
   static constexpr int KSUB = BK / 16;               // MFMA k-steps per stage
-  static constexpr int LDS_BYTES = NS * STAGE + 1040;  // + the tile prefix
+  // + the tile prefix, and for gate/up the gathered rows of a tile (mode 6)
+  static constexpr int LDS_BYTES = NS * STAGE + kPrefixBytes + (GATEUP ? BM * 4 : 0);
 };
 
 // Chunk swizzle of T-layout row R (k index): the four rows a transpose read
@@ -234,6 +236,8 @@ struct GemmArgs {
   uint16_t* U;          // mode 1: U out; mode 2: U in
   int M, lda, ldb, msplit;  // mode 3 (lda also modes 4, 5; ldb mode 5)
   void* C1;                 // modes 3-5
+  const int32_t* gather;    // mode 6: source row of A for each row r < offsets[E]
+  int gather_rows;          // mode 6: rows of A
 };
 
 // A [R, K] bf16 rows; B0/B1 [E, N, K] bf16, or FP8 E4M3 codes when BF8
@@ -252,9 +256,15 @@ struct GemmArgs {
 // T layout, fp32 out): half 0 writes dG Wg to C, half 1 dU Wu to C1.
 // MODE 5: the down projection split in two K halves the same way (A [R, lda],
 // B [E, N, ldb] with K = lda / 2 per half): partial sums to C and C1.
+// MODE 6: mode 0's gate/up with the A rows gathered: row r of the expert-
+// grouped order is row gather[r] of A ([gather_rows, K], the layer's input
+// X), so no permuted copy of the input is written or read.
 template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS, int BAUX, bool BF8,
-          int MODE>
+          int MODE_>
 __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const GemmArgs g) {
+  constexpr bool GATHER = MODE_ == 6;
+  constexpr int MODE = GATHER ? 0 : MODE_;
+  static_assert(!GATHER || GATEUP, "mode 6 is a gate/up mode");
   constexpr bool AT = MODE == 3;
   constexpr bool BT = MODE >= 2 && MODE <= 4;
   const uint16_t* __restrict__ A = g.A;
@@ -283,6 +293,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   constexpr int MSTEP = TALL ? 256 : BM;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   int32_t* s_pref = reinterpret_cast<int32_t*>(smem + NS * STAGE);
+  int32_t* s_rows = reinterpret_cast<int32_t*>(smem + NS * STAGE + kPrefixBytes);  // GATHER
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -382,7 +393,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
       if (MODE == 4 && half) B0 = B1;
       if (half) Cout = g.C1;
     } else {
-      a_off = (int64_t)m_start * K;
+      a_off = GATHER ? 0 : (int64_t)m_start * K;
       kbytes = (uint32_t)K * 2u;
     }
     if constexpr (BT) {
@@ -404,9 +415,11 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   // the columns past M or N read the next row, which only reaches output
   // rows or columns that the epilogue drops.  Widths are multiples of 8
   // elements: no 16-byte chunk straddles a range end.
+  // Gathered A: the whole input (its rows are looked up per tile below).
   const uint32_t a_bytes =
-      AT ? (K > 0 ? (uint32_t)(K - 1) * kbytes + (uint32_t)rows * 2u : 0u)
-         : (uint32_t)rows * kbytes - (uint32_t)half * (uint32_t)K * 2u;
+      GATHER ? (uint32_t)g.gather_rows * kbytes
+      : AT ? (K > 0 ? (uint32_t)(K - 1) * kbytes + (uint32_t)rows * 2u : 0u)
+           : (uint32_t)rows * kbytes - (uint32_t)half * (uint32_t)K * 2u;
   const uint32_t b_bytes =
       BT ? (K > 0 ? (uint32_t)(K - 1) * kbytesB + (uint32_t)ncols * 2u : 0u)
          : (uint32_t)ncols * kbytesB - (uint32_t)half * (uint32_t)K * (BF8 ? 1u : 2u);
@@ -452,18 +465,53 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
     }
     return uint2{voff, (uint32_t)kcol};
   };
+  // Gathered A: the tile's source rows are requested first (before the
+  // weight loads of the first stages, so their latency overlaps them), go to
+  // the LDS once, and then each of the wave's A loads keeps its byte offset
+  // at k = 0 (the source row's, or one past every buffer for rows past the
+  // tile, which read zero).
+  constexpr int NAW = GATHER ? (NIA + LW - 1) / LW : 1;
+  constexpr int RPT = GATHER ? (BM + Cfg::NT - 1) / Cfg::NT : 1;  // rows per thread
+  uint32_t a_gat[NAW];
+  int32_t rsrc_row[RPT];
+  if constexpr (GATHER) {
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int r = tid + j * Cfg::NT;
+      rsrc_row[j] = r < rows ? g.gather[m_start + r] : -1;
+    }
+    asm volatile("" ::: "memory");  // the row loads go out before the stage loads
+  }
+  auto gather_rows = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int r = tid + j * Cfg::NT;
+      if (r < BM) s_rows[r] = rsrc_row[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NAW; ++i) {
+      const int qi = wave + LW * i;
+      const uint32_t R = qi * RPIA + lane / CPRA;
+      const uint32_t c = (lane % CPRA) ^ swz<CPRA>(R);
+      const int src = qi < NIA ? s_rows[R] : -1;
+      a_gat[i] = src < 0 ? kOob : (uint32_t)src * kbytes + c * 16;
+    }
+  };
   const int nk = (K + BK - 1) / BK;
   const bool ktail = (K % BK) != 0;
   // bytes a stage advances along K
   const uint32_t stepA = AT ? (uint32_t)BK * kbytes : (uint32_t)RBA;
   const uint32_t stepB = BT ? (uint32_t)BK * kbytesB : (uint32_t)RBB;
 
-  auto issue = [&](int stage, int kt) __attribute__((always_inline)) {
+  // part 0: the stage's loads; 1: only its A loads; 2: only its B loads
+  auto issue = [&](int stage, int kt, int part) __attribute__((always_inline)) {
     if (LW < NWAVES && wave >= LW) return;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int qi = wave + LW * i;
       const bool is_a = qi < NIA;
+      if ((part == 1 && !is_a) || (part == 2 && is_a)) continue;
       // A rows past the tile's rows are not loaded when a whole load (8
       // rows) lies past them: their sub-tiles issue no MFMA, or only for
       // rows that are never stored (a partly filled sub-tile reads stale LDS
@@ -472,7 +520,8 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
       if (NS == 2 && !AT && is_a && qi * RPIA >= rows) continue;
       const uint2 lo = load_off(i);
       const int kc = (int)lo.y;
-      uint32_t vo = lo.x + (uint32_t)kt * (is_a ? stepA : stepB);
+      uint32_t vo = ((GATHER && is_a) ? a_gat[i < NAW ? i : 0] : lo.x) +
+                    (uint32_t)kt * (is_a ? stepA : stepB);
       const bool t_layout = is_a ? AT : BT;
       if (!t_layout && ktail && kt * BK + kc >= K) vo = kOob;
       char* dst = smem + stage * STAGE + qi * 1024;
@@ -570,13 +619,19 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   auto kloop = [&](auto na) {
     constexpr int NA = decltype(na)::value;
     auto active = [&](int mi) { return NA < 0 ? mi < tm_active : mi < NA; };
+    if constexpr (!GATHER) {
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-      if (s < nk) issue(s, s);
+      for (int s = 0; s < NS - 1; ++s)
+        if (s < nk) issue(s, s, 0);
+    }
     for (int kt = 0; kt < nk; ++kt) {
-      if (kt + NS - 2 < nk) stage_barrier<IPW * (NS - 2)>();
+      // gathered A: the first stages' A loads went out after all their B
+      // loads, so the first wait leaves only later stages' A loads pending
+      // (the fewest any loading wave has)
+      if (GATHER && NS > 2 && kt == 0 && kt + NS - 2 < nk) stage_barrier<NIA / LW * (NS - 2)>();
+      else if (kt + NS - 2 < nk) stage_barrier<IPW * (NS - 2)>();
       else stage_barrier<0>();
-      if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, kt + NS - 1);
+      if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, kt + NS - 1, 0);
       const char* st = smem + (kt % NS) * STAGE;
 #pragma unroll
       for (int ks = 0; ks < KSUB; ++ks) {
@@ -615,6 +670,17 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
       }
     }
   };
+  // gathered A: the first NS - 1 stages' B loads, then the rows, then their
+  // A loads (kloop issues the first stages itself otherwise)
+  if constexpr (GATHER) {
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < nk) issue(s, s, 2);
+    gather_rows();
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < nk) issue(s, s, 1);
+  }
   if (tm_active == TM) kloop(std::integral_constant<int, TM>{});
   else if (TM == 5 && tm_active == 4) kloop(std::integral_constant<int, 4>{});
   else kloop(std::integral_constant<int, -1>{});
@@ -909,11 +975,14 @@ hipError_t launch_gemm_args(const GemmArgs& a, int64_t R, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// gather != nullptr (gate/up only): A rows gathered by gather[], A has
+// gather_rows rows (mode 6).
 template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS, int BAUX, bool BF8 = false>
 hipError_t launch_gemm(const void* A, const void* B0, const void* B1, int N,
                        int K, int E, int64_t R, const int32_t* offsets,
                        const int32_t* mt_prefix, void* C, hipStream_t stream,
-                       const float* scales = nullptr) {
+                       const float* scales = nullptr, const int32_t* gather = nullptr,
+                       int gather_rows = 0) {
   GemmArgs a{};
   a.A = static_cast<const uint16_t*>(A);
   a.B0 = B0;
@@ -925,6 +994,13 @@ hipError_t launch_gemm(const void* A, const void* B0, const void* B1, int N,
   a.mt_prefix = mt_prefix;
   a.C = C;
   a.scales = scales;
+  if constexpr (GATEUP) {
+    if (gather != nullptr) {
+      a.gather = gather;
+      a.gather_rows = gather_rows;
+      return launch_gemm_args<MW, NW, TM, TN, GATEUP, BK, NS, BAUX, BF8, 6>(a, R, stream);
+    }
+  }
   return launch_gemm_args<MW, NW, TM, TN, GATEUP, BK, NS, BAUX, BF8, 0>(a, R, stream);
 }
 
@@ -1024,7 +1100,8 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
                               const void* W_up, const void* W_down, int64_t R,
                               int d, int E, int d_ff, int rows_per_expert,
                               float* Y_perm, void* scratch, bool prefix_ready,
-                              hipStream_t stream, const float* w_scales, bool defer) {
+                              hipStream_t stream, const float* w_scales, bool defer,
+                              const int32_t* gather, int gather_rows) {
   const bool fp8 = w_scales != nullptr;
   const int bm = ffn_tile_rows(bf16, rows_per_expert, fp8);
   const bool small_m = bm == 32;
@@ -1032,6 +1109,8 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
   int32_t* mt_prefix = static_cast<int32_t*>(scratch);
   void* H = static_cast<char*>(scratch) + align256((size_t)(E + 1) * 4);
   float* Y_half = ffn_half_sums(scratch, R, E, d, d_ff, bf16, rows_per_expert);
+  if (gather != nullptr && (!bf16 || (int64_t)gather_rows * d * 2 > INT32_MAX))
+    return hipErrorInvalidValue;  // gathered rows: bf16, one 32-bit buffer range
   if (!bf16) {
     const dim3 g1((d_ff + 255) / 256, (unsigned)R), g2((d + 255) / 256, (unsigned)R);
     ffn_f32_gateup_kernel<<<g1, 256, 0, stream>>>(
@@ -1052,11 +1131,11 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (fp8) {
-      err = launch_gemm<1, kF8SNW, 1, 1, true, kF8SBK, kF8SNS, kSBAUX, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales);
+      err = launch_gemm<1, kF8SNW, 1, 1, true, kF8SBK, kF8SNS, kSBAUX, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales, gather, gather_rows);
       if (err != hipSuccess) return err;
       return launch_gemm<1, kF8SNW, 1, 1, false, kF8SBK, kF8SNS, kSBAUX, true>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream, w_scales);
     }
-    err = launch_gemm<1, kSNW, 1, 1, true, kSBK, kSNS, kSBAUX>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
+    err = launch_gemm<1, kSNW, 1, 1, true, kSBK, kSNS, kSBAUX>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, nullptr, gather, gather_rows);
     if (err != hipSuccess) return err;
     return launch_gemm<1, kSNW, 1, 1, false, kSBK, kSNS, kSBAUX>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
   }
@@ -1070,18 +1149,18 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
     // K = 128 per stage, so each weight row is read 128 bytes (one cache
     // line) at a time; 64 KB stages, two of them
     if (rows_per_expert <= 128) {
-      err = launch_gemm<2, 4, 2, 1, true, 128, 2, kNonTemporal, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales);
+      err = launch_gemm<2, 4, 2, 1, true, 128, 2, kNonTemporal, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales, gather, gather_rows);
       if (err != hipSuccess) return err;
       return launch_down<2, 4, 2, 2, 128, 2, kNonTemporal, true>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, w_scales, defer);
     }
-    err = launch_gemm<2, 4, 2, 1, true, 128, 2, 0, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales);
+    err = launch_gemm<2, 4, 2, 1, true, 128, 2, 0, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales, gather, gather_rows);
     if (err != hipSuccess) return err;
     return launch_down<2, 4, 2, 2, 128, 2, 0, true>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, w_scales, defer);
   }
   if (fp8) {
     // FP8 weights, many rows per expert: the tall 256-row tiles of the bf16
     // path (the weight tiles are shared by several M-tiles through L2)
-    err = launch_gemm<2, kNW, 5, 4 / kNW, true, kBK, 2, 0, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales);
+    err = launch_gemm<2, kNW, 5, 4 / kNW, true, kBK, 2, 0, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales, gather, gather_rows);
     if (err != hipSuccess) return err;
     return launch_down<2, kNW, 5, kDTN / kNW, kBK, 2, 0, true>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, w_scales, defer);
   }
@@ -1091,19 +1170,19 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
     // 160-row tiles of 4 waves (160 x 64 wave tiles) leave room for three
     // 52 KB stages (two in flight while one is multiplied); 128-byte
     // weight-row pieces per stage, read past the caches
-    err = launch_gemm<1, 4, 5, 1, true, kBK, 3, kNonTemporal>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
+    err = launch_gemm<1, 4, 5, 1, true, kBK, 3, kNonTemporal>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, nullptr, gather, gather_rows);
     if (err != hipSuccess) return err;
     return launch_down<1, 4, 5, 2, kBK, 3, kNonTemporal, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr, defer);
   }
   if (rows_per_expert <= kBntRows) {
     // about one M-tile per expert: every weight tile is read once
-    err = launch_gemm<2, kNW, 4, 4 / kNW, true, kBK, kNS, kNonTemporal>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
+    err = launch_gemm<2, kNW, 4, 4 / kNW, true, kBK, kNS, kNonTemporal>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, nullptr, gather, gather_rows);
     if (err != hipSuccess) return err;
     return launch_down<2, kNW, 4, kDTN / kNW, kBK, kNS, kNonTemporal, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr, defer);
   }
   // several M-tiles per expert: tall tiles (the schedule merges remainders
   // of up to 64 rows into the expert's last tile)
-  err = launch_gemm<2, kNW, 5, 4 / kNW, true, kBK, 2, 0>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream);
+  err = launch_gemm<2, kNW, 5, 4 / kNW, true, kBK, 2, 0>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, nullptr, gather, gather_rows);
   if (err != hipSuccess) return err;
   return launch_down<2, kNW, 5, kDTN / kNW, kBK, 2, 0, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr, defer);
 }

@@ -23,6 +23,8 @@ hipError_t launch_route(const void* X, bool x_bf16, const float* W_r,
 // scan with capacity; destination rows and the row copy (one kernel for few
 // copies).  With mt_prefix != nullptr it also writes the grouped FFN's tile
 // schedule: M-tiles per expert under tile_code (m_tiles; see launch_grouped_ffn).
+// X_perm == nullptr: no row is copied (dest_row and row_token only, for a
+// grouped FFN that gathers its input rows through row_token).
 size_t permute_scratch_bytes(int T, int k, int E);
 hipError_t launch_permute(const void* X, bool x_bf16, const int32_t* topk_idx,
                           int T, int d, int E, int k, int C,
@@ -39,7 +41,10 @@ hipError_t launch_permute(const void* X, bool x_bf16, const int32_t* topk_idx,
 // nullptr: the weights are FP8 E4M3 codes with scales [E, 3] (bf16 layers).
 // The down projection runs as two K halves (their sums added afterwards) for
 // shapes whose 256 x 256 tiles fill the chip only a few times; the second
-// half's partial sums need R d fp32 more scratch.
+// half's partial sums need R d fp32 more scratch.  gather != nullptr (bf16
+// layers, gather_rows * d * 2 < 2^31): X_perm is the layer's input X itself
+// ([gather_rows, d]) and row r of the expert-grouped order is its row
+// gather[r] (the permute's row_token), so the permuted copy is never made.
 int ffn_tile_rows(bool bf16, int rows_per_expert, bool fp8 = false);
 // The M-tile code of moe_forward's grouped FFN (m_tiles): ffn_tile_rows, or
 // 256-row tiles that take remainders of up to 64 rows (256-row tiles with
@@ -56,7 +61,8 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
                               int64_t R, int d, int E, int d_ff, int rows_per_expert,
                               float* Y_perm, void* scratch, bool prefix_ready,
                               hipStream_t stream, const float* w_scales = nullptr,
-                              bool defer_half_sum = false);
+                              bool defer_half_sum = false, const int32_t* gather = nullptr,
+                              int gather_rows = 0);
 
 // Where a split down projection leaves its second K half (inside `scratch`),
 // or nullptr when it is not split.

@@ -69,6 +69,12 @@ int mean_rows_per_expert(const moe_problem_t* p) {
   return (int)std::ceil(mean);
 }
 
+// bf16 layers: the grouped FFN reads the tokens' rows of X through row_token
+// (one 32-bit buffer range over X), so no permuted copy of X is made.
+bool gather_input(const moe_problem_t* p) {
+  return is_bf16(p) && (int64_t)p->T * p->d_model * 2 <= INT32_MAX;
+}
+
 struct ForwardLayout {
   size_t topk_idx, topk_w, route_scratch, perm_scratch, stats, dest_row, row_token,
       x_perm, ffn_scratch, y_perm, total;
@@ -87,7 +93,7 @@ ForwardLayout forward_layout(const moe_problem_t* p, bool router_stats = false) 
   L.stats = o; o += a256((size_t)(2 * p->E + 2) * 4);
   L.dest_row = o; o += a256(Tk * 4);
   L.row_token = o; o += a256(R * 4);
-  L.x_perm = o; o += a256(R * p->d_model * act_bytes(p));
+  L.x_perm = o; o += gather_input(p) ? 0 : a256(R * p->d_model * act_bytes(p));
   L.ffn_scratch = o;
   o += a256(moe::ffn_scratch_bytes((int64_t)R, p->E, p->d_model, p->d_ff, is_bf16(p),
                                    mean_rows_per_expert(p)));
@@ -156,14 +162,16 @@ hipError_t enqueue_routed(const moe_problem_t* p, const void* X, const float* W_
   // the permute also writes the FFN's tile schedule (start of its scratch)
   const int bm = moe::ffn_tile_code(bf, mean_rows_per_expert(p), w_scales != nullptr);
   int32_t* mt_prefix = bm > 0 ? reinterpret_cast<int32_t*>(ws + L.ffn_scratch) : nullptr;
+  const bool gather = gather_input(p);
   e = moe::launch_permute(X, bf, topk_idx, p->T, p->d_model, p->E, p->top_k,
                           capacity_int(p), counts, offsets, dropped, dest_row, row_token,
-                          x_perm, ws + L.perm_scratch, mt_prefix, bm, stream);
+                          gather ? nullptr : x_perm, ws + L.perm_scratch, mt_prefix, bm, stream);
   if (e != hipSuccess) return e;
-  return moe::launch_grouped_ffn(x_perm, bf, offsets, W_gate, W_up, W_down, moe_rows_bound(p),
-                                 p->d_model, p->E, p->d_ff, mean_rows_per_expert(p), y_perm,
-                                 ws + L.ffn_scratch, mt_prefix != nullptr, stream, w_scales,
-                                 /*defer_half_sum=*/true);
+  return moe::launch_grouped_ffn(gather ? X : x_perm, bf, offsets, W_gate, W_up, W_down,
+                                 moe_rows_bound(p), p->d_model, p->E, p->d_ff,
+                                 mean_rows_per_expert(p), y_perm, ws + L.ffn_scratch,
+                                 mt_prefix != nullptr, stream, w_scales,
+                                 /*defer_half_sum=*/true, gather ? row_token : nullptr, p->T);
 }
 
 // The whole layer with its intermediates carved from `ws` (L.total bytes).
@@ -355,8 +363,7 @@ moe_status_t moe_permute(const moe_problem_t* p, const void* X,
   moe_status_t st = validate(p, true);
   if (st != MOE_OK) return st;
   if (!expert_counts || !expert_offsets || !num_dropped) return MOE_ERR_INVALID_ARG;
-  if (p->T > 0 && (!X || !topk_idx || !dest_row || !row_token || !X_perm))
-    return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && (!X || !topk_idx || !dest_row || !row_token)) return MOE_ERR_INVALID_ARG;
   if (!workspace || ws_bytes < moe_permute_workspace_bytes(p)) return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_permute(X, is_bf16(p), topk_idx, p->T, p->d_model, p->E,
                                         p->top_k, capacity_int(p), expert_counts,
@@ -379,6 +386,26 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* X_perm,
                                             W_down, R, p->d_model, p->E, p->d_ff,
                                             mean_rows_per_expert(p), Y_perm, workspace, false,
                                             stream));
+}
+
+moe_status_t moe_grouped_ffn_rows(const moe_problem_t* p, const void* X,
+                                  const int32_t* row_token, const int32_t* expert_offsets,
+                                  const void* W_gate, const void* W_up, const void* W_down,
+                                  const float* w_scales, float* Y_perm, void* workspace,
+                                  size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = validate(p, true);
+  if (st != MOE_OK) return st;
+  if (!gather_input(p)) return MOE_ERR_UNSUPPORTED;
+  const int64_t R = moe_rows_bound(p);
+  if (R == 0) return MOE_OK;
+  if (!X || !row_token || !expert_offsets || !W_gate || !W_up || !W_down || !Y_perm)
+    return MOE_ERR_INVALID_ARG;
+  if (is_fp8(p) != (w_scales != nullptr)) return MOE_ERR_INVALID_ARG;
+  if (!workspace || ws_bytes < moe_grouped_ffn_workspace_bytes(p)) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_grouped_ffn(X, true, expert_offsets, W_gate, W_up, W_down, R,
+                                            p->d_model, p->E, p->d_ff,
+                                            mean_rows_per_expert(p), Y_perm, workspace, false,
+                                            stream, w_scales, false, row_token, p->T));
 }
 
 moe_status_t moe_combine(const moe_problem_t* p, const float* Y_perm,

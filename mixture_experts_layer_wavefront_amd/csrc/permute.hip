@@ -25,7 +25,9 @@
 //                  scan over experts, and the dropped total.
 //   K3 scatter     one wavefront per token: destination rows, the inverse
 //                  map, then the X row is read once and written to each of
-//                  its kept destinations.
+//                  its kept destinations.  Without X_perm (a grouped FFN
+//                  that gathers its rows through the inverse map) K3 is
+//                  one thread per copy and copies nothing.
 //
 // Few copies (T*k <= kSmallCopies): one kernel.  Every workgroup ranks all
 // copies itself (one copy per lane, 256 per round, token-major), so no
@@ -209,6 +211,24 @@ __global__ __launch_bounds__(256) void scatter_kernel(
   }
 }
 
+// K3 without the row copy: one thread per copy (t, j).
+__global__ __launch_bounds__(256) void assign_kernel(
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ local_rank,
+    const int32_t* __restrict__ block_base, const int32_t* __restrict__ offsets, int T,
+    int E, int k, int C, int32_t* __restrict__ dest_row, int32_t* __restrict__ row_token) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= (int64_t)T * k) return;
+  const int t = (int)(q / k);
+  const int e = topk_idx[q];
+  const int rank = block_base[(int64_t)(t / kPermThreads) * E + e] + local_rank[q];
+  int dest = -1;
+  if (rank < C) {
+    dest = offsets[e] + rank;
+    row_token[dest] = t;
+  }
+  dest_row[q] = dest;
+}
+
 constexpr int kSmallCopies = 2048;
 
 __global__ __launch_bounds__(256) void permute_small_kernel(
@@ -303,6 +323,7 @@ __global__ __launch_bounds__(256) void permute_small_kernel(
   }
 
   // X rows of this workgroup's tokens, one wavefront per (token, slot)
+  if (X_perm == nullptr) return;
   const int t0 = blockIdx.x * tok_per_block;
   const int nq = min(tok_per_block, T - t0) * k;
   for (int i = wave; i < nq; i += 4) {
@@ -331,6 +352,12 @@ hipError_t launch_k(const void* X, bool x_bf16, const int32_t* topk_idx, int T,
                                      mt_prefix, tile_code);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (X_perm == nullptr) {
+    const int64_t n = (int64_t)T * k;
+    assign_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(
+        topk_idx, local_rank, block_counts, offsets, T, E, k, C, dest_row, row_token);
+    return hipGetLastError();
+  }
   const int row_chunks = d * (x_bf16 ? 2 : 4) / 16;
   constexpr int kTokPerBlock = 4;
   scatter_kernel<KMAX><<<(T + kTokPerBlock - 1) / kTokPerBlock, kTokPerBlock * kWave, 0, stream>>>(
@@ -364,7 +391,9 @@ hipError_t launch_permute(const void* X, bool x_bf16, const int32_t* topk_idx,
   }
   if ((int64_t)T * k <= kSmallCopies) {
     const int row_chunks = d * (x_bf16 ? 2 : 4) / 16;
-    const int tpb = (T + 255) / 256;  // tokens per workgroup: at most 256 workgroups
+    // tokens per workgroup: at most 256 workgroups; one when no row is copied
+    // (workgroup 0 publishes everything else)
+    const int tpb = X_perm == nullptr ? T : (T + 255) / 256;
     permute_small_kernel<<<(unsigned)((T + tpb - 1) / tpb), 256, 0, stream>>>(
         static_cast<const i32x4*>(X), topk_idx, T, E, k, C, row_chunks, tpb, counts,
         offsets, dropped, dest_row, row_token, static_cast<i32x4*>(X_perm), mt_prefix, tile_code);

@@ -50,8 +50,14 @@ def test_workspace_sizes_cover_the_intermediates():
     p = B.problem(4096, 7168, 256, 8, 2048, 0.0, "bf16", 1)
     R = B.rows_bound(p)
     ws = B.workspace_bytes(p)
-    # X_perm (bf16) + H (bf16) + Y_perm (fp32) at least
-    assert ws >= R * 7168 * 2 + R * 2048 * 2 + R * 7168 * 4
+    # bf16: H (bf16) + Y_perm (fp32) at least; the FFN gathers the rows of X,
+    # so no permuted copy of X is kept
+    assert ws >= R * 2048 * 2 + R * 7168 * 4
+    assert ws < R * 7168 * 2 + R * 2048 * 2 + R * 7168 * 4
+    # fp32 layers keep X_perm (fp32) + H (fp32) + Y_perm (fp32)
+    pf = B.problem(64, 256, 8, 2, 128, 0.0, "f32")
+    Rf = B.rows_bound(pf)
+    assert B.workspace_bytes(pf) >= Rf * 256 * 4 + Rf * 128 * 4 + Rf * 256 * 4
     assert B.grouped_ffn_workspace_bytes(p) >= R * 2048 * 2
     assert B.permute_workspace_bytes(p) >= 4096 * 8 * 4
     assert ws % 256 == 0
@@ -120,6 +126,31 @@ def test_null_pointers_and_small_workspace_rejected():
     r = lib.moe_grouped_ffn(ctypes.byref(p), fake, fake, fake, fake, fake,
                             fake, fake, need - 1, None)
     assert r == B.MOE_ERR_WORKSPACE
+
+
+def test_grouped_ffn_rows_arguments_checked_on_the_host():
+    lib = B.load()
+    fake = ctypes.c_void_p(0x1000)
+    p = B.problem(8, 64, 4, 2, 64)
+    need = lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(p))
+    args = lambda **kw: [kw.get(n, fake) for n in  # noqa: E731
+                         ("X", "rt", "off", "wg", "wu", "wd")]
+    call = lambda p, a, sc, ws: lib.moe_grouped_ffn_rows(  # noqa: E731
+        ctypes.byref(p), *a, sc, fake, fake, ws, None)
+    assert call(p, args(), None, need - 1) == B.MOE_ERR_WORKSPACE
+    assert call(p, args(rt=None), None, need) == B.MOE_ERR_INVALID_ARG
+    assert call(p, args(X=None), None, need) == B.MOE_ERR_INVALID_ARG
+    # scales only with FP8 weights, and then required
+    assert call(p, args(), fake, need) == B.MOE_ERR_INVALID_ARG
+    p8 = B.problem(8, 64, 4, 2, 64, w_dtype="fp8")
+    need8 = lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(p8))
+    assert call(p8, args(), None, need8) == B.MOE_ERR_INVALID_ARG
+    # fp32 layers keep X_perm: unsupported here
+    pf = B.problem(8, 64, 4, 2, 64, 0.0, "f32")
+    assert call(pf, args(), None, 1 << 40) == B.MOE_ERR_UNSUPPORTED
+    # X beyond one 32-bit buffer range
+    pb = B.problem(1 << 18, 4096, 8, 2, 64)
+    assert call(pb, args(), None, 1 << 50) == B.MOE_ERR_UNSUPPORTED
 
 
 def test_shared_expert_arguments_checked_on_the_host():
