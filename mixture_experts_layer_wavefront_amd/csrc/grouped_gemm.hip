@@ -902,47 +902,96 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
 }
 
 // ---- fp32 path (plain FMA; for fp32 layers, which are small) ---------------
-__device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int r) {
-  int lo = 0, hi = E;  // offsets[lo] <= r < offsets[hi]
+// fp32 layers: the grouped FFN with fp32 FMAs (no fp32 matrix path is worth
+// the fixed cost at the sizes fp32 layers run at).  One workgroup per 64 x 64
+// output tile of one expert's rows (tile schedule: mt_prefix with 64-row
+// tiles), K staged through the LDS 16 at a time; each of the 256 threads
+// holds a 4 x 4 block of outputs (gate/up: of both projections, SwiGLU
+// applied before the one store of H).  A [R, K] fp32 rows by expert; B0/B1
+// [E, N, K] fp32; C [R, N] fp32.  K is a multiple of 4 (rows of 16 bytes).
+constexpr int kF32Tile = 64;
+template <bool GATEUP>
+__global__ __launch_bounds__(256) void ffn_f32_tile_kernel(
+    const float* __restrict__ A, const float* __restrict__ B0, const float* __restrict__ B1,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ mt_prefix, int E, int N,
+    int K, float* __restrict__ C) {
+  constexpr int BM = kF32Tile, BN = kF32Tile, BK = 16, NBM = GATEUP ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) float sA[BK][BM + 4];
+  __shared__ __attribute__((aligned(16))) float sB[NBM][BK][BN + 4];
+  __shared__ int32_t s_pref[257];
+  const int tid = threadIdx.x;
+  for (int i = tid; i <= E; i += 256) s_pref[i] = mt_prefix[i];
+  __syncthreads();
+  const int n_nt = (N + BN - 1) / BN;
+  const int tile = blockIdx.x;
+  if (tile >= s_pref[E] * n_nt) return;
+  int lo = 0, hi = E;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (offsets[mid] <= r) lo = mid; else hi = mid;
+    if (s_pref[mid] * n_nt <= tile) lo = mid; else hi = mid;
   }
-  return lo;
-}
+  const int e = lo;
+  const int local = tile - s_pref[e] * n_nt;
+  const int m_t = local / n_nt, n_t = local - m_t * n_nt;  // the N-tiles of an M-tile in a row
+  const int m_start = offsets[e] + m_t * BM;
+  const int rows = min(BM, offsets[e + 1] - m_start);
+  const int n0 = n_t * BN;
+  const int ncols = min(BN, N - n0);
 
-__global__ __launch_bounds__(256) void ffn_f32_gateup_kernel(
-    const float* __restrict__ Xp, const float* __restrict__ Wg,
-    const float* __restrict__ Wu, const int32_t* __restrict__ offsets, int E,
-    int d, int dff, float* __restrict__ H) {
-  const int r = blockIdx.y;
-  const int n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= offsets[E] || n >= dff) return;
-  const int e = expert_of_row(offsets, E, r);
-  const float* x = Xp + (int64_t)r * d;
-  const float* wg = Wg + ((int64_t)e * dff + n) * d;
-  const float* wu = Wu + ((int64_t)e * dff + n) * d;
-  float g = 0.f, u = 0.f;
-  for (int i = 0; i < d; ++i) {
-    g = fmaf(x[i], wg[i], g);
-    u = fmaf(x[i], wu[i], u);
+  // loads: thread -> (row or column tid / 4, four k from (tid % 4) * 4)
+  const int lr = tid / 4, lk = (tid % 4) * 4;
+  const float* a_row = A + (int64_t)(m_start + lr) * K + lk;
+  const float* b_row0 = B0 + ((int64_t)e * N + n0 + lr) * K + lk;
+  const float* b_row1 = GATEUP ? B1 + ((int64_t)e * N + n0 + lr) * K + lk : nullptr;
+  const int ty = tid / 16, tx = tid % 16;  // outputs rows 4 ty.., columns 4 tx..
+  float acc[NBM][4][4];
+#pragma unroll
+  for (int b = 0; b < NBM; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[b][i][j] = 0.f;
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    const bool kin = k0 + lk < K;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 va = (kin && lr < rows) ? *reinterpret_cast<const f32x4*>(a_row + k0) : z;
+    const f32x4 vb0 = (kin && lr < ncols) ? *reinterpret_cast<const f32x4*>(b_row0 + k0) : z;
+    f32x4 vb1 = z;
+    if constexpr (GATEUP) vb1 = (kin && lr < ncols) ? *reinterpret_cast<const f32x4*>(b_row1 + k0) : z;
+    __syncthreads();  // the previous step's reads are done
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sA[lk + i][lr] = va[i];
+      sB[0][lk + i][lr] = vb0[i];
+      if constexpr (GATEUP) sB[1][lk + i][lr] = vb1[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&sA[kk][4 * ty]);
+#pragma unroll
+      for (int b = 0; b < NBM; ++b) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(&sB[b][kk][4 * tx]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[b][i][j] = fmaf(a[i], w[j], acc[b][i][j]);
+      }
+    }
   }
-  H[(int64_t)r * dff + n] = g / (1.f + expf(-g)) * u;
-}
-
-__global__ __launch_bounds__(256) void ffn_f32_down_kernel(
-    const float* __restrict__ H, const float* __restrict__ Wd,
-    const int32_t* __restrict__ offsets, int E, int d, int dff,
-    float* __restrict__ Y) {
-  const int r = blockIdx.y;
-  const int n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= offsets[E] || n >= d) return;
-  const int e = expert_of_row(offsets, E, r);
-  const float* h = H + (int64_t)r * dff;
-  const float* w = Wd + ((int64_t)e * d + n) * dff;
-  float y = 0.f;
-  for (int i = 0; i < dff; ++i) y = fmaf(h[i], w[i], y);
-  Y[(int64_t)r * d + n] = y;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * ty + i;
+    if (r >= rows) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 4 * tx + j;
+      if (c >= ncols) continue;
+      float v = acc[0][i][j];
+      if constexpr (GATEUP) v = v / (1.f + expf(-v)) * acc[NBM - 1][i][j];
+      C[(int64_t)(m_start + r) * N + n0 + c] = v;
+    }
+  }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -1072,7 +1121,7 @@ int ffn_tile_code(bool bf16, int rows_per_expert, bool fp8) {
 }
 
 int ffn_tile_rows(bool bf16, int rows_per_expert, bool fp8) {
-  if (!bf16) return 0;
+  if (!bf16) return kF32Tile;
   if (rows_per_expert <= 64) return 32;
   if (fp8) return rows_per_expert <= 512 ? 128 : 256;
   return rows_per_expert <= kStreamRows ? kStreamRows : 256;
@@ -1112,15 +1161,24 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
   if (gather != nullptr && (!bf16 || (int64_t)gather_rows * d * 2 > INT32_MAX))
     return hipErrorInvalidValue;  // gathered rows: bf16, one 32-bit buffer range
   if (!bf16) {
-    const dim3 g1((d_ff + 255) / 256, (unsigned)R), g2((d + 255) / 256, (unsigned)R);
-    ffn_f32_gateup_kernel<<<g1, 256, 0, stream>>>(
+    if (!prefix_ready) {
+      ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, kF32Tile, mt_prefix);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
+    // upper bound on 64-row tiles: every expert may add one partial tile
+    const int64_t mt_max = (R + kF32Tile - 1) / kF32Tile + std::min<int64_t>(E, R);
+    const int64_t g1 = mt_max * ((d_ff + kF32Tile - 1) / kF32Tile);
+    const int64_t g2 = mt_max * ((d + kF32Tile - 1) / kF32Tile);
+    if (g1 > 0x7fffffff || g2 > 0x7fffffff) return hipErrorInvalidValue;
+    ffn_f32_tile_kernel<true><<<(unsigned)g1, 256, 0, stream>>>(
         static_cast<const float*>(X_perm), static_cast<const float*>(W_gate),
-        static_cast<const float*>(W_up), offsets, E, d, d_ff, static_cast<float*>(H));
+        static_cast<const float*>(W_up), offsets, mt_prefix, E, d_ff, d, static_cast<float*>(H));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    ffn_f32_down_kernel<<<g2, 256, 0, stream>>>(static_cast<const float*>(H),
-                                                static_cast<const float*>(W_down),
-                                                offsets, E, d, d_ff, Y_perm);
+    ffn_f32_tile_kernel<false><<<(unsigned)g2, 256, 0, stream>>>(
+        static_cast<const float*>(H), static_cast<const float*>(W_down), nullptr, offsets,
+        mt_prefix, E, d, d_ff, Y_perm);
     return hipGetLastError();
   }
   hipError_t err;

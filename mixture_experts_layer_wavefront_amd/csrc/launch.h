@@ -34,8 +34,8 @@ hipError_t launch_permute(const void* X, bool x_bf16, const int32_t* topk_idx,
                           hipStream_t stream);
 
 // Grouped SwiGLU FFN.  `rows_per_expert` (the mean, known on the host from
-// the shape alone) picks the tile shape: ffn_tile_rows() rows per tile (0:
-// fp32 layers, no tile schedule).  The tile schedule (exclusive prefix over
+// the shape alone) picks the tile shape: ffn_tile_rows() rows per tile (64
+// for fp32 layers, whose FMA kernels take 64 x 64 tiles).  The tile schedule (exclusive prefix over
 // experts of their tile counts, E + 1 ints) lives at the start of `scratch`;
 // with prefix_ready the caller has already written it there.  w_scales !=
 // nullptr: the weights are FP8 E4M3 codes with scales [E, 3] (bf16 layers).

@@ -48,6 +48,11 @@ SMALL = {
     # 68, 14 and 6 rows; ten experts without rows): tall tiles next to
     # nearly empty ones, with a down projection in two K halves
     "skew16": WL("skew16", 3000, 264, 16, 2, 2112, W.BF16, TK, 0.0, 1.2, 21),
+    # fp32 layers on several 64 x 64 FMA tiles per expert: K tails (200 and
+    # 136 are not multiples of 16), N tails (136 = 2 x 64 + 8, 200 = 3 x 64
+    # + 8), ragged last M-tiles; then capacity drops with skew
+    "f32_tiles": WL("f32_tiles", 700, 200, 6, 2, 136, W.F32, TK, 0.0, 0.8, 22),
+    "f32_cap": WL("f32_cap", 500, 96, 16, 4, 72, W.F32, ST, 0.75, 1.2, 23),
 }
 
 
