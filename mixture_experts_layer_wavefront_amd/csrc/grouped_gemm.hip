@@ -50,6 +50,13 @@
 //    hardware's round-robin of workgroups over the 8 XCDs gives each XCD a
 //    contiguous run of tiles: the tiles sharing one expert's weights and
 //    rows share one L2.
+//  * Gathered rows (the forward's gate/up GEMM): row r of X_perm is read as
+//    row row_token[r] of X itself, so no permuted copy of the input is ever
+//    written.  A tile copies its rows' token ids into the LDS (those loads go
+//    out before the tile's first weight loads), and each A load of the K
+//    loop addresses its source row directly; results are bit-identical to
+//    reading X_perm.
+//  * fp32 layers run 64 x 64 FMA tiles on the same schedule.
 #include "common.h"
 
 #include <type_traits>
