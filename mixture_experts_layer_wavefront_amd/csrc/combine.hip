@@ -19,32 +19,38 @@
 namespace moe {
 namespace {
 
-constexpr int kTokPerBlock = 4;
+constexpr int kMaxWavesPerBlock = 4;
 constexpr int kColsPerWave = 8 * kWave;  // 8 columns per lane
 
-// One wavefront per (token, slice of kColsPerWave columns): blockIdx.x picks
-// kTokPerBlock tokens, blockIdx.y the column slice.  A slice is 128 chunks
-// of four fp32 columns; lane l owns chunks l and l + 64, so every load and
-// store instruction of the wave covers 1 KB of contiguous memory.  The k
+// One wavefront per (token, slice of kColsPerWave columns).  A workgroup
+// holds wpb consecutive slices of one token (wpb divides the slice count, so
+// no wave is idle), and consecutive workgroups walk a token's row before the
+// next token: the k source rows of a token are read whole, one after the
+// other, instead of one slice of many tokens' rows at a time (measured:
+// DeepSeek-V3 combine 200 -> 189 us, Qwen3 capacity 85 -> 67, Mixtral 40 ->
+// 37).  A slice is 128 chunks of four fp32 columns; lane l owns chunks l and
+// l + 64, so every load and store instruction of the wave covers 1 KB of
+// contiguous memory.  The k
 // source rows are read eight slots at a time (all loads issued before the
 // FMAs, which run in slot order); each source row is read once, past the
 // caches (non-temporal).  The token's destination rows and gate weights are
 // the same for the whole wavefront: scalar loads fetch them, so the row
 // loads start without a round trip through the LDS.
 template <bool OUT_BF16>
-__global__ __launch_bounds__(kTokPerBlock * kWave) void combine_kernel(
+__global__ __launch_bounds__(kMaxWavesPerBlock * kWave) void combine_kernel(
     const float* __restrict__ Y, const float* __restrict__ Y2,
     const int32_t* __restrict__ dest_row, const float* __restrict__ topk_w, int T, int d,
-    int k, const float* __restrict__ add_rows, void* __restrict__ out) {
+    int k, int groups, const float* __restrict__ add_rows, void* __restrict__ out) {
   const int lane = threadIdx.x % kWave;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int t = blockIdx.x * kTokPerBlock + wv;
+  const int t = blockIdx.x / groups;  // groups = slices per token / waves per block
+  const int slice = (blockIdx.x - t * groups) * (blockDim.x / kWave) + wv;
   if (t >= T) return;  // uniform per wavefront; no block-wide barrier below
   // the token's (row, weight) pairs: the same for the whole wavefront
   const int32_t* __restrict__ td = dest_row + (int64_t)t * k;
   const float* __restrict__ tw = topk_w + (int64_t)t * k;
   const int nq = d / 4;                                // chunks of 4 columns per row
-  const int q0 = blockIdx.y * (2 * kWave) + lane;      // this lane's chunks: q0, q1
+  const int q0 = slice * (2 * kWave) + lane;           // this lane's chunks: q0, q1
   const int q1 = q0 + kWave;
   if (q0 >= nq) return;
   const bool has1 = q1 < nq;
@@ -116,11 +122,16 @@ hipError_t launch_combine(const float* Y_perm, const int32_t* dest_row,
                           const float* add_rows, bool out_bf16, void* out,
                           hipStream_t stream, const float* Y_half) {
   if (T == 0) return hipSuccess;
-  const dim3 grid((T + kTokPerBlock - 1) / kTokPerBlock, (d + kColsPerWave - 1) / kColsPerWave);
+  const int nslices = (d + kColsPerWave - 1) / kColsPerWave;
+  int wpb = kMaxWavesPerBlock;  // waves per block: the largest divisor of the slice count
+  while (nslices % wpb != 0) --wpb;
+  const int groups = nslices / wpb;
+  const int64_t blocks = (int64_t)T * groups;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (out_bf16)
-    combine_kernel<true><<<grid, kTokPerBlock * kWave, 0, stream>>>(Y_perm, Y_half, dest_row, topk_w, T, d, k, add_rows, out);
+    combine_kernel<true><<<(unsigned)blocks, wpb * kWave, 0, stream>>>(Y_perm, Y_half, dest_row, topk_w, T, d, k, groups, add_rows, out);
   else
-    combine_kernel<false><<<grid, kTokPerBlock * kWave, 0, stream>>>(Y_perm, Y_half, dest_row, topk_w, T, d, k, add_rows, out);
+    combine_kernel<false><<<(unsigned)blocks, wpb * kWave, 0, stream>>>(Y_perm, Y_half, dest_row, topk_w, T, d, k, groups, add_rows, out);
   return hipGetLastError();
 }
 
