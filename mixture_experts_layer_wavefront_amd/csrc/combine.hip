@@ -27,8 +27,8 @@ constexpr int kColsPerWave = 8 * kWave;  // 8 columns per lane
 // no wave is idle), and consecutive workgroups walk a token's row before the
 // next token: the k source rows of a token are read whole, one after the
 // other, instead of one slice of many tokens' rows at a time (measured:
-// DeepSeek-V3 combine 200 -> 189 us, Qwen3 capacity 85 -> 67, Mixtral 40 ->
-// 37).  A slice is 128 chunks of four fp32 columns; lane l owns chunks l and
+// DeepSeek-V3 combine 199 -> 185 us, Qwen3 capacity 86 -> 68, gpt-oss 88 ->
+// 83, Mixtral 41 -> 37).  A slice is 128 chunks of four fp32 columns; lane l owns chunks l and
 // l + 64, so every load and store instruction of the wave covers 1 KB of
 // contiguous memory.  The k
 // source rows are read eight slots at a time (all loads issued before the
