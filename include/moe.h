@@ -10,8 +10,11 @@
  *   3. per-expert capacity slots (overflowing copies dropped)   -> moe_permute
  *   4. permute token copies into expert-contiguous order        -> moe_permute
  *   5. each expert's FFN on its rows, as one grouped GEMM       -> moe_grouped_ffn
+ *      (or moe_grouped_ffn_rows, which reads the rows from X through
+ *      the permute's row map instead of a permuted copy)
  *   6. un-permute and combine with the gate weights             -> moe_combine
- * moe_forward runs all of them.
+ * moe_forward runs all of them (bf16 layers: steps 3-4 assign rows without
+ * copying them, and step 5 reads them from X).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
