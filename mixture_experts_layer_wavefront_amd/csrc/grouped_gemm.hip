@@ -852,31 +852,12 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
           }
       }
     }
-  } else if constexpr (MODE == 3) {
-    float* C0 = static_cast<float*>(Cout);
-    float* C1 = static_cast<float*>(g.C1);
-    const int ms = g.msplit, M = g.M;
-#pragma unroll
-    for (int nj = 0; nj < TN; ++nj) {
-      const int col = wn * TN * 32 + nj * 32 + col_l;
-      if (col >= ncols) continue;
-#pragma unroll
-      for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = sub_row0(mi) + rlane + 8 * (r >> 2) + (r & 3);
-          if (row < rows) {
-            const int m = m_start + row;
-            float* dst = m < ms ? C0 + ((int64_t)e * ms + m) * N
-                                : C1 + ((int64_t)e * (M - ms) + (m - ms)) * N;
-            dst[n0 + col] = acc[mi][nj][r];
-          }
-        }
-    }
   } else {
     // fp32 results through the LDS as for H above: 32 x TN*32 fp32 per row
     // sub-tile (rows padded by 32 bytes), then 16-byte stores, 64 / (TN*8)
-    // rows of TN*128 contiguous bytes per instruction
+    // rows of TN*128 contiguous bytes per instruction.  Mode 3 (weight
+    // gradient): C row m of expert e goes to C [E, msplit, N] below msplit,
+    // else to C1 [E, M - msplit, N].
     constexpr int RS = TN * 128 + 32;
     constexpr int CPRW = TN * 8;
     constexpr int RPI = kWave / CPRW;
@@ -901,8 +882,17 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
         const int rl = r0 + rsub;
         const int row = sub_row0(mi) + rl;
         const f32x4 v = *reinterpret_cast<const f32x4*>(wreg + rl * RS + ch * 16);
-        if (row < rows && colc < ncols)
-          *reinterpret_cast<f32x4*>(Y + (int64_t)(m_start + row) * N + n0 + colc) = v;
+        if (row < rows && colc < ncols) {
+          float* drow;
+          if constexpr (MODE == 3) {
+            const int m = m_start + row, ms = g.msplit;
+            drow = m < ms ? Y + ((int64_t)e * ms + m) * N
+                          : static_cast<float*>(g.C1) + ((int64_t)e * (g.M - ms) + (m - ms)) * N;
+          } else {
+            drow = Y + (int64_t)(m_start + row) * N;
+          }
+          *reinterpret_cast<f32x4*>(drow + n0 + colc) = v;
+        }
       }
     }
   }
