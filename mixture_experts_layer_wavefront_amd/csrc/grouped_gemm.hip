@@ -857,7 +857,8 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
     // sub-tile (rows padded by 32 bytes), then 16-byte stores, 64 / (TN*8)
     // rows of TN*128 contiguous bytes per instruction.  Mode 3 (weight
     // gradient): C row m of expert e goes to C [E, msplit, N] below msplit,
-    // else to C1 [E, M - msplit, N].
+    // else to C1 [E, M - msplit, N], with non-temporal stores (measured:
+    // Mixtral backward 7.16 -> 7.0 ms, DeepSeek-V3 18.3 -> 16.9 ms).
     constexpr int RS = TN * 128 + 32;
     constexpr int CPRW = TN * 8;
     constexpr int RPI = kWave / CPRW;
@@ -891,7 +892,10 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
           } else {
             drow = Y + (int64_t)(m_start + row) * N;
           }
-          *reinterpret_cast<f32x4*>(drow + n0 + colc) = v;
+          if constexpr (MODE == 3)  // weight gradients are written once, not read back here
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(drow + n0 + colc));
+          else
+            *reinterpret_cast<f32x4*>(drow + n0 + colc) = v;
         }
       }
     }
