@@ -29,13 +29,21 @@
  *   This is the packed one-tensor-per-projection layout of "MoonEP의 계획
  *   코드를 직접 돌려봤습니다" (thakicloud.com), section "설치 및 통합".
  * - Ownership: the caller owns every buffer, including the workspace.  The
- *   library never allocates, frees or synchronises, and keeps no mutable
- *   global state (one exception: moe_forward_noalloc's fixed per-GPU
- *   scratch array).  Calls on distinct streams with distinct buffers and
- *   workspaces may run concurrently.
- * - Every call only enqueues kernels on `stream` and returns; no host
+ *   library never allocates device memory, frees or synchronises.  Global
+ *   state: moe_forward_noalloc's fixed per-GPU scratch array, and one side
+ *   stream with two events per GPU for grouped FFNs that run two classes of
+ *   experts (bf16 layers of at least 64 experts averaging more than 256 rows
+ *   each; see moe_grouped_ffn), made on the first such call that is not
+ *   inside a graph capture and kept until the process ends.  Calls on
+ *   distinct streams with distinct buffers and workspaces may run
+ *   concurrently.
+ * - Every call only enqueues work on `stream` and returns; no host
  *   synchronisation happens inside any call (no per-expert size is read
  *   back: the grouped GEMM schedules its tiles from device-side offsets).
+ *   Two-class grouped FFNs fork part of their work onto the side stream
+ *   after what `stream` holds and join it back into `stream` before they
+ *   return, so later work on `stream` sees every result and a graph capture
+ *   of the call holds both branches.
  * - Errors: arguments are validated on the host before anything is
  *   enqueued.  An invalid argument returns a negative status and writes
  *   nothing.  A failed launch returns MOE_ERR_HIP.  Faults inside kernels
@@ -174,7 +182,12 @@ moe_status_t moe_permute(const moe_problem_t* p, const void* X,
  *   Y[r] = (silu(X_perm[r] Wg_e^T) * (X_perm[r] Wu_e^T)) Wd_e^T
  * with silu(z) = z / (1 + exp(-z)).  bf16 inputs use bf16 MFMA with fp32
  * accumulation; the SwiGLU product is formed in fp32 and rounded once to
- * the act dtype.
+ * the act dtype.  With bf16 weights, at least 64 experts and more than 256
+ * rows per expert on average, each expert's tile height is chosen on the
+ * device from its row count (experts of at most 160 rows on 160-row tiles,
+ * on the library's side stream, beside the others' taller tiles); each
+ * row's sums run in the same order either way, so the result is the same
+ * bit pattern.
  *   X_perm         [R, d_model] act dtype
  *   expert_offsets [E+1] int32 (device; never read back to the host)
  *   Y_perm         [R, d_model] fp32 out (rows >= offsets[E] not written)

@@ -68,6 +68,10 @@ def load(path: str = LIB_PATH):
         raise RuntimeError(
             f"{path} is missing: build it with "
             "`python -m mixture_experts_layer_wavefront_amd.build`")
+    # torch first: the library then binds to the HIP runtime torch has loaded
+    # (loaded the other way round, a second runtime would own the library's
+    # launches and see none of torch's memory or streams)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER(Problem)
     vp, sz, st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p

@@ -36,17 +36,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
 // A byte offset that is always outside any buffer resource's range.
 constexpr uint32_t kOob = 0x80000000u;
 
-// Wave-wide reductions (64 lanes) via cross-lane shuffles.
 // M-tiles of an expert with `rows` rows under a tile code: tiles of
-// (code & 0xFFFF) rows, and a remainder of at most (code >> 16) rows joins
-// the last full tile instead of taking a tile of its own.
+// (code & 0xFFFF) rows, and a remainder of at most ((code >> 16) & 0xFF) rows
+// joins the last full tile instead of taking a tile of its own.  Bits 24-25
+// restrict a schedule to one class of experts, so that experts of few and of
+// many rows can run on tiles of different heights: kClassSmall keeps the
+// experts of at most kClassRows rows, kClassLarge the others; the experts of
+// the other class get no tile.
+constexpr int kClassRows = 160;
+constexpr int kClassSmall = 1 << 24;
+constexpr int kClassLarge = 2 << 24;
 constexpr int kTallTileCode = 256 | (64 << 16);
 __host__ __device__ __forceinline__ int m_tiles(int rows, int code) {
-  const int step = code & 0xFFFF, extra = code >> 16;
+  const int cls = (code >> 24) & 3;
+  if ((cls == 1 && rows > kClassRows) || (cls == 2 && rows <= kClassRows)) return 0;
+  const int step = code & 0xFFFF, extra = (code >> 16) & 0xFF;
   const int full = rows / step, rem = rows - full * step;
   return (rem == 0 || (full > 0 && rem <= extra)) ? full : full + 1;
 }
 
+// Wave-wide reductions (64 lanes) via cross-lane shuffles.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);

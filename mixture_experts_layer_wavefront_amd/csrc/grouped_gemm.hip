@@ -59,7 +59,10 @@
 //  * fp32 layers run 64 x 64 FMA tiles on the same schedule.
 #include "common.h"
 
+#include <algorithm>
+#include <mutex>
 #include <type_traits>
+
 #include "launch.h"
 
 namespace moe {
@@ -126,22 +129,36 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Tile schedule(s) from the expert offsets: mt_prefix [E + 1] under
+// tile_code and, when tile_code2 != 0, a second one under tile_code2 at
+// mt_prefix + E + 1.
 __global__ __launch_bounds__(256) void ffn_schedule_kernel(
     const int32_t* __restrict__ offsets, int E, int tile_code,
-    int32_t* __restrict__ mt_prefix) {
+    int32_t* __restrict__ mt_prefix, int tile_code2 = 0) {
   __shared__ int32_t s[256];
+  __shared__ int32_t s2[256];
   const int e = threadIdx.x;
-  const int mt = (e < E) ? m_tiles(offsets[e + 1] - offsets[e], tile_code) : 0;
+  const int rows = (e < E) ? offsets[e + 1] - offsets[e] : 0;
+  const int mt = (e < E) ? m_tiles(rows, tile_code) : 0;
+  const int mt2 = (e < E && tile_code2 != 0) ? m_tiles(rows, tile_code2) : 0;
   s[e] = mt;
+  s2[e] = mt2;
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {
     const int a = (e >= o) ? s[e - o] : 0;
+    const int b = (e >= o) ? s2[e - o] : 0;
     __syncthreads();
     s[e] += a;
+    s2[e] += b;
     __syncthreads();
   }
   if (e < E) mt_prefix[e] = s[e] - mt;
   if (e == E - 1) mt_prefix[E] = s[e];
+  if (tile_code2 != 0) {
+    int32_t* mt_prefix2 = mt_prefix + E + 1;
+    if (e < E) mt_prefix2[e] = s2[e] - mt2;
+    if (e == E - 1) mt_prefix2[E] = s2[e];
+  }
 }
 
 // Operand layouts.  "NT" (row-major along K): A [M][K], B [N][K]; a stage
@@ -999,9 +1016,12 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Modes 0-2: R = rows bound (grid upper bound).  Mode 3: a.M rows of C per
 // expert, every (expert, m-tile, n-tile) is a tile.
+// mt_cap >= 0: a tighter bound on the schedule's M-tiles than R gives (a
+// schedule of one class of experts).
 template <int MW, int NW, int TM, int TN, bool GATEUP, int BK, int NS, int BAUX, bool BF8,
           int MODE>
-hipError_t launch_gemm_args(const GemmArgs& a, int64_t R, hipStream_t stream) {
+hipError_t launch_gemm_args(const GemmArgs& a, int64_t R, hipStream_t stream,
+                            int64_t mt_cap = -1) {
   using Cfg = GemmCfg<MW, NW, TM, TN, GATEUP, BK, NS, BF8>;
   auto kern = grouped_gemm_kernel<MW, NW, TM, TN, GATEUP, BK, NS, BAUX, BF8, MODE>;
   static const hipError_t attr = hipFuncSetAttribute(
@@ -1015,7 +1035,8 @@ hipError_t launch_gemm_args(const GemmArgs& a, int64_t R, hipStream_t stream) {
   } else {
     // upper bound on M-tiles: every expert may add one partial tile
     constexpr int MSTEP = (TM == 5 && MW == 2) ? 256 : Cfg::BM;  // tall tiles step by 256 rows
-    const int64_t mt_max = (R + MSTEP - 1) / MSTEP + std::min<int64_t>(a.E, R);
+    int64_t mt_max = (R + MSTEP - 1) / MSTEP + std::min<int64_t>(a.E, R);
+    if (mt_cap >= 0) mt_max = std::min(mt_max, mt_cap);
     tiles = mt_max * n_nt * ((MODE == 4 || MODE == 5) ? 2 : 1);
   }
   const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
@@ -1032,7 +1053,7 @@ hipError_t launch_gemm(const void* A, const void* B0, const void* B1, int N,
                        int K, int E, int64_t R, const int32_t* offsets,
                        const int32_t* mt_prefix, void* C, hipStream_t stream,
                        const float* scales = nullptr, const int32_t* gather = nullptr,
-                       int gather_rows = 0) {
+                       int gather_rows = 0, int64_t mt_cap = -1) {
   GemmArgs a{};
   a.A = static_cast<const uint16_t*>(A);
   a.B0 = B0;
@@ -1048,10 +1069,10 @@ hipError_t launch_gemm(const void* A, const void* B0, const void* B1, int N,
     if (gather != nullptr) {
       a.gather = gather;
       a.gather_rows = gather_rows;
-      return launch_gemm_args<MW, NW, TM, TN, GATEUP, BK, NS, BAUX, BF8, 6>(a, R, stream);
+      return launch_gemm_args<MW, NW, TM, TN, GATEUP, BK, NS, BAUX, BF8, 6>(a, R, stream, mt_cap);
     }
   }
-  return launch_gemm_args<MW, NW, TM, TN, GATEUP, BK, NS, BAUX, BF8, 0>(a, R, stream);
+  return launch_gemm_args<MW, NW, TM, TN, GATEUP, BK, NS, BAUX, BF8, 0>(a, R, stream, mt_cap);
 }
 
 // Y[r] += Y2[r] for the kept rows r < offsets[E] (the two K halves of the
@@ -1077,10 +1098,11 @@ template <int MW, int NW, int TM, int TN, int BK, int NS, int BAUX, bool BF8>
 hipError_t launch_down(const void* H, const void* W_down, int d, int d_ff, int E, int64_t R,
                        const int32_t* offsets, const int32_t* mt_prefix, float* Y_perm,
                        float* Y_half, hipStream_t stream, const float* scales,
-                       bool defer = false) {
+                       bool defer = false, int64_t mt_cap = -1) {
   if (Y_half == nullptr)
     return launch_gemm<MW, NW, TM, TN, false, BK, NS, BAUX, BF8>(
-        H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream, scales);
+        H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream, scales, nullptr,
+        0, mt_cap);
   GemmArgs a{};
   a.A = static_cast<const uint16_t*>(H);
   a.B0 = W_down;
@@ -1094,12 +1116,36 @@ hipError_t launch_down(const void* H, const void* W_down, int d, int d_ff, int E
   a.scales = scales;
   a.lda = d_ff;
   a.ldb = d_ff;
-  hipError_t err = launch_gemm_args<MW, NW, TM, TN, false, BK, NS, BAUX, BF8, 5>(a, R, stream);
+  hipError_t err = launch_gemm_args<MW, NW, TM, TN, false, BK, NS, BAUX, BF8, 5>(a, R, stream,
+                                                                                 mt_cap);
   if (err != hipSuccess || defer) return err;  // defer: the caller adds the halves
   const int64_t n4 = R * d / 4;
   const unsigned grid = (unsigned)std::min<int64_t>((n4 + 255) / 256, 4096);
   ffn_add_halves_kernel<<<grid, 256, 0, stream>>>(Y_perm, Y_half, offsets, E, d);
   return hipGetLastError();
+}
+
+size_t prefix_bytes(int E) { return align256((size_t)2 * (E + 1) * 4); }
+
+// The side stream of the two-class grouped FFN and its fork and join events,
+// one set per device, made on first use and kept until the process ends.
+// g_side_mu also serialises the enqueueing of a fork ... join sequence, so
+// calls from several host threads do not interleave their event records.
+constexpr int kSideDevices = 64;
+constexpr int kTwoClassMinE = 64;  // measured: 128 experts gain, 32 do not
+struct SideStream {
+  hipStream_t stream;
+  hipEvent_t fork, join;
+  bool failed;
+};
+std::mutex g_side_mu;
+SideStream g_side[kSideDevices];
+
+// The set `side` belongs to (nullptr if it is not one of ours).
+const SideStream* side_of(hipStream_t side) {
+  for (int i = 0; i < kSideDevices; ++i)
+    if (side != nullptr && g_side[i].stream == side) return &g_side[i];
+  return nullptr;
 }
 
 }  // namespace
@@ -1116,9 +1162,52 @@ bool ffn_split_down(bool bf16, int E, int rows_per_expert, int d, int d_ff) {
   return tiles < 4 * 256 && rem != 0 && rem <= 128;
 }
 
-int ffn_tile_code(bool bf16, int rows_per_expert, bool fp8) {
+bool ffn_two_class(bool bf16, bool fp8, int E, int rows_per_expert, int d, int d_ff) {
+  // tall tiles (more than 256 rows per expert on average) over enough
+  // experts that capacity and routing skew leave many of them with few rows
+  return bf16 && !fp8 && E >= kTwoClassMinE && ffn_tile_rows(bf16, rows_per_expert, fp8) == 256 &&
+         rows_per_expert > kBntRows && !ffn_split_down(bf16, E, rows_per_expert, d, d_ff);
+}
+
+int ffn_tile_code(bool bf16, int rows_per_expert, bool fp8, bool two_class) {
+  if (two_class) return kStreamRows | kClassSmall;
   const int bm = ffn_tile_rows(bf16, rows_per_expert, fp8);
   return (bm == 256 && rows_per_expert > kBntRows) ? kTallTileCode : bm;
+}
+
+int ffn_tile_code2(bool two_class) { return two_class ? (kTallTileCode | kClassLarge) : 0; }
+
+hipStream_t ffn_side_stream(hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kSideDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream& r = g_side[dev];
+  if (r.stream == nullptr && !r.failed) {
+    // not while `stream` is being captured into a graph (creating a stream
+    // is not a capturable call); the next call outside a capture makes it
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+      (void)hipGetLastError();  // not left for a later launch check to find
+      return nullptr;
+    }
+    if (cs != hipStreamCaptureStatusNone) return nullptr;
+    hipStream_t s = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) == hipSuccess &&
+        hipEventCreateWithFlags(&f, hipEventDisableTiming) == hipSuccess &&
+        hipEventCreateWithFlags(&j, hipEventDisableTiming) == hipSuccess) {
+      r.stream = s;
+      r.fork = f;
+      r.join = j;
+    } else {
+      if (j) (void)hipEventDestroy(j);
+      if (f) (void)hipEventDestroy(f);
+      if (s) (void)hipStreamDestroy(s);
+      r.failed = true;  // one class from now on
+      (void)hipGetLastError();
+    }
+  }
+  return r.stream;
 }
 
 int ffn_tile_rows(bool bf16, int rows_per_expert, bool fp8) {
@@ -1136,12 +1225,12 @@ int ffn_train_tile_code(int rows_per_expert) {
 float* ffn_half_sums(void* scratch, int64_t R, int E, int d, int d_ff, bool bf16,
                      int rows_per_expert) {
   if (!ffn_split_down(bf16, E, rows_per_expert, d, d_ff)) return nullptr;
-  return reinterpret_cast<float*>(static_cast<char*>(scratch) + align256((size_t)(E + 1) * 4) +
+  return reinterpret_cast<float*>(static_cast<char*>(scratch) + prefix_bytes(E) +
                                   align256((size_t)R * d_ff * 2));
 }
 
 size_t ffn_scratch_bytes(int64_t R, int E, int d, int d_ff, bool bf16, int rows_per_expert) {
-  return align256((size_t)(E + 1) * 4) + align256((size_t)R * d_ff * (bf16 ? 2 : 4)) +
+  return prefix_bytes(E) + align256((size_t)R * d_ff * (bf16 ? 2 : 4)) +
          (ffn_split_down(bf16, E, rows_per_expert, d, d_ff) ? align256((size_t)R * d * 4) : 0);
 }
 
@@ -1151,13 +1240,13 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
                               int d, int E, int d_ff, int rows_per_expert,
                               float* Y_perm, void* scratch, bool prefix_ready,
                               hipStream_t stream, const float* w_scales, bool defer,
-                              const int32_t* gather, int gather_rows) {
+                              const int32_t* gather, int gather_rows, hipStream_t side) {
   const bool fp8 = w_scales != nullptr;
   const int bm = ffn_tile_rows(bf16, rows_per_expert, fp8);
   const bool small_m = bm == 32;
   if (R == 0) return hipSuccess;
   int32_t* mt_prefix = static_cast<int32_t*>(scratch);
-  void* H = static_cast<char*>(scratch) + align256((size_t)(E + 1) * 4);
+  void* H = static_cast<char*>(scratch) + prefix_bytes(E);
   float* Y_half = ffn_half_sums(scratch, R, E, d, d_ff, bf16, rows_per_expert);
   if (gather != nullptr && (!bf16 || (int64_t)gather_rows * d * 2 > INT32_MAX))
     return hipErrorInvalidValue;  // gathered rows: bf16, one 32-bit buffer range
@@ -1198,10 +1287,36 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
     if (err != hipSuccess) return err;
     return launch_gemm<1, kSNW, 1, 1, false, kSBK, kSNS, kSBAUX>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream);
   }
-  const int code = ffn_tile_code(bf16, rows_per_expert, fp8);
+  const bool two = side != nullptr && ffn_two_class(bf16, fp8, E, rows_per_expert, d, d_ff);
+  const int code = ffn_tile_code(bf16, rows_per_expert, fp8, two);
   if (!prefix_ready) {
-    ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, code, mt_prefix);
+    ffn_schedule_kernel<<<1, 256, 0, stream>>>(offsets, E, code, mt_prefix, ffn_tile_code2(two));
     if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (two) {
+    // Experts of at most kClassRows rows (schedule mt_prefix) on 160-row
+    // tiles that stream their weights three stages deep, on the side stream;
+    // the others (schedule mt_prefix + E + 1) on tall tiles on `stream`.  The
+    // two launches share the CUs, so neither waits for the other's last
+    // round.  Each expert's rows take the same K order on either tile, so the
+    // results equal the one-class launch's bit for bit.
+    const int32_t* pre_big = mt_prefix + E + 1;
+    const int64_t cap_small = std::min<int64_t>(E, R);  // at most one 160-row tile each
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    const SideStream* ss = side_of(side);
+    if (ss == nullptr) return hipErrorInvalidValue;
+    if ((err = hipEventRecord(ss->fork, stream)) != hipSuccess) return err;
+    if ((err = hipStreamWaitEvent(side, ss->fork, 0)) != hipSuccess) return err;
+    err = launch_gemm<2, kNW, 5, 4 / kNW, true, kBK, 2, 0>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, pre_big, H, stream, nullptr, gather, gather_rows);
+    if (err != hipSuccess) return err;
+    err = launch_gemm<1, 4, 5, 1, true, kBK, 3, kNonTemporal>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, side, nullptr, gather, gather_rows, cap_small);
+    if (err != hipSuccess) return err;
+    err = launch_down<2, kNW, 5, kDTN / kNW, kBK, 2, 0, false>(H, W_down, d, d_ff, E, R, offsets, pre_big, Y_perm, nullptr, stream, nullptr);
+    if (err != hipSuccess) return err;
+    err = launch_down<1, 4, 5, 2, kBK, 3, kNonTemporal, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, nullptr, side, nullptr, false, cap_small);
+    if (err != hipSuccess) return err;
+    if ((err = hipEventRecord(ss->join, side)) != hipSuccess) return err;
+    return hipStreamWaitEvent(stream, ss->join, 0);
   }
   if (fp8 && bm == 128) {
     // FP8 weights, up to a few hundred rows per expert: 128-row tiles and

@@ -24,20 +24,22 @@ hipError_t launch_route(const void* X, bool x_bf16, const float* W_r,
 // copies).  With mt_prefix != nullptr it also writes the grouped FFN's tile
 // schedule: M-tiles per expert under tile_code (m_tiles; see launch_grouped_ffn).
 // X_perm == nullptr: no row is copied (dest_row and row_token only, for a
-// grouped FFN that gathers its input rows through row_token).
+// grouped FFN that gathers its input rows through row_token).  tile_code2 !=
+// 0: a second schedule under it at mt_prefix + E + 1 (the two-class FFN).
 size_t permute_scratch_bytes(int T, int k, int E);
 hipError_t launch_permute(const void* X, bool x_bf16, const int32_t* topk_idx,
                           int T, int d, int E, int k, int C,
                           int32_t* counts, int32_t* offsets, int32_t* dropped,
                           int32_t* dest_row, int32_t* row_token, void* X_perm,
                           void* scratch, int32_t* mt_prefix, int tile_code,
-                          hipStream_t stream);
+                          hipStream_t stream, int tile_code2 = 0);
 
 // Grouped SwiGLU FFN.  `rows_per_expert` (the mean, known on the host from
 // the shape alone) picks the tile shape: ffn_tile_rows() rows per tile (64
-// for fp32 layers, whose FMA kernels take 64 x 64 tiles).  The tile schedule (exclusive prefix over
-// experts of their tile counts, E + 1 ints) lives at the start of `scratch`;
-// with prefix_ready the caller has already written it there.  w_scales !=
+// for fp32 layers, whose FMA kernels take 64 x 64 tiles).  The tile schedule
+// (exclusive prefix over experts of their tile counts, E + 1 ints; a region
+// of 2 (E + 1) ints) lives at the start of `scratch`; with prefix_ready the
+// caller has already written it there.  w_scales !=
 // nullptr: the weights are FP8 E4M3 codes with scales [E, 3] (bf16 layers).
 // The down projection runs as two K halves (their sums added afterwards) for
 // shapes whose 256 x 256 tiles fill the chip only a few times; the second
@@ -45,11 +47,26 @@ hipError_t launch_permute(const void* X, bool x_bf16, const int32_t* topk_idx,
 // layers, gather_rows * d * 2 < 2^31): X_perm is the layer's input X itself
 // ([gather_rows, d]) and row r of the expert-grouped order is its row
 // gather[r] (the permute's row_token), so the permuted copy is never made.
+// side != nullptr (from ffn_side_stream) and ffn_two_class: the experts run
+// in two classes, the few-row one on `side` (forked from and joined back
+// into `stream`); the schedule region holds two prefixes, 2 (E + 1) ints.
 int ffn_tile_rows(bool bf16, int rows_per_expert, bool fp8 = false);
 // The M-tile code of moe_forward's grouped FFN (m_tiles): ffn_tile_rows, or
 // 256-row tiles that take remainders of up to 64 rows (256-row tiles with
-// more than 256 rows per expert, bf16 or FP8 weights).
-int ffn_tile_code(bool bf16, int rows_per_expert, bool fp8 = false);
+// more than 256 rows per expert, bf16 or FP8 weights).  With two_class: the
+// schedule of the experts of at most kClassRows rows on 160-row tiles, and
+// ffn_tile_code2 that of the others on tall tiles (0: no second schedule).
+int ffn_tile_code(bool bf16, int rows_per_expert, bool fp8 = false, bool two_class = false);
+int ffn_tile_code2(bool two_class);
+// Whether the shape runs the grouped FFN in two classes of experts (tall
+// tiles over at least 64 experts): the experts' rows decide each expert's
+// class on the device, the few-row class runs on a side stream beside the
+// other (ffn_side_stream).
+bool ffn_two_class(bool bf16, bool fp8, int E, int rows_per_expert, int d, int d_ff);
+// The library's side stream for the current device (made on the first call
+// that is not inside a graph capture of `stream`, kept until the process
+// ends), or nullptr where there is none: then the FFN runs in one class.
+hipStream_t ffn_side_stream(hipStream_t stream);
 // The M-tile code of the training forward's and the backward's GEMMs (their
 // own tile shapes: 32-row, 256-row or tall tiles).
 int ffn_train_tile_code(int rows_per_expert);
@@ -62,7 +79,7 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
                               float* Y_perm, void* scratch, bool prefix_ready,
                               hipStream_t stream, const float* w_scales = nullptr,
                               bool defer_half_sum = false, const int32_t* gather = nullptr,
-                              int gather_rows = 0);
+                              int gather_rows = 0, hipStream_t side = nullptr);
 
 // Where a split down projection leaves its second K half (inside `scratch`),
 // or nullptr when it is not split.

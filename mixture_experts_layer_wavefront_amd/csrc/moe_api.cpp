@@ -135,11 +135,14 @@ struct RoutedOut {
   float* y_half;  // second K half of a split down projection (the combine adds it), or null
 };
 
+// side_ok: the grouped FFN may run its two classes of experts concurrently on
+// the library's side stream (not for moe_forward_noalloc, which makes no
+// stream).
 hipError_t enqueue_routed(const moe_problem_t* p, const void* X, const float* W_r,
                           const float* bias, const void* W_gate, const void* W_up,
                           const void* W_down, int32_t* stats, float* router_stats,
                           char* ws, const ForwardLayout& L, hipStream_t stream,
-                          RoutedOut* r, const float* w_scales = nullptr) {
+                          RoutedOut* r, const float* w_scales = nullptr, bool side_ok = true) {
   int32_t* topk_idx = reinterpret_cast<int32_t*>(ws + L.topk_idx);
   float* topk_w = reinterpret_cast<float*>(ws + L.topk_w);
   int32_t* st_buf = stats ? stats : reinterpret_cast<int32_t*>(ws + L.stats);
@@ -159,29 +162,43 @@ hipError_t enqueue_routed(const moe_problem_t* p, const void* X, const float* W_
                                    (int)p->gating, topk_idx, topk_w, ws + L.route_scratch,
                                    router_stats, stream);
   if (e != hipSuccess) return e;
-  // the permute also writes the FFN's tile schedule (start of its scratch)
-  const int bm = moe::ffn_tile_code(bf, mean_rows_per_expert(p), w_scales != nullptr);
+  // the permute also writes the FFN's tile schedule(s) (start of its scratch)
+  const int rows = mean_rows_per_expert(p);
+  const bool fp8 = w_scales != nullptr;
+  hipStream_t side = (side_ok && moe::ffn_two_class(bf, fp8, p->E, rows, p->d_model, p->d_ff))
+                         ? moe::ffn_side_stream(stream)
+                         : nullptr;
+  const int bm = moe::ffn_tile_code(bf, rows, fp8, side != nullptr);
   int32_t* mt_prefix = bm > 0 ? reinterpret_cast<int32_t*>(ws + L.ffn_scratch) : nullptr;
   const bool gather = gather_input(p);
   e = moe::launch_permute(X, bf, topk_idx, p->T, p->d_model, p->E, p->top_k,
                           capacity_int(p), counts, offsets, dropped, dest_row, row_token,
-                          gather ? nullptr : x_perm, ws + L.perm_scratch, mt_prefix, bm, stream);
+                          gather ? nullptr : x_perm, ws + L.perm_scratch, mt_prefix, bm, stream,
+                          moe::ffn_tile_code2(side != nullptr));
   if (e != hipSuccess) return e;
   return moe::launch_grouped_ffn(gather ? X : x_perm, bf, offsets, W_gate, W_up, W_down,
-                                 moe_rows_bound(p), p->d_model, p->E, p->d_ff,
-                                 mean_rows_per_expert(p), y_perm, ws + L.ffn_scratch,
-                                 mt_prefix != nullptr, stream, w_scales,
-                                 /*defer_half_sum=*/true, gather ? row_token : nullptr, p->T);
+                                 moe_rows_bound(p), p->d_model, p->E, p->d_ff, rows, y_perm,
+                                 ws + L.ffn_scratch, mt_prefix != nullptr, stream, w_scales,
+                                 /*defer_half_sum=*/true, gather ? row_token : nullptr, p->T,
+                                 side);
+}
+
+// The side stream for a stage-level grouped FFN call on `stream` (nullptr:
+// one class of experts).
+hipStream_t ffn_side(const moe_problem_t* p, bool fp8, hipStream_t stream) {
+  return moe::ffn_two_class(is_bf16(p), fp8, p->E, mean_rows_per_expert(p), p->d_model, p->d_ff)
+             ? moe::ffn_side_stream(stream)
+             : nullptr;
 }
 
 // The whole layer with its intermediates carved from `ws` (L.total bytes).
 moe_status_t enqueue_forward(const moe_problem_t* p, const void* X, const float* W_r,
                              const float* bias, const void* W_gate, const void* W_up,
                              const void* W_down, void* out, int32_t* stats, char* ws,
-                             const ForwardLayout& L, hipStream_t stream) {
+                             const ForwardLayout& L, hipStream_t stream, bool side_ok = true) {
   RoutedOut r{};
   hipError_t e = enqueue_routed(p, X, W_r, bias, W_gate, W_up, W_down, stats, nullptr, ws, L,
-                                stream, &r);
+                                stream, &r, nullptr, side_ok);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_combine(r.y_perm, r.dest_row, r.topk_w, p->T, p->d_model, p->top_k,
                           nullptr, out_bf16(p), out, stream, r.y_half);
@@ -385,7 +402,8 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* X_perm,
   return hip_status(moe::launch_grouped_ffn(X_perm, is_bf16(p), expert_offsets, W_gate, W_up,
                                             W_down, R, p->d_model, p->E, p->d_ff,
                                             mean_rows_per_expert(p), Y_perm, workspace, false,
-                                            stream));
+                                            stream, nullptr, false, nullptr, 0,
+                                            ffn_side(p, false, stream)));
 }
 
 moe_status_t moe_grouped_ffn_rows(const moe_problem_t* p, const void* X,
@@ -405,7 +423,8 @@ moe_status_t moe_grouped_ffn_rows(const moe_problem_t* p, const void* X,
   return hip_status(moe::launch_grouped_ffn(X, true, expert_offsets, W_gate, W_up, W_down, R,
                                             p->d_model, p->E, p->d_ff,
                                             mean_rows_per_expert(p), Y_perm, workspace, false,
-                                            stream, w_scales, false, row_token, p->T));
+                                            stream, w_scales, false, row_token, p->T,
+                                            ffn_side(p, w_scales != nullptr, stream)));
 }
 
 moe_status_t moe_combine(const moe_problem_t* p, const float* Y_perm,
@@ -445,7 +464,8 @@ moe_status_t moe_forward_noalloc(const moe_problem_t* p, const void* X, const fl
   if (L.total > kScratchBytes) return MOE_ERR_SCRATCH_LIMIT;
   char* ws = nullptr;
   if (scratch_address(&ws) != hipSuccess) return MOE_ERR_HIP;
-  return enqueue_forward(p, X, W_r, bias, W_gate, W_up, W_down, out, stats, ws, L, stream);
+  return enqueue_forward(p, X, W_r, bias, W_gate, W_up, W_down, out, stats, ws, L, stream,
+                         /*side_ok=*/false);
 }
 
 size_t moe_forward_stats_workspace_bytes(const moe_problem_t* p) {

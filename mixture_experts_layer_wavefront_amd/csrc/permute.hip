@@ -114,10 +114,12 @@ __global__ __launch_bounds__(kPermThreads) void count_rank_kernel(
 __global__ __launch_bounds__(256) void scan_kernel(
     int32_t* __restrict__ block_counts, int nblk, int E, int C,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ dropped, int32_t* __restrict__ mt_prefix, int tile_code) {
+    int32_t* __restrict__ dropped, int32_t* __restrict__ mt_prefix, int tile_code,
+    int tile_code2) {
   __shared__ int32_t s_kept[256];
   __shared__ int32_t s_drop[256];
   __shared__ int32_t s_mt[256];
+  __shared__ int32_t s_mt2[256];
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
@@ -137,29 +139,37 @@ __global__ __launch_bounds__(256) void scan_kernel(
   }
   const int kept = (e < E) ? min(run, C) : 0;
   const int mt = (mt_prefix != nullptr) ? m_tiles(kept, tile_code) : 0;
+  const int mt2 = (mt_prefix != nullptr && tile_code2 != 0) ? m_tiles(kept, tile_code2) : 0;
   s_kept[e] = kept;
   s_drop[e] = (e < E) ? run - kept : 0;
   s_mt[e] = mt;
+  s_mt2[e] = mt2;
   __syncthreads();
   // inclusive Hillis-Steele scan over 256 entries
   for (int o = 1; o < 256; o <<= 1) {
     const int a = (e >= o) ? s_kept[e - o] : 0;
     const int b = (e >= o) ? s_drop[e - o] : 0;
     const int c = (e >= o) ? s_mt[e - o] : 0;
+    const int c2 = (e >= o) ? s_mt2[e - o] : 0;
     __syncthreads();
     s_kept[e] += a;
     s_drop[e] += b;
     s_mt[e] += c;
+    s_mt2[e] += c2;
     __syncthreads();
   }
+  // the second schedule (tile_code2 != 0) follows the first: mt_prefix + E + 1
+  int32_t* mt_prefix2 = (mt_prefix != nullptr && tile_code2 != 0) ? mt_prefix + E + 1 : nullptr;
   if (e < E) {
     counts[e] = run;
     offsets[e] = s_kept[e] - kept;
     if (mt_prefix != nullptr) mt_prefix[e] = s_mt[e] - mt;
+    if (mt_prefix2 != nullptr) mt_prefix2[e] = s_mt2[e] - mt2;
     if (e == E - 1) {
       offsets[E] = s_kept[e];
       dropped[0] = s_drop[e];
       if (mt_prefix != nullptr) mt_prefix[E] = s_mt[e];
+      if (mt_prefix2 != nullptr) mt_prefix2[E] = s_mt2[e];
     }
   }
 }
@@ -236,9 +246,11 @@ __global__ __launch_bounds__(256) void permute_small_kernel(
     int k, int C, int row_chunks, int tok_per_block, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ dropped,
     int32_t* __restrict__ dest_row, int32_t* __restrict__ row_token,
-    i32x4* __restrict__ X_perm, int32_t* __restrict__ mt_prefix, int tile_code) {
+    i32x4* __restrict__ X_perm, int32_t* __restrict__ mt_prefix, int tile_code,
+    int tile_code2) {
   __shared__ int32_t s_run[256];        // copies of each expert ranked so far
   __shared__ int32_t s_mt[256];         // M-tiles per expert (m_tiles)
+  __shared__ int32_t s_mt2[256];        // the same under tile_code2
   __shared__ int32_t s_wcnt[4][256];    // per-wave copies of each expert in a round
   __shared__ int32_t s_off[256];        // kept-row offsets
   __shared__ int32_t s_drop[256];
@@ -285,20 +297,25 @@ __global__ __launch_bounds__(256) void permute_small_kernel(
   const int cnt = (tid < E) ? s_run[tid] : 0;
   const int kept = min(cnt, C);
   const int mt = (mt_prefix != nullptr) ? m_tiles(kept, tile_code) : 0;
+  const int mt2 = (mt_prefix != nullptr && tile_code2 != 0) ? m_tiles(kept, tile_code2) : 0;
   s_off[tid] = kept;
   s_drop[tid] = cnt - kept;
   s_mt[tid] = mt;
+  s_mt2[tid] = mt2;
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {
     const int a = (tid >= o) ? s_off[tid - o] : 0;
     const int b = (tid >= o) ? s_drop[tid - o] : 0;
     const int c = (tid >= o) ? s_mt[tid - o] : 0;
+    const int c2 = (tid >= o) ? s_mt2[tid - o] : 0;
     __syncthreads();
     s_off[tid] += a;
     s_drop[tid] += b;
     s_mt[tid] += c;
+    s_mt2[tid] += c2;
     __syncthreads();
   }
+  int32_t* mt_prefix2 = (mt_prefix != nullptr && tile_code2 != 0) ? mt_prefix + E + 1 : nullptr;
   const int incl = s_off[tid];
   __syncthreads();
   s_off[tid] = incl - kept;  // exclusive
@@ -308,11 +325,13 @@ __global__ __launch_bounds__(256) void permute_small_kernel(
       counts[tid] = cnt;
       offsets[tid] = s_off[tid];
       if (mt_prefix != nullptr) mt_prefix[tid] = s_mt[tid] - mt;
+      if (mt_prefix2 != nullptr) mt_prefix2[tid] = s_mt2[tid] - mt2;
     }
     if (tid == E - 1) {
       offsets[E] = incl;
       dropped[0] = s_drop[tid];
       if (mt_prefix != nullptr) mt_prefix[E] = s_mt[tid];
+      if (mt_prefix2 != nullptr) mt_prefix2[E] = s_mt2[tid];
     }
     for (int q = tid; q < n; q += 256) {
       const int r = s_rank[q], e = s_exp[q];
@@ -342,14 +361,15 @@ hipError_t launch_k(const void* X, bool x_bf16, const int32_t* topk_idx, int T,
                     int d, int E, int k, int C, int32_t* counts,
                     int32_t* offsets, int32_t* dropped, int32_t* dest_row,
                     int32_t* row_token, void* X_perm, int32_t* local_rank,
-                    int32_t* block_counts, int32_t* mt_prefix, int tile_code, hipStream_t stream) {
+                    int32_t* block_counts, int32_t* mt_prefix, int tile_code, int tile_code2,
+                    hipStream_t stream) {
   const int nblk = (T + kPermThreads - 1) / kPermThreads;
   count_rank_kernel<KMAX><<<nblk, kPermThreads, 0, stream>>>(
       topk_idx, T, E, k, local_rank, block_counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   scan_kernel<<<1, 256, 0, stream>>>(block_counts, nblk, E, C, counts, offsets, dropped,
-                                     mt_prefix, tile_code);
+                                     mt_prefix, tile_code, tile_code2);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (X_perm == nullptr) {
@@ -379,14 +399,15 @@ hipError_t launch_permute(const void* X, bool x_bf16, const int32_t* topk_idx,
                           int T, int d, int E, int k, int C, int32_t* counts,
                           int32_t* offsets, int32_t* dropped, int32_t* dest_row,
                           int32_t* row_token, void* X_perm, void* scratch,
-                          int32_t* mt_prefix, int tile_code, hipStream_t stream) {
+                          int32_t* mt_prefix, int tile_code, hipStream_t stream,
+                          int tile_code2) {
   int32_t* local_rank = static_cast<int32_t*>(scratch);
   int32_t* block_counts = reinterpret_cast<int32_t*>(
       static_cast<char*>(scratch) + align256((size_t)T * k * 4));
   if (T == 0) {
     // still publish empty counts/offsets so callers see a consistent state
     scan_kernel<<<1, 256, 0, stream>>>(block_counts, 0, E, C, counts, offsets, dropped,
-                                       mt_prefix, tile_code);
+                                       mt_prefix, tile_code, tile_code2);
     return hipGetLastError();
   }
   if ((int64_t)T * k <= kSmallCopies) {
@@ -396,14 +417,15 @@ hipError_t launch_permute(const void* X, bool x_bf16, const int32_t* topk_idx,
     const int tpb = X_perm == nullptr ? T : (T + 255) / 256;
     permute_small_kernel<<<(unsigned)((T + tpb - 1) / tpb), 256, 0, stream>>>(
         static_cast<const i32x4*>(X), topk_idx, T, E, k, C, row_chunks, tpb, counts,
-        offsets, dropped, dest_row, row_token, static_cast<i32x4*>(X_perm), mt_prefix, tile_code);
+        offsets, dropped, dest_row, row_token, static_cast<i32x4*>(X_perm), mt_prefix, tile_code,
+        tile_code2);
     return hipGetLastError();
   }
 #define MOE_PERM_CASE(KM)                                                                 \
   if (k <= KM)                                                                            \
     return launch_k<KM>(X, x_bf16, topk_idx, T, d, E, k, C, counts, offsets, dropped,     \
                         dest_row, row_token, X_perm, local_rank, block_counts,       \
-                        mt_prefix, tile_code, stream);
+                        mt_prefix, tile_code, tile_code2, stream);
   MOE_PERM_CASE(1)
   MOE_PERM_CASE(2)
   MOE_PERM_CASE(4)

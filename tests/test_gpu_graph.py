@@ -20,6 +20,10 @@ CASES = {
     "mixtral_s": WL("mixtral_s", 512, 512, 8, 2, 448, W.BF16, W.TOPK_THEN_SOFTMAX, 0.0, 0.0, 12),
     "cap_skew": WL("cap_skew", 600, 256, 16, 4, 192, W.BF16, W.TOPK_THEN_SOFTMAX, 0.8, 1.2, 81),
     "tall": WL("tall_g", 1100, 264, 8, 2, 200, W.BF16, W.SOFTMAX_THEN_TOPK, 0.0, 0.0, 82),
+    # 64 experts, 300 rows each on average with Zipf skew: the two classes of
+    # experts on the library's side stream, forked and joined inside the graph
+    "two_class": WL("two_class_g", 4800, 256, 64, 4, 192, W.BF16, W.TOPK_THEN_SOFTMAX, 0.0,
+                    1.2, 83),
 }
 
 

@@ -62,6 +62,16 @@ def test_noalloc_matches_moe_forward_on_two_calls():
     _check(SECOND)
 
 
+def test_noalloc_matches_the_two_class_ffn():
+    # 64 experts averaging 320 rows, capacity and Zipf skew: moe_forward runs
+    # the experts of at most 160 rows on 160-row tiles on its side stream and
+    # the others on tall tiles; moe_forward_noalloc makes no stream and runs
+    # every expert on tall tiles.  The K order of each row is the same on
+    # both, so the results must be equal bit for bit.
+    wl = W.Workload("noalloc_two_class", 2560, 256, 64, 8, 192, W.BF16, TK, 1.25, 1.2, 73)
+    _check(wl)
+
+
 def test_noalloc_rejects_a_problem_beyond_the_scratch():
     wl = W.WORKLOADS["mixtral"]
     p = problem_of(wl)
