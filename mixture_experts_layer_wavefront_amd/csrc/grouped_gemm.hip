@@ -86,7 +86,8 @@ constexpr int kWgGroupM = 4;   // weight-gradient tiles: M-tiles per group
 constexpr int kGroupM = 4;     // grouped GEMM tiles: M-tiles per band
 constexpr int kF8SBK = 128;    // 32-row tiles with FP8 weights: K per stage (128-byte rows)
 constexpr int kF8SNS = 2;      // 32-row tiles with FP8 weights: stages
-constexpr int kF8SNW = 2;      // 32-row tiles with FP8 weights: 64 output columns
+constexpr int kF8SNW = 2;      // 32-row tiles with FP8 weights: 64 output columns (gate/up)
+constexpr int kF8DNW = 4;      // 32-row tiles with FP8 weights: 128 columns (down projection)
 constexpr int kBntRows = 256;  // 256-row tiles: stream the weights up to this many rows per expert
 constexpr int kStreamRows = 160;  // few rows per expert: 160-row tiles, 4 waves, 3 stages
 constexpr int kPrefixBytes = 1040;  // LDS copy of the tile prefix (E + 1 <= 257 entries)
@@ -1281,7 +1282,9 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
     if (fp8) {
       err = launch_gemm<1, kF8SNW, 1, 1, true, kF8SBK, kF8SNS, kSBAUX, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales, gather, gather_rows);
       if (err != hipSuccess) return err;
-      return launch_gemm<1, kF8SNW, 1, 1, false, kF8SBK, kF8SNS, kSBAUX, true>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream, w_scales);
+      // down: 128 columns, so the H rows (bf16, twice the bytes of a code
+      // row) are a third of each stage's loads rather than half
+      return launch_gemm<1, kF8DNW, 1, 1, false, kF8SBK, kF8SNS, kSBAUX, true>(H, W_down, nullptr, d, d_ff, E, R, offsets, mt_prefix, Y_perm, stream, w_scales);
     }
     err = launch_gemm<1, kSNW, 1, 1, true, kSBK, kSNS, kSBAUX>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, nullptr, gather, gather_rows);
     if (err != hipSuccess) return err;
