@@ -41,6 +41,12 @@
 //    five row sub-tiles per wave) instead of taking a tile of its own, which
 //    would stream the whole weight tile again for a few rows.  The tile
 //    schedule (m_tiles) and the kernels agree through a tile code.
+//  * Two classes: with tall tiles over at least 64 experts, the schedule is
+//    written twice, once per class of experts (kept rows up to kClassRows,
+//    and more), and the classes run concurrently: 160-row tiles on the
+//    library's side stream, tall tiles on the caller's stream.  Every tile
+//    kind sums each row in the same K order, so the class split does not
+//    change a bit of the result.
 //  * Schedule: a one-workgroup kernel turns expert_offsets into a prefix of
 //    per-expert M-tile counts.  The grid is a static upper bound; each
 //    workgroup finds its (expert, n-tile, m-tile) from the prefix and exits
@@ -1137,7 +1143,6 @@ constexpr int kTwoClassMinE = 64;  // measured: 128 experts gain, 32 do not
 struct SideStream {
   hipStream_t stream;
   hipEvent_t fork, join;
-  bool failed;
 };
 std::mutex g_side_mu;
 SideStream g_side[kSideDevices];
@@ -1183,7 +1188,7 @@ hipStream_t ffn_side_stream(hipStream_t stream) {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kSideDevices) return nullptr;
   std::lock_guard<std::mutex> lock(g_side_mu);
   SideStream& r = g_side[dev];
-  if (r.stream == nullptr && !r.failed) {
+  if (r.stream == nullptr) {
     // not while `stream` is being captured into a graph (creating a stream
     // is not a capturable call); the next call outside a capture makes it
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -1201,10 +1206,11 @@ hipStream_t ffn_side_stream(hipStream_t stream) {
       r.fork = f;
       r.join = j;
     } else {
+      // one class for this call (e.g. another thread is capturing a graph
+      // in a mode that forbids the creation); a later call tries again
       if (j) (void)hipEventDestroy(j);
       if (f) (void)hipEventDestroy(f);
       if (s) (void)hipStreamDestroy(s);
-      r.failed = true;  // one class from now on
       (void)hipGetLastError();
     }
   }
