@@ -376,28 +376,35 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     int EP, int S, int k, int gating, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w) {
   const int lane = threadIdx.x % kWave;
-  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (t >= T) return;
+  // the partials of all of this lane's experts are requested CH at a time per
+  // expert before any is added (one memory round trip per chunk instead of
+  // one per expert and chunk), then added in the order s = 0, 1, ...
+  constexpr int CH = VPL <= 2 ? 32 : 16;
+  float acc[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) acc[i] = 0.f;
+  for (int s0 = 0; s0 < S; s0 += CH) {
+    float pv[VPL][CH];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + kWave * i;
+#pragma unroll
+      for (int u = 0; u < CH; ++u)
+        pv[i][u] = (e < E && s0 + u < S) ? partial[((int64_t)(s0 + u) * T + t) * EP + e] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+#pragma unroll
+      for (int u = 0; u < CH; ++u)
+        if (s0 + u < S) acc[i] += pv[i][u];
+  }
   float v[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + kWave * i;
-    if (e < E) {
-      // loads issued sixteen at a time, added in the order s = 0, 1, ...
-      float acc = 0.f;
-      for (int s0 = 0; s0 < S; s0 += 16) {
-        float pv[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-          pv[u] = (s0 + u < S) ? partial[((int64_t)(s0 + u) * T + t) * EP + e] : 0.f;
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-          if (s0 + u < S) acc += pv[u];
-      }
-      v[i] = acc + (bias != nullptr ? bias[e] : 0.f);
-    } else {
-      v[i] = -INFINITY;
-    }
+    v[i] = (e < E) ? acc[i] + (bias != nullptr ? bias[e] : 0.f) : -INFINITY;
   }
   topk_softmax_store<VPL>(v, E, k, gating, lane, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
 }
@@ -708,13 +715,17 @@ hipError_t launch_select(const float* partial, const float* bias, int T, int E, 
         router_select_group_kernel<16, 16><<<g16, 256, 0, stream>>>(partial, bias, T, E, EP, S, k, gating, topk_idx, topk_w);
       return hipGetLastError();
     }
-    const unsigned gs = (unsigned)((T + 3) / 4);
+    // one token per wavefront; up to 64 tokens one wavefront per workgroup,
+    // so few tokens spread over as many CUs
+    const int wpb = T <= 64 ? 1 : 4;
+    const unsigned gs = (unsigned)((T + wpb - 1) / wpb);
+    const unsigned bs = (unsigned)(wpb * kWave);
     if (E <= 64)
-      router_select_kernel<1><<<gs, 256, 0, stream>>>(partial, bias, T, E, EP, S, k, gating, topk_idx, topk_w);
+      router_select_kernel<1><<<gs, bs, 0, stream>>>(partial, bias, T, E, EP, S, k, gating, topk_idx, topk_w);
     else if (E <= 128)
-      router_select_kernel<2><<<gs, 256, 0, stream>>>(partial, bias, T, E, EP, S, k, gating, topk_idx, topk_w);
+      router_select_kernel<2><<<gs, bs, 0, stream>>>(partial, bias, T, E, EP, S, k, gating, topk_idx, topk_w);
     else
-      router_select_kernel<4><<<gs, 256, 0, stream>>>(partial, bias, T, E, EP, S, k, gating, topk_idx, topk_w);
+      router_select_kernel<4><<<gs, bs, 0, stream>>>(partial, bias, T, E, EP, S, k, gating, topk_idx, topk_w);
     return hipGetLastError();
   }
   const int nblk = (T + kStatBlockTok - 1) / kStatBlockTok;
