@@ -20,8 +20,11 @@
 //    same output columns, so SwiGLU is applied in registers before the
 //    single bf16 store of H.  256-row tiles use 8 wavefronts (2 x 4) with
 //    128 x 64 wave tiles; 160-row tiles (65-160 rows per expert on average)
-//    three stages and 4 wavefronts for gate/up, 8 (160 x 32 each) for the
-//    down projection; 32-row tiles (few rows per expert) 4.
+//    three stages and 8 wavefronts, two per SIMD: for gate/up a SIMD's
+//    two waves hold the gate and the up accumulators of one 32-column block
+//    (the up wave hands its sums to the gate wave through the LDS for
+//    SwiGLU), for the down projection 160 x 32 each; 32-row tiles (few rows
+//    per expert) 4.
 //    The epilogue writes each 32-row sub-tile into the free LDS stages and
 //    stores it with 16-byte stores.
 //  * Operands are staged global -> LDS with buffer_load_dwordx4 ... lds (no
@@ -97,6 +100,7 @@ constexpr int kF8SNW = 2;      // 32-row tiles with FP8 weights: 64 output colum
 constexpr int kF8DNW = 4;      // 32-row tiles with FP8 weights: 128 columns (down projection)
 constexpr int kBntRows = 256;  // 256-row tiles: stream the weights up to this many rows per expert
 constexpr int kStreamRows = 160;  // few rows per expert: 160-row tiles, 4 waves, 3 stages
+constexpr int kStreamGateNW = 8;  // 160-row gate/up tiles: 8 waves, gate and up of a column block on one SIMD
 constexpr int kStreamDownNW = 8;  // 160-row down-projection tiles: 8 waves of 160 x 32 (two per SIMD)
 constexpr int kPrefixBytes = 1040;  // LDS copy of the tile prefix (E + 1 <= 257 entries)
 
@@ -182,8 +186,13 @@ struct GemmCfg {
   static constexpr int NWAVES = MW * NW;
   static constexpr int NT = NWAVES * kWave;
   static constexpr int BM = MW * TM * 32;
-  static constexpr int BN = NW * TN * 32;            // output columns per tile
-  static constexpr int NB = GATEUP ? 2 * TN : TN;    // B sub-tiles per wave
+  // SPLIT (gate/up, one wave row of 8 waves): waves w < 4 hold the gate
+  // accumulators of column block w, waves w + 4 the up accumulators of the
+  // same block (the hardware pairs waves w and w + 4 on one SIMD); the up
+  // waves hand theirs to the gate waves through the LDS for SwiGLU
+  static constexpr bool SPLIT = GATEUP && MW == 1 && NW == 8;
+  static constexpr int BN = (SPLIT ? NW / 2 : NW) * TN * 32;  // output columns per tile
+  static constexpr int NB = (GATEUP && !SPLIT) ? 2 * TN : TN;  // B sub-tiles per wave
   static constexpr int BROWS = GATEUP ? 2 * BN : BN;  // B rows staged per K step
   // LDS stage: the A region (ROWSA rows of RBA bytes), then the B region
   // (ROWSB rows of RBB bytes; FP8 codes when BF8)
@@ -572,6 +581,12 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   // SIMD holds waves of different row halves and skipping the empty row
   // sub-tiles of a ragged tile leaves every SIMD with work.
   const int wm = wave / NW, wn = wave % NW;
+  // SPLIT: column block and projection (0 gate, 1 up) of this wave; the
+  // B-local first row of the wave's sub-tiles
+  constexpr bool SPLIT = Cfg::SPLIT;
+  static_assert(!SPLIT || (MODE == 0 && !BF8), "split gate/up: forward bf16 only");
+  const int wq = SPLIT ? wn % (NW / 2) : wn;
+  const int half_gu = SPLIT ? wn / (NW / 2) : 0;
   // Rows of the wave's sub-tiles: wave row wm covers rows wm * TM * 32 +
   // 32 mi; a tall kernel's tiles of at most 256 rows use 4 sub-tiles per
   // wave row (wm * 128 + 32 mi) so the two wave rows stay balanced, and the
@@ -595,7 +610,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   uint32_t abase[KSUB], bbase[KSUB];
   // B sub-tile nj: 32-row blocks past B-local row wn * TN * 32 (gate/up: the
   // up rows start BN rows on)
-  auto bj = [](int nj) { return (GATEUP && nj >= TN) ? nj + (NW - 1) * TN : nj; };
+  auto bj = [](int nj) { return (GATEUP && nj >= TN) ? nj + (NW - 1) * TN : nj; };  // SPLIT: nj < TN
   if constexpr (AT) {
 #pragma unroll
     for (int mi = 0; mi < TM; ++mi) offA[mi][0] = tr_lane_off(lane, sub_row0(mi), RBA);
@@ -619,13 +634,16 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
       }
     }
     if constexpr (BCOMPACT) {
-      const uint32_t R = wn * TN * 32 + (lane & 31);
+      uint32_t R;
+      if constexpr (SPLIT) R = half_gu * BN + wq * TN * 32 + (lane & 31);
+      else R = wn * TN * 32 + (lane & 31);
       bbase[ks] = AREG + R * RBB + ((c ^ swz<CPRB>(R)) * 16);
     } else if constexpr (!BT) {
 #pragma unroll
       for (int nj = 0; nj < NB; ++nj) {
         uint32_t brow;
-        if (GATEUP) brow = (nj < TN) ? wn * TN * 32 + nj * 32 : BN + wn * TN * 32 + (nj - TN) * 32;
+        if constexpr (SPLIT) brow = half_gu * BN + wq * TN * 32 + nj * 32;
+        else if (GATEUP) brow = (nj < TN) ? wn * TN * 32 + nj * 32 : BN + wn * TN * 32 + (nj - TN) * 32;
         else brow = wn * TN * 32 + nj * 32;
         const uint32_t R = brow + (lane & 31);  // B-local row
         if constexpr (BF8)  // 8 codes: half (lane >> 5) of 16-byte chunk ks
@@ -753,9 +771,28 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
     static_assert(NWAVES * 32 * RS <= NS * STAGE, "the staging fits the stages");
     uint16_t* H = static_cast<uint16_t*>(Cout);
     __syncthreads();  // every wave is done with the last stage
-    char* wreg = smem + wave * (32 * RS);
+    // SPLIT: the up waves' accumulators go to the LDS ([block][mi][r][lane]
+    // fp32) and the gate waves read the ones of their block, element for
+    // element in their own layout; the up waves are then done
+    constexpr int XCH = SPLIT ? (NW / 2) * TM * 16 * kWave * 4 : 0;
+    static_assert(XCH + NWAVES * 32 * RS <= NS * STAGE, "exchange and staging fit the stages");
+    [[maybe_unused]] const float* xu = reinterpret_cast<const float*>(smem) + wq * TM * 16 * kWave;
+    if constexpr (SPLIT) {
+      if (half_gu == 1) {
+        float* xw = reinterpret_cast<float*>(smem) + wq * TM * 16 * kWave;
+#pragma unroll
+        for (int mi = 0; mi < TM; ++mi)
+          if (mi < tm_active)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) xw[(mi * 16 + r) * kWave + lane] = acc[mi][0][r];
+      }
+      __syncthreads();
+      if (half_gu == 1) return;  // no barrier follows
+    }
+    char* wreg = SPLIT ? smem + XCH + wave * (32 * RS) : smem + wave * (32 * RS);
     const int rsub = lane / CPRW, ch = lane % CPRW;
-    const int colc = wn * TN * 32 + ch * 8;  // tile-local first column of the chunk
+    // tile-local first column of the chunk
+    const int colc = SPLIT ? wq * TN * 32 + ch * 8 : wn * TN * 32 + ch * 8;
 #pragma unroll
     for (int mi = 0; mi < TM; ++mi) {
       if (mi >= tm_active) continue;  // uniform: no rows of the tile here
@@ -763,7 +800,10 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
       for (int nj = 0; nj < TN; ++nj)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float gv = acc[mi][nj][r], u = acc[mi][nj + TN][r];
+          const float gv = acc[mi][nj][r];
+          float u;
+          if constexpr (SPLIT) u = xu[(mi * 16 + r) * kWave + lane];  // TN == 1
+          else u = acc[mi][nj + TN][r];
           const float h = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * u;
           const int rl = rlane + 8 * (r >> 2) + (r & 3);
           *reinterpret_cast<uint16_t*>(wreg + rl * RS + (nj * 32 + col_l) * 2) =
@@ -1320,7 +1360,7 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
     if ((err = hipStreamWaitEvent(side, ss->fork, 0)) != hipSuccess) return err;
     err = launch_gemm<2, kNW, 5, 4 / kNW, true, kBK, 2, 0>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, pre_big, H, stream, nullptr, gather, gather_rows);
     if (err != hipSuccess) return err;
-    err = launch_gemm<1, 4, 5, 1, true, kBK, 3, kNonTemporal>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, side, nullptr, gather, gather_rows, cap_small);
+    err = launch_gemm<1, kStreamGateNW, 5, 1, true, kBK, 3, kNonTemporal>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, side, nullptr, gather, gather_rows, cap_small);
     if (err != hipSuccess) return err;
     err = launch_down<2, kNW, 5, kDTN / kNW, kBK, 2, 0, false>(H, W_down, d, d_ff, E, R, offsets, pre_big, Y_perm, nullptr, stream, nullptr);
     if (err != hipSuccess) return err;
@@ -1354,11 +1394,14 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
     // the weights stream once, so the bytes in flight per CU set the rate.
     // 160-row tiles of 4 waves (160 x 64 wave tiles) leave room for three
     // 52 KB stages (two in flight while one is multiplied); 128-byte
-    // weight-row pieces per stage, read past the caches.  The down
-    // projection's 256 columns are split over 8 waves (two per SIMD, each
-    // 160 x 32), so one wave of a SIMD issues MFMAs while the other waits on
-    // its loads: DeepSeek-V3-shaped FFN 4.66-4.73 -> 4.64-4.68 ms, same sums
-    err = launch_gemm<1, 4, 5, 1, true, kBK, 3, kNonTemporal>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, nullptr, gather, gather_rows);
+    // weight-row pieces per stage, read past the caches.  Both GEMMs run 8
+    // waves, two per SIMD, so one wave of a SIMD issues MFMAs while the other
+    // waits on its loads: the gate/up tile's gate and up accumulators of a
+    // column block sit on the two waves of one SIMD (SwiGLU joins them
+    // through the LDS), the down projection's 256 columns are 8 blocks of
+    // 32.  DeepSeek-V3-shaped FFN 4.66-4.73 -> 4.64-4.68 ms (down) -> 4.51-
+    // 4.52 ms (gate/up), the same sums bit for bit
+    err = launch_gemm<1, kStreamGateNW, 5, 1, true, kBK, 3, kNonTemporal>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, nullptr, gather, gather_rows);
     if (err != hipSuccess) return err;
     return launch_down<1, kStreamDownNW, 5, 8 / kStreamDownNW, kBK, 3, kNonTemporal, false>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, nullptr, defer);
   }
