@@ -99,7 +99,7 @@ constexpr int kF8SNS = 2;      // 32-row tiles with FP8 weights: stages
 constexpr int kF8SNW = 2;      // 32-row tiles with FP8 weights: 64 output columns (gate/up)
 constexpr int kF8DNW = 4;      // 32-row tiles with FP8 weights: 128 columns (down projection)
 constexpr int kBntRows = 256;  // 256-row tiles: stream the weights up to this many rows per expert
-constexpr int kStreamRows = 160;  // few rows per expert: 160-row tiles, 4 waves, 3 stages
+constexpr int kStreamRows = 160;  // few rows per expert: 160-row tiles, 8 waves, 3 stages
 constexpr int kStreamGateNW = 8;  // 160-row gate/up tiles: 8 waves, gate and up of a column block on one SIMD
 constexpr int kStreamDownNW = 8;  // 160-row down-projection tiles: 8 waves of 160 x 32 (two per SIMD)
 constexpr int kPrefixBytes = 1040;  // LDS copy of the tile prefix (E + 1 <= 257 entries)
@@ -1392,8 +1392,8 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
   if (bm == kStreamRows) {
     // up to 160 rows per expert on average (one M-tile for most experts):
     // the weights stream once, so the bytes in flight per CU set the rate.
-    // 160-row tiles of 4 waves (160 x 64 wave tiles) leave room for three
-    // 52 KB stages (two in flight while one is multiplied); 128-byte
+    // 160-row tiles of 128 (gate/up) or 256 (down) columns leave room for
+    // three 52 KB stages (two in flight while one is multiplied); 128-byte
     // weight-row pieces per stage, read past the caches.  Both GEMMs run 8
     // waves, two per SIMD, so one wave of a SIMD issues MFMAs while the other
     // waits on its loads: the gate/up tile's gate and up accumulators of a
