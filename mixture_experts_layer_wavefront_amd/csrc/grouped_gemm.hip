@@ -55,7 +55,7 @@
 //    per-expert M-tile counts.  The grid is a static upper bound; each
 //    workgroup finds its (expert, n-tile, m-tile) from the prefix and exits
 //    if it has none -- no host round trip.  Tiles are ordered expert-major,
-//    an expert's tall tile first (longest first), then in bands of four
+//    an expert's tall tile first (longest first), then in bands of eight
 //    M-tiles that walk the N-tiles together, and remapped so that the
 //    hardware's round-robin of workgroups over the 8 XCDs gives each XCD a
 //    contiguous run of tiles: the tiles sharing one expert's weights and
@@ -93,7 +93,7 @@ constexpr int kSBK = 64;       // 32-row tiles: K per stage
 constexpr int kSNS = 3;        // 32-row tiles: stages
 constexpr int kSBAUX = kNonTemporal;  // 32-row tiles: weight loads stream (nt)
 constexpr int kWgGroupM = 4;   // weight-gradient tiles: M-tiles per group
-constexpr int kGroupM = 4;     // grouped GEMM tiles: M-tiles per band
+constexpr int kGroupM = 8;     // grouped GEMM tiles: M-tiles per band
 constexpr int kF8SBK = 128;    // 32-row tiles with FP8 weights: K per stage (128-byte rows)
 constexpr int kF8SNS = 2;      // 32-row tiles with FP8 weights: stages
 constexpr int kF8SNW = 2;      // 32-row tiles with FP8 weights: 64 output columns (gate/up)
