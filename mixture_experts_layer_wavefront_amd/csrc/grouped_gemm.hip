@@ -584,7 +584,7 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
   // SPLIT: column block and projection (0 gate, 1 up) of this wave; the
   // B-local first row of the wave's sub-tiles
   constexpr bool SPLIT = Cfg::SPLIT;
-  static_assert(!SPLIT || (MODE == 0 && !BF8), "split gate/up: forward bf16 only");
+  static_assert(!SPLIT || MODE == 0, "split gate/up: forward only");
   const int wq = SPLIT ? wn % (NW / 2) : wn;
   const int half_gu = SPLIT ? wn / (NW / 2) : 0;
   // Rows of the wave's sub-tiles: wave row wm covers rows wm * TM * 32 +
@@ -745,7 +745,8 @@ __global__ __launch_bounds__(kWave * MW * NW) void grouped_gemm_kernel(const Gem
 #pragma unroll
       for (int nj = 0; nj < NB; ++nj)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mi][nj][r] *= (GATEUP && nj >= TN) ? s1 : s0;
+        for (int r = 0; r < 16; ++r)
+          acc[mi][nj][r] *= (SPLIT ? half_gu == 1 : (GATEUP && nj >= TN)) ? s1 : s0;
   }
 
   // ---- epilogue ---------------------------------------------------------------
@@ -1262,7 +1263,7 @@ hipStream_t ffn_side_stream(hipStream_t stream) {
 int ffn_tile_rows(bool bf16, int rows_per_expert, bool fp8) {
   if (!bf16) return kF32Tile;
   if (rows_per_expert <= 64) return 32;
-  if (fp8) return rows_per_expert <= 512 ? 128 : 256;
+  if (fp8) return rows_per_expert <= kStreamRows ? kStreamRows : rows_per_expert <= 512 ? 128 : 256;
   return rows_per_expert <= kStreamRows ? kStreamRows : 256;
 }
 
@@ -1368,6 +1369,14 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
     if (err != hipSuccess) return err;
     if ((err = hipEventRecord(ss->join, side)) != hipSuccess) return err;
     return hipStreamWaitEvent(stream, ss->join, 0);
+  }
+  if (fp8 && bm == kStreamRows) {
+    // FP8 weights, up to 160 rows per expert on average (one M-tile for most
+    // experts): the 8-wave 160-row tiles of the bf16 path with K = 128 per
+    // stage (128-byte code rows), two 72 KB stages
+    err = launch_gemm<1, kStreamGateNW, 5, 1, true, 128, 2, kNonTemporal, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales, gather, gather_rows);
+    if (err != hipSuccess) return err;
+    return launch_down<1, kStreamDownNW, 5, 8 / kStreamDownNW, 128, 2, kNonTemporal, true>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, w_scales, defer);
   }
   if (fp8 && bm == 128) {
     // FP8 weights, up to a few hundred rows per expert: 128-row tiles and
