@@ -1379,14 +1379,9 @@ hipError_t launch_grouped_ffn(const void* X_perm, bool bf16,
     return launch_down<1, kStreamDownNW, 5, 8 / kStreamDownNW, 128, 2, kNonTemporal, true>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, w_scales, defer);
   }
   if (fp8 && bm == 128) {
-    // FP8 weights, up to a few hundred rows per expert: 128-row tiles and
-    // K = 128 per stage, so each weight row is read 128 bytes (one cache
-    // line) at a time; 64 KB stages, two of them
-    if (rows_per_expert <= 128) {
-      err = launch_gemm<2, 4, 2, 1, true, 128, 2, kNonTemporal, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales, gather, gather_rows);
-      if (err != hipSuccess) return err;
-      return launch_down<2, 4, 2, 2, 128, 2, kNonTemporal, true>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, w_scales, defer);
-    }
+    // FP8 weights, 160 to 512 rows per expert: 128-row tiles and K = 128 per
+    // stage, so each weight row is read 128 bytes (one cache line) at a time;
+    // 64 KB stages, two of them
     err = launch_gemm<2, 4, 2, 1, true, 128, 2, 0, true>(X_perm, W_gate, W_up, d_ff, d, E, R, offsets, mt_prefix, H, stream, w_scales, gather, gather_rows);
     if (err != hipSuccess) return err;
     return launch_down<2, 4, 2, 2, 128, 2, 0, true>(H, W_down, d, d_ff, E, R, offsets, mt_prefix, Y_perm, Y_half, stream, w_scales, defer);
